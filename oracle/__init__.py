@@ -4,21 +4,29 @@ TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-ba
 of ``bench.py`` may import this package. It shares no code with the HIP library
 (``tensor_transformer_layers_amd``) and imports nothing from it.
 
-The arithmetic lives in ``oracle.c`` (plain loops, fp64, OpenMP over rows); this module
-only builds it with gcc and marshals numpy arrays through ctypes. Every function follows
-the passages cited in ``oracle.c``:
+The oracle follows the pages' notation and layout: activations X [rows, H_in], weights
+W in R^{H_in x H_out} (llms.blog, "The Core Primitives"), token row t = b * seq + s.
+Every step is fp64. The linear layers are fp64 matrix products (numpy's matmul serves as
+the library primitive; inputs are exact fp32/bf16 values widened to fp64); GeLU, the
+softmax attention (query by query) and the partial sum are plain loops in ``oracle.c``.
 
-* ``gelu``                      exact-erf GeLU (the pages name GeLU without a formula).
+* ``gelu``                      exact-erf GeLU x Phi(x) (the pages name GeLU without a
+                                formula; the exact form is the reading taken).
 * ``linear``                    Y = X W + b (llms.blog, "The Core Primitives").
 * ``mlp_column``/``mlp_row``    rank r's column-parallel GeLU(X A_r + a_r) and row-parallel
-                                Y_r B_r (ai360xpert.com, "How It Works"; llms.blog, MLP block).
-* ``mlp_shard``                 rank r's partial; N = 1 is the unsharded block.
+                                Y_r B_r, A_r = A[:, r F/N:(r+1) F/N], B_r = B[r F/N:(r+1) F/N, :]
+                                (ai360xpert.com, "How It Works", steps 1-2; llms.blog,
+                                "Partitioning the Multi-Layer Perceptron (MLP) Block").
+* ``mlp_shard``                 rank r's partial; N = 1 is the unsharded block GeLU(XA + a)B.
 * ``qkv_shard``/``attention``/``out_proj_shard``/``attn_shard``
-                                head-partitioned attention (llms.blog, "Partitioning
-                                Multi-Head and Grouped-Query Attention").
+                                head-partitioned attention: rank r owns heads r H/N ... of
+                                width d = h/H, i.e. columns [r h/N, (r+1) h/N) of W_Q, W_K,
+                                W_V and the same rows of W_O (llms.blog, "Partitioning
+                                Multi-Head and Grouped-Query Attention", steps 1-3).
 * ``sum_partials``              the all-reduce's sum (llms.blog, "Row-Parallel Linear Layer").
 
-Parity pins live in ``tests/test_oracle.py``; every function above is pinned there.
+Unequal splits raise ``OracleError``: the pages only use exact shards. Every function is
+pinned in ``tests/test_oracle.py``.
 """
 from __future__ import annotations
 
@@ -39,6 +47,10 @@ _f = ctypes.POINTER(ctypes.c_float)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
+
+# Column chunk of a weight widened to fp64 at a time (bounds memory; each output element's
+# dot product is still computed whole by the matmul).
+_CHUNK_ELEMS = 1 << 26
 
 
 def build(force: bool = True) -> str:
@@ -65,23 +77,11 @@ def _load():
     lib.oracle_gelu.restype = ctypes.c_double
     lib.oracle_gelu.argtypes = [ctypes.c_double]
     lib.oracle_gelu_array.argtypes = [_d, _d, _i64]
-    lib.oracle_linear.argtypes = [_d, _f, _f, _d, _i64, _i64, _i64]
-    lib.oracle_mlp_column.argtypes = [_d, _f, _f, _d, _i64, _i64, _i64, _int, _int]
-    lib.oracle_mlp_row.argtypes = [_d, _f, _d, _i64, _i64, _i64, _int, _int]
-    lib.oracle_mlp_shard.argtypes = [_d, _f, _f, _f, _d, _i64, _i64, _i64, _int, _int]
-    lib.oracle_qkv_shard.argtypes = [_d, _f, _f, _f, _f, _f, _f, _d, _d, _d,
-                                     _i64, _i64, _int, _int, _int]
     lib.oracle_attention.argtypes = [_d, _d, _d, _d, _i64, _i64, _int, _i64, _int, _i64p, _i64]
-    lib.oracle_out_proj_shard.argtypes = [_d, _f, _d, _i64, _i64, _int, _int, _int]
-    lib.oracle_attn_shard.argtypes = [_d, _f, _f, _f, _f, _f, _f, _f, _d, _d,
-                                      _i64, _i64, _i64, _int, _int, _int, _int, _i64p, _i64]
+    lib.oracle_attention.restype = _int
     lib.oracle_sum_partials.argtypes = [_f, _int, _i64, _d]
-    lib.oracle_matmul_dd.argtypes = [_d, _d, _d, _i64, _i64, _i64]
+    lib.oracle_sum_partials.restype = _int
     lib.oracle_max_threads.restype = _int
-    for name in ("oracle_mlp_column", "oracle_mlp_row", "oracle_mlp_shard", "oracle_qkv_shard",
-                 "oracle_attention", "oracle_out_proj_shard", "oracle_attn_shard",
-                 "oracle_sum_partials"):
-        getattr(lib, name).restype = _int
     _lib = lib
     return lib
 
@@ -94,21 +94,8 @@ def _dp(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(_d)
 
 
-def _fp(a: Optional[np.ndarray]):
-    return None if a is None else a.ctypes.data_as(_f)
-
-
 def _as_d(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
-
-
-def _as_f(a) -> Optional[np.ndarray]:
-    if a is None:
-        return None
-    a = np.ascontiguousarray(a)
-    if a.dtype != np.float32:
-        raise TypeError("oracle weights must be float32 arrays (got %s)" % a.dtype)
-    return a
 
 
 def _check(rc: int, what: str):
@@ -116,10 +103,19 @@ def _check(rc: int, what: str):
         raise OracleError("%s failed (rc=%d): invalid shape, rank or split" % (what, rc))
 
 
+def _split(n: int, N: int, r: int, what: str) -> slice:
+    """Rank r's contiguous 1/N of a dimension of size n (exact splits only)."""
+    if N < 1 or r < 0 or r >= N or n % N != 0:
+        raise OracleError("cannot split %s=%d over N=%d for rank %d" % (what, n, N, r))
+    w = n // N
+    return slice(r * w, (r + 1) * w)
+
+
 def threads() -> int:
     return int(_load().oracle_max_threads())
 
 
+# ---- element-wise -------------------------------------------------------------------------
 def gelu(x):
     x = _as_d(x)
     y = np.empty_like(x)
@@ -127,68 +123,63 @@ def gelu(x):
     return y
 
 
+# ---- linear layer -------------------------------------------------------------------------
 def linear(X, W, b=None) -> np.ndarray:
-    """Y = X W (+ b); X [rows, in] (fp64 copy), W [in, out] float32 (pages' layout)."""
+    """Y = X W (+ b): X [rows, H_in], W [H_in, H_out] (pages' layout), b [H_out], all fp64."""
     X = _as_d(X)
-    W = _as_f(W)
-    b = _as_f(b)
+    W = np.asarray(W)
     rows, k = X.shape
     k2, n = W.shape
-    assert k == k2
+    if k != k2:
+        raise OracleError("linear: X has %d columns, W has %d rows" % (k, k2))
     Y = np.empty((rows, n), dtype=np.float64)
-    _load().oracle_linear(_dp(X), _fp(W), _fp(b), _dp(Y), rows, k, n)
+    step = max(1, _CHUNK_ELEMS // max(1, k))
+    for c0 in range(0, n, step):
+        c1 = min(n, c0 + step)
+        np.matmul(X, W[:, c0:c1].astype(np.float64), out=Y[:, c0:c1])
+    if b is not None:
+        Y += np.asarray(b, dtype=np.float64)
     return Y
 
 
+# ---- MLP block ----------------------------------------------------------------------------
 def mlp_column(X, A, a, N: int, r: int) -> np.ndarray:
-    X = _as_d(X)
-    A = _as_f(A)
-    a = _as_f(a)
-    T, h = X.shape
-    F = A.shape[1]
-    Y = np.empty((T, F // max(N, 1)), dtype=np.float64)
-    _check(_load().oracle_mlp_column(_dp(X), _fp(A), _fp(a), _dp(Y), T, h, F, N, r),
-           "mlp_column")
-    return Y
+    """Y_r = GeLU(X A_r + a_r) with A_r = A[:, r F/N:(r+1) F/N] and a_r the same slice of a."""
+    cols = _split(np.shape(A)[1], N, r, "F")
+    return gelu(linear(X, A[:, cols], None if a is None else a[cols]))
 
 
 def mlp_row(Y_r, B, N: int, r: int) -> np.ndarray:
-    Y_r = _as_d(Y_r)
-    B = _as_f(B)
-    F, h = B.shape
-    T = Y_r.shape[0]
-    Z = np.empty((T, h), dtype=np.float64)
-    _check(_load().oracle_mlp_row(_dp(Y_r), _fp(B), _dp(Z), T, h, F, N, r), "mlp_row")
-    return Z
+    """Z_r = Y_r B_r with B_r = B[r F/N:(r+1) F/N, :]."""
+    rows = _split(np.shape(B)[0], N, r, "F")
+    return linear(Y_r, B[rows, :])
 
 
 def mlp_shard(X, A, a, B, N: int = 1, r: int = 0) -> np.ndarray:
     """Rank r's partial GeLU(X A_r + a_r) B_r; N = 1 gives the unsharded MLP block."""
-    X = _as_d(X)
-    A, a, B = _as_f(A), _as_f(a), _as_f(B)
-    T, h = X.shape
-    F = A.shape[1]
-    Z = np.empty((T, h), dtype=np.float64)
-    _check(_load().oracle_mlp_shard(_dp(X), _fp(A), _fp(a), _fp(B), _dp(Z), T, h, F, N, r),
-           "mlp_shard")
-    return Z
+    return mlp_row(mlp_column(X, A, a, N, r), B, N, r)
+
+
+# ---- attention block ---------------------------------------------------------------------
+def _head_cols(h: int, H: int, N: int, r: int) -> slice:
+    if H < 1 or h % H != 0:
+        raise OracleError("hidden %d is not divisible by %d heads" % (h, H))
+    if H % N != 0:
+        raise OracleError("%d heads are not divisible over N=%d" % (H, N))
+    return _split(h, N, r, "hidden")
 
 
 def qkv_shard(X, Wq, Wk, Wv, bq=None, bk=None, bv=None, H: int = 1, N: int = 1, r: int = 0):
-    X = _as_d(X)
-    Wq, Wk, Wv = _as_f(Wq), _as_f(Wk), _as_f(Wv)
-    bq, bk, bv = _as_f(bq), _as_f(bk), _as_f(bv)
-    T, h = X.shape
-    w = h // N
-    Q = np.empty((T, w)); K = np.empty((T, w)); V = np.empty((T, w))
-    _check(_load().oracle_qkv_shard(_dp(X), _fp(Wq), _fp(Wk), _fp(Wv), _fp(bq), _fp(bk),
-                                    _fp(bv), _dp(Q), _dp(K), _dp(V), T, h, H, N, r),
-           "qkv_shard")
-    return Q, K, V
+    """Q_r = X W_Q[:, C_r] + b_Q[C_r] and alike for K and V, each [T, h/N]."""
+    h = np.shape(X)[1]
+    c = _head_cols(h, H, N, r)
+    sl = lambda b: None if b is None else b[c]
+    return (linear(X, Wq[:, c], sl(bq)), linear(X, Wk[:, c], sl(bk)), linear(X, Wv[:, c], sl(bv)))
 
 
 def attention(Q, K, V, batch: int, seq: int, n_heads: int, causal: bool = True,
               rows=None) -> np.ndarray:
+    """softmax(Q_j K_j^T / sqrt(d) + mask) V_j per head j, heads concatenated, on query rows."""
     Q, K, V = _as_d(Q), _as_d(K), _as_d(V)
     T, w = Q.shape
     d = w // n_heads
@@ -203,55 +194,55 @@ def attention(Q, K, V, batch: int, seq: int, n_heads: int, causal: bool = True,
 
 
 def out_proj_shard(O_r, Wo, H: int, N: int, r: int) -> np.ndarray:
-    O_r = _as_d(O_r)
-    Wo = _as_f(Wo)
-    n, _ = O_r.shape
-    h = Wo.shape[1]
-    Z = np.empty((n, h), dtype=np.float64)
-    _check(_load().oracle_out_proj_shard(_dp(O_r), _fp(Wo), _dp(Z), n, h, H, N, r),
-           "out_proj_shard")
-    return Z
+    """Z_r = O_r W_O[C_r, :]: the locally concatenated heads times the row slice of W_O."""
+    h = np.shape(Wo)[0]
+    c = _head_cols(h, H, N, r)
+    return linear(O_r, Wo[c, :])
 
 
 def attn_shard(X, Wq, Wk, Wv, bq, bk, bv, Wo, batch: int, seq: int, H: int, N: int = 1,
                r: int = 0, causal: bool = True, rows=None, want_heads: bool = False):
     """Rank r's attention partial on the requested token rows (all rows if None).
 
-    Returns Z_r [n_rows, h] (fp64) or (Z_r, O_r) with O_r [n_rows, h/N], the locally
-    concatenated head outputs, when ``want_heads``.
+    Only the key positions a requested query can see are projected (causal: positions up to
+    the latest requested one in its sequence). Returns Z_r [n_rows, h] (fp64), or
+    (Z_r, O_r) with O_r [n_rows, h/N] the locally concatenated head outputs.
     """
-    X = _as_d(X)
-    Wq, Wk, Wv, Wo = _as_f(Wq), _as_f(Wk), _as_f(Wv), _as_f(Wo)
-    bq, bk, bv = _as_f(bq), _as_f(bk), _as_f(bv)
+    X = np.asarray(X)
     T, h = X.shape
-    assert T == batch * seq
-    rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
-    nq = T if rws is None else rws.size
-    Z = np.empty((nq, h), dtype=np.float64)
-    O = np.empty((nq, h // N), dtype=np.float64) if want_heads else None
-    _check(_load().oracle_attn_shard(_dp(X), _fp(Wq), _fp(Wk), _fp(Wv), _fp(bq), _fp(bk),
-                                     _fp(bv), _fp(Wo), _dp(Z), _dp(O), batch, seq, h, H, N, r,
-                                     int(bool(causal)),
-                                     None if rws is None else rws.ctypes.data_as(_i64p), nq),
-           "attn_shard")
+    if T != batch * seq:
+        raise OracleError("X has %d rows, batch*seq = %d" % (T, batch * seq))
+    c = _head_cols(h, H, N, r)
+    Hl = H // N
+    w = h // N
+    rws = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if rws.size and (rws.min() < 0 or rws.max() >= T):
+        raise OracleError("row index out of range")
+    sl = lambda b: None if b is None else b[c]
+    Q = np.zeros((T, w))
+    K = np.zeros((T, w))
+    V = np.zeros((T, w))
+    for b in np.unique(rws // seq):
+        pos = rws[rws // seq == b] % seq
+        need = int(pos.max()) + 1 if causal else seq
+        blk = slice(b * seq, b * seq + need)
+        K[blk] = linear(X[blk], Wk[:, c], sl(bk))
+        V[blk] = linear(X[blk], Wv[:, c], sl(bv))
+    Q[rws] = linear(X[rws], Wq[:, c], sl(bq))
+    O = attention(Q, K, V, batch, seq, Hl, causal, rows=rws)
+    Z = out_proj_shard(O, Wo, H, N, r)
     return (Z, O) if want_heads else Z
 
 
+# ---- partial sum ----------------------------------------------------------------------------
 def sum_partials(parts) -> np.ndarray:
     """Z = sum_r parts[r] in fp64; parts is [n_parts, numel] float32."""
     P = np.ascontiguousarray(parts, dtype=np.float32)
     n = P.shape[0]
     numel = int(np.prod(P.shape[1:]))
     Z = np.empty(numel, dtype=np.float64)
-    _check(_load().oracle_sum_partials(_fp(P), n, numel, _dp(Z)), "sum_partials")
+    _check(_load().oracle_sum_partials(P.ctypes.data_as(_f), n, numel, _dp(Z)), "sum_partials")
     return Z.reshape(P.shape[1:])
-
-
-def matmul_dd(X, W) -> np.ndarray:
-    X, W = _as_d(X), _as_d(W)
-    Y = np.empty((X.shape[0], W.shape[1]))
-    _load().oracle_matmul_dd(_dp(X), _dp(W), _dp(Y), X.shape[0], X.shape[1], W.shape[1])
-    return Y
 
 
 def rel_frobenius(got, ref) -> float:

@@ -29,9 +29,10 @@ import numpy as np
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Return the bfloat16 bit patterns (uint16) nearest to float32 ``x`` (ties to even)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs: |bits| <= 0xFF7FFFFF, so adding at most 0x8000 cannot wrap in uint32
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16))
+    r = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
