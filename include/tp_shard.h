@@ -1,0 +1,160 @@
+/*
+ * tp_shard.h -- C ABI of libtpshard: one tensor-parallel rank's share of a Transformer block
+ * (the column-parallel / row-parallel MLP pair and the head-partitioned attention block),
+ * computed by hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The split follows the pages' statement of tensor parallelism:
+ *   - Column-parallel linear (llms.blog, "The Core Primitives", 1. Column-Parallel Linear
+ *     Layer): W = [W_1 ... W_N] split on its output dimension, each rank computes X W_i from
+ *     the replicated X, no communication; an element-wise activation applies to the local
+ *     slice (same section, last paragraph).
+ *   - Row-parallel linear (same page, 2. Row-Parallel Linear Layer): W split on its input
+ *     dimension, each rank computes the partial X_i W_i; the true output is the sum of the
+ *     N partials, which the all-reduce forms.
+ *   - MLP block (ai360xpert.com, "How It Works"; llms.blog, "Partitioning the Multi-Layer
+ *     Perceptron (MLP) Block"): Y = GeLU(X A) B; rank i holds A_i (columns) and B_i (rows)
+ *     and produces the partial Z_i = GeLU(X A_i + a_i) B_i.
+ *   - Attention block (llms.blog, "Partitioning Multi-Head and Grouped-Query Attention",
+ *     steps 1-3): h_heads / N heads per rank; Q, K, V projections column-parallel on the
+ *     rank's heads; softmax(Q K^T / sqrt(d_k)) V per head with no cross-head exchange;
+ *     head outputs concatenated locally and multiplied by the rank's row slice of W_O.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer, row-major, allocated and owned by the
+ *     caller. The library allocates no device memory and keeps no state between calls
+ *     (apart from the thread-local error string and a per-device capability check).
+ *   - Weights are stored the way a linear layer stores its weight: [out_features,
+ *     in_features] row-major, i.e. the transpose of the pages' W in R^{H_in x H_out}.
+ *     Rank r's shards are passed as the rank's own contiguous arrays.
+ *   - Token rows are t = b * seq + s (each sequence is a contiguous block of rows).
+ *   - hidden, ffn and n_heads are the FULL (unsharded) sizes; the shard widths ffn / N
+ *     and hidden / N are derived. N (n_shards) and rank follow the pages' split; a size
+ *     that does not divide evenly is an error, never an uneven shard.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and return after the kernels are enqueued. Results are bitwise
+ *     reproducible for a given shape, dtype and device (no atomics, fixed reduction order).
+ *   - Errors: validation runs on the host before any HIP call and returns a tp_status;
+ *     nothing aborts and no exception crosses the ABI. tp_last_error() describes the last
+ *     non-OK status on the calling thread. Pointers must be 16-byte aligned; hidden,
+ *     ffn / N and the head width must be multiples of 8 (16-byte rows); tokens and seq may
+ *     be any value >= 1.
+ *   - Precision: TP_BF16 inputs, weights and intermediates (Y_i, Q/K/V, head outputs) are
+ *     bfloat16 rounded to nearest even, with fp32 accumulation; TP_F32 is fp32 throughout.
+ *     Partials Z_i are always fp32.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_F32 = 0,   /* IEEE binary32 */
+    TP_BF16 = 1   /* bfloat16 (1-8-7), round to nearest even */
+} tp_dtype;
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,           /* a required pointer is NULL (or a partial is missing)   */
+    TP_ERR_SHAPE = 2,          /* a size is out of range                                  */
+    TP_ERR_NOT_DIVISIBLE = 3,  /* ffn % N, n_heads % N or hidden % n_heads is not zero     */
+    TP_ERR_RANK = 4,           /* rank outside [0, N)                                     */
+    TP_ERR_DTYPE = 5,          /* dtype not supported by this call                        */
+    TP_ERR_ALIGN = 6,          /* pointer not 16-byte aligned or row width not 8-multiple */
+    TP_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than *_workspace_bytes()       */
+    TP_ERR_HIP = 8,            /* a HIP runtime call or kernel launch failed               */
+    TP_ERR_DEVICE = 9          /* the current device is not gfx950                         */
+} tp_status;
+
+/* ------------------------------------------------------------------------------------------
+ * MLP shard: Z_i = GeLU(X A_i + a_i) B_i          (ai360xpert.com "How It Works", steps 1-2;
+ *                                                  llms.blog MLP block, steps 1-3)
+ * GeLU is the exact form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
+ *
+ *   X    [tokens, hidden]       dt   replicated input
+ *   A_i  [ffn/N, hidden]        dt   rank's column shard of A, stored transposed:
+ *                                    A_i[j][k] = A[k][rank*ffn/N + j]
+ *   a_i  [ffn/N]                dt   rank's slice of the column bias a, or NULL for none
+ *   B_i  [hidden, ffn/N]        dt   rank's row shard of B, stored transposed:
+ *                                    B_i[o][j] = B[rank*ffn/N + j][o]
+ *   Z_i  [tokens, hidden]       fp32 rank's partial (to be summed over ranks)
+ *   workspace: Y_i = GeLU(X A_i + a_i) [tokens, ffn/N] in dt at byte offset 0.
+ * A row-parallel output bias, if a model has one, is added once after the sum, not here.
+ * dt: TP_F32 or TP_BF16.
+ * ---------------------------------------------------------------------------------------- */
+size_t tp_mlp_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                              tp_dtype dt);
+
+tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                           float* Z_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                           int n_shards, int rank, tp_dtype dt,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Attention shard: Z_i = concat_j(Head_j) W_O,i over the rank's heads j, with
+ *   Head_j = softmax(Q_j K_j^T / sqrt(d) + M) V_j      (llms.blog attention, steps 1-3)
+ * d = hidden / n_heads; Hl = n_heads / N local heads, rank r owning heads r*Hl ... r*Hl+Hl-1.
+ * M is the causal mask (key k visible to query s iff k <= s within a sequence) when
+ * causal != 0, else zero.
+ *
+ *   X       [batch*seq, hidden]   bf16
+ *   Wqkv_i  [3*Hl*d, hidden]      bf16  rows 0..Hl*d-1 = W_Q[:, C_r]^T, then W_K[:, C_r]^T,
+ *                                       then W_V[:, C_r]^T, C_r = columns r*Hl*d ... of the
+ *                                       rank's heads (head-major, d columns per head)
+ *   bqkv_i  [3*Hl*d]              bf16  matching bias slices, or NULL for none
+ *   Wo_i    [hidden, Hl*d]        bf16  rank's row shard of W_O, stored transposed:
+ *                                       Wo_i[o][j] = W_O[r*Hl*d + j][o]
+ *   Z_i     [batch*seq, hidden]   fp32  rank's partial
+ * Workspace layout (byte offsets from tp_attn_workspace_layout, each 256-byte aligned):
+ *   Q   [batch, Hl, seq, d]  bf16     projected queries of the local heads
+ *   K   [batch, Hl, seq, d]  bf16     projected keys
+ *   Vt  [batch, Hl, d, seq]  bf16     projected values, transposed per head
+ *   O   [batch*seq, Hl*d]    bf16     head outputs, concatenated locally
+ * dt: TP_BF16 only. d must be 64 or 128.
+ * ---------------------------------------------------------------------------------------- */
+size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                               int n_shards, tp_dtype dt);
+
+tp_status tp_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                   int n_shards, tp_dtype dt, size_t* q_off, size_t* k_off,
+                                   size_t* vt_off, size_t* o_off);
+
+tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                            const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
+                            int64_t hidden, int n_heads, int causal, int n_shards, int rank,
+                            tp_dtype dt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Partial sum, the single-device stand-in for the tensor-parallel all-reduce:
+ *   Z = Z_0 + Z_1 + ... + Z_{n_parts-1}       (llms.blog, Row-Parallel Linear Layer: the
+ *                                              output and communication bullets)
+ * summed in fp32 in the fixed order 0, 1, ..., n_parts-1, then stored as out_dt (fp32, or
+ * bf16 rounded to nearest even when the next block consumes bf16).
+ *
+ *   Z_parts  HOST array of n_parts DEVICE pointers, each [numel] fp32, 16-byte aligned;
+ *            a NULL entry is a missing rank (TP_ERR_NULL).
+ *   n_parts  1 ... 64
+ *   Z        [numel] out_dt; may alias Z_parts[0], no other aliasing.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel,
+                          void* Z, tp_dtype out_dt, void* stream);
+
+/* Description of the last non-OK status returned on the calling thread ("" if none).
+   The string is owned by the library and valid until the next call on that thread. */
+const char* tp_last_error(void);
+
+/* ABI version of this header (incremented on any signature or layout change). */
+int tp_abi_version(void);
+
+#define TP_SHARD_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

@@ -1,0 +1,145 @@
+"""ctypes binding of libtpshard (include/tp_shard.h), with the same entry-point names.
+
+Argument marshalling only: tensors are passed as device pointers (``data_ptr()``), streams
+as their ``hipStream_t`` handle. Every step of the computation runs in the library's HIP
+kernels; there is no host or PyTorch fallback. If the library has not been built, loading
+it raises ``TPShardNotBuilt``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libtpshard.so")
+
+TP_F32 = 0
+TP_BF16 = 1
+TP_ERR_SHAPE = 2
+
+STATUS_NAMES = {
+    0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_NOT_DIVISIBLE", 4: "TP_ERR_RANK",
+    5: "TP_ERR_DTYPE", 6: "TP_ERR_ALIGN", 7: "TP_ERR_WORKSPACE", 8: "TP_ERR_HIP",
+    9: "TP_ERR_DEVICE",
+}
+
+# Every symbol include/tp_shard.h declares.
+EXPORTED = (
+    "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd", "tp_attn_workspace_bytes",
+    "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_last_error",
+    "tp_abi_version",
+)
+
+
+class TPShardNotBuilt(RuntimeError):
+    pass
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise TPShardNotBuilt(
+            "libtpshard.so is not built (%s); run `python -m tensor_transformer_layers_amd.build`"
+            % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    L.tp_abi_version.restype = _int
+    L.tp_last_error.restype = ctypes.c_char_p
+    L.tp_mlp_workspace_bytes.restype = _sz
+    L.tp_mlp_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
+    L.tp_mlp_shard_fwd.restype = _int
+    L.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                   _vp, _sz, _vp]
+    L.tp_attn_workspace_bytes.restype = _sz
+    L.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int]
+    L.tp_attn_workspace_layout.restype = _int
+    L.tp_attn_workspace_layout.argtypes = [_i64, _i64, _i64, _int, _int, _int,
+                                           ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                           ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+    L.tp_attn_shard_fwd.restype = _int
+    L.tp_attn_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                    _int, _int, _vp, _sz, _vp]
+    L.tp_sum_partials.restype = _int
+    L.tp_sum_partials.argtypes = [ctypes.POINTER(_vp), _int, _i64, _vp, _int, _vp]
+    _lib = L
+    return L
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or an int / None passed through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def tp_last_error() -> str:
+    return lib().tp_last_error().decode()
+
+
+def tp_abi_version() -> int:
+    return lib().tp_abi_version()
+
+
+def tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:
+    return lib().tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt)
+
+
+def tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z_i, tokens, hidden, ffn, n_shards, rank, dt,
+                     workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(Z_i), tokens,
+                                  hidden, ffn, n_shards, rank, dt, _ptr(workspace),
+                                  workspace_bytes, _stream(stream))
+
+
+def tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, dt) -> int:
+    return lib().tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, dt)
+
+
+def tp_attn_workspace_layout(batch, seq, hidden, n_heads, n_shards, dt):
+    """(status, {"q": off, "k": off, "vt": off, "o": off}) byte offsets in the workspace."""
+    offs = [_sz(0) for _ in range(4)]
+    st = lib().tp_attn_workspace_layout(batch, seq, hidden, n_heads, n_shards, dt,
+                                        *[ctypes.byref(o) for o in offs])
+    return st, dict(zip(("q", "k", "vt", "o"), (o.value for o in offs)))
+
+
+def tp_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z_i, batch, seq, hidden, n_heads, causal,
+                      n_shards, rank, dt, workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(bqkv_i), _ptr(Wo_i), _ptr(Z_i),
+                                   batch, seq, hidden, n_heads, int(causal), n_shards, rank, dt,
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def tp_sum_partials(Z_parts: Sequence, n_parts, numel, Z, out_dt, stream=None) -> int:
+    arr = (_vp * max(1, len(Z_parts)))(*[_ptr(z) for z in Z_parts])
+    return lib().tp_sum_partials(arr, n_parts, numel, _ptr(Z), out_dt, _stream(stream))
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise TPError(status, tp_last_error())

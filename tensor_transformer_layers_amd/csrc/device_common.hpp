@@ -1,0 +1,57 @@
+// device_common.hpp -- vector types and small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tps {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte global load / store (the natural width of one lane's MFMA operand chunk).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v)
+{
+    return bf16x4{to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3])};
+}
+
+__device__ __forceinline__ f32x4 bf16x4_to_f32(bf16x4 v)
+{
+    return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                 static_cast<float>(v[3])};
+}
+
+// Exact GeLU, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), in fp32 with the device erff.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+// D = A * B + C on a 16x16 output block with K = 32 (bf16 in, fp32 accumulate).
+// Lane l supplies A row (l & 15) and B column (l & 15), 8 consecutive K values each, and
+// receives D rows 4 * (l >> 4) + i, i = 0..3, of column (l & 15).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same block shape with fp32 operands and K = 4: lane l supplies one K value, (l >> 4).
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace tps

@@ -1,0 +1,413 @@
+// gemm.hip -- tensor-core (MFMA) GEMMs of the column- and row-parallel linear layers on gfx950.
+//
+//   C[m, n] = sum_k A[m, k] * B[n, k]      A = activations [M, K], B = weight [N, K] ([out, in])
+//
+// Both operands are K-contiguous, which is the layout an MFMA lane consumes: one 16-byte
+// chunk of 8 bf16 (or 4 fp32) consecutive K values per lane. The output stage is fused:
+//   BiasGelu  Y_i = GeLU(X A_i + a_i)                   column-parallel MLP layer
+//   F32       Z_i = Y_i B_i  (fp32 partial)             row-parallel layers (MLP, W_O)
+//   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
+//             per head, V written transposed for the attention kernel's P V product.
+//
+// Block = 4 waves (256 lanes) in a 2 x 2 grid, each wave owning a (BM/2) x (BN/2) output
+// tile of 16 x 16 MFMA blocks. The K loop streams BK-wide slabs of A and B through a
+// double-buffered LDS ring: the next slab is fetched into registers while the MFMAs run on
+// the current one, then written to the other buffer; one barrier per slab. LDS rows are
+// 128 bytes (8 chunks of 16 B); chunk c of row r is stored at chunk c ^ (r & 7), so the
+// 16 lanes of an MFMA operand read (16 rows, same chunk) hit 8 distinct bank groups.
+//
+// The MFMA is issued as D = B_frag * A_frag (weight rows as the "M" side), so each lane's
+// four accumulator values are four consecutive output COLUMNS of one row: epilogue stores
+// are 16-byte (fp32) or 8-byte (bf16) vectors, and the bias is one vector load.
+#include <cstdio>
+#include <cstdlib>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tps {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Map the linear block index to an output tile. Blocks are dealt round-robin to the 8 XCDs
+// (block b runs on XCD b % 8); the remap gives each XCD a contiguous run of logical tiles,
+// and logical tiles are ordered in bands of kGroupM tile-rows so that blocks running at the
+// same time on one XCD share A rows and B columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    constexpr int kXcd = 8, kGroupM = 4;
+    const int nb = tiles_m * tiles_n;
+    int bid = blockIdx.x;
+    if (nb % kXcd == 0) bid = (bid % kXcd) * (nb / kXcd) + bid / kXcd;
+    const int per_group = kGroupM * tiles_n;
+    const int group = bid / per_group;
+    const int first_m = group * kGroupM;
+    const int gsz = min(tiles_m - first_m, kGroupM);
+    const int in_group = bid - group * per_group;
+    tm = first_m + in_group % gsz;
+    tn = in_group / gsz;
+}
+
+// ---- output stage ------------------------------------------------------------------------
+// v holds C[m, n .. n+3]; n is a multiple of 4 and N a multiple of 8, so all four are valid.
+template <Epi EPI, typename T>
+__device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f32x4 v)
+{
+    if constexpr (EPI == Epi::F32) {
+        float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+        *reinterpret_cast<f32x4*>(c) = v;
+    } else {
+        if (p.bias) {
+            if constexpr (sizeof(T) == 2) {
+                v += bf16x4_to_f32(*reinterpret_cast<const bf16x4*>(
+                    reinterpret_cast<const bf16*>(p.bias) + n));
+            } else {
+                v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.bias) + n);
+            }
+        }
+        if constexpr (EPI == Epi::BiasGelu) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+            if constexpr (sizeof(T) == 2) {
+                bf16* c = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc + n;
+                *reinterpret_cast<bf16x4*>(c) = to_bf16x4(v);
+            } else {
+                float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+                *reinterpret_cast<f32x4*>(c) = v;
+            }
+        } else {  // Qkv (bf16 only)
+            const int width = p.heads_local * p.head_dim;
+            const int which = n / width;
+            const int rem = n - which * width;
+            const int head = rem / p.head_dim;
+            const int j = rem - head * p.head_dim;
+            const int b = m / p.seq;
+            const int s = m - b * p.seq;
+            const int64_t bh = (int64_t)b * p.heads_local + head;
+            const bf16x4 o = to_bf16x4(v);
+            if (which < 2) {
+                bf16* dst = reinterpret_cast<bf16*>(which == 0 ? p.q : p.k) +
+                            (bh * p.seq + s) * p.head_dim + j;
+                *reinterpret_cast<bf16x4*>(dst) = o;
+            } else {
+                bf16* dst = reinterpret_cast<bf16*>(p.vt) + (bh * p.head_dim + j) * p.ld_vt + s;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * p.ld_vt] = o[i];
+            }
+        }
+    }
+}
+
+// ---- bf16 GEMM ---------------------------------------------------------------------------
+template <int BM, int BN, Epi EPI>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmProblem p)
+{
+    constexpr int BK = 64;                 // K per LDS slab: 128-byte rows
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int ACH = BM * 8 / kThreads;  // 16-byte chunks of the A slab per lane
+    constexpr int BCH = BN * 8 / kThreads;
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && ACH >= 1 && BCH >= 1, "tile");
+
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * BK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const bf16* __restrict__ gA = reinterpret_cast<const bf16*>(p.A);
+    const bf16* __restrict__ gB = reinterpret_cast<const bf16*>(p.B);
+
+    // Lane tid loads chunk (tid & 7) of rows (tid >> 3) + 32 i.
+    const int lc = tid & 7;
+    const int lr = tid >> 3;
+    u32x4 ra[ACH], rb[BCH];
+
+    auto fetch = [&](int k0) {
+        const int kk = k0 + lc * 8;
+        const bool kin = kk < p.K;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int gm = m0 + lr + 32 * i;
+            ra[i] = (kin && gm < p.M) ? ld16(gA + (int64_t)gm * p.lda + kk) : zero16();
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int gn = n0 + lr + 32 * i;
+            rb[i] = (kin && gn < p.N) ? ld16(gB + (int64_t)gn * p.ldb + kk) : zero16();
+        }
+    };
+    auto stash = [&](int buf) {
+        bf16* sA = smem + buf * (BM + BN) * BK;
+        bf16* sB = sA + BM * BK;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int r = lr + 32 * i;
+            st16(sA + r * BK + ((lc ^ (r & 7)) << 3), ra[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int r = lr + 32 * i;
+            st16(sB + r * BK + ((lc ^ (r & 7)) << 3), rb[i]);
+        }
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (p.K + BK - 1) / BK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
+    const int fr = lane & 15;   // operand row within a 16-row block
+    const int fg = lane >> 4;   // which 8-wide K group of the 32-wide MFMA step
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) fetch((kt + 1) * BK);
+        const bf16* sA = smem + cur * (BM + BN) * BK;
+        const bf16* sB = sA + BM * BK;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int ch = ks * 4 + fg;
+            bf16x8 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 16 + fr;
+                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ (r & 7)) << 3));
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int r = wn * WTN + i * 16 + fr;
+                fb[i] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ (r & 7)) << 3));
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = mfma16x16x32(fb[i], fa[j], acc[i][j]);
+        }
+        if (kt + 1 < KT) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    // acc[i][j][v] = C[m0 + wm*WTM + j*16 + fr][n0 + wn*WTN + i*16 + 4*fg + v]
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * WTM + j * 16 + fr;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int n = n0 + wn * WTN + i * 16 + 4 * fg;
+            if (n < p.N) store_out<EPI, bf16>(p, m, n, acc[i][j]);
+        }
+    }
+}
+
+// ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
+// Same structure; a 16-byte chunk holds 4 fp32 K values, BK = 32 (128-byte rows again). Lane
+// l reads chunk 4*ks + (l >> 4) and feeds its 4 values to 4 consecutive MFMAs, so MFMA t of
+// step ks consumes K = 4*(4*ks + g) + t on lane group g, identically for both operands.
+template <int BM, int BN, Epi EPI>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
+{
+    constexpr int BK = 32;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int ACH = BM * 8 / kThreads;
+    constexpr int BCH = BN * 8 / kThreads;
+    static_assert(FM >= 1 && FN >= 1 && ACH >= 1 && BCH >= 1, "tile");
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * (BM + BN) * BK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const float* __restrict__ gA = reinterpret_cast<const float*>(p.A);
+    const float* __restrict__ gB = reinterpret_cast<const float*>(p.B);
+
+    const int lc = tid & 7;
+    const int lr = tid >> 3;
+    u32x4 ra[ACH], rb[BCH];
+    auto fetch = [&](int k0) {
+        const int kk = k0 + lc * 4;
+        const bool kin = kk < p.K;   // K is a multiple of 8, so a chunk is all in or all out
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int gm = m0 + lr + 32 * i;
+            ra[i] = (kin && gm < p.M) ? ld16(gA + (int64_t)gm * p.lda + kk) : zero16();
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int gn = n0 + lr + 32 * i;
+            rb[i] = (kin && gn < p.N) ? ld16(gB + (int64_t)gn * p.ldb + kk) : zero16();
+        }
+    };
+    auto stash = [&](int buf) {
+        float* sA = smem + buf * (BM + BN) * BK;
+        float* sB = sA + BM * BK;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int r = lr + 32 * i;
+            st16(sA + r * BK + ((lc ^ (r & 7)) << 2), ra[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int r = lr + 32 * i;
+            st16(sB + r * BK + ((lc ^ (r & 7)) << 2), rb[i]);
+        }
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (p.K + BK - 1) / BK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) fetch((kt + 1) * BK);
+        const float* sA = smem + cur * (BM + BN) * BK;
+        const float* sB = sA + BM * BK;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ks * 4 + fg;
+            f32x4 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 16 + fr;
+                fa[i] = *reinterpret_cast<const f32x4*>(sA + r * BK + ((ch ^ (r & 7)) << 2));
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int r = wn * WTN + i * 16 + fr;
+                fb[i] = *reinterpret_cast<const f32x4*>(sB + r * BK + ((ch ^ (r & 7)) << 2));
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        acc[i][j] = mfma16x16x4f32(fb[i][t], fa[j][t], acc[i][j]);
+        }
+        if (kt + 1 < KT) stash(cur ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * WTM + j * 16 + fr;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int n = n0 + wn * WTN + i * 16 + 4 * fg;
+            if (n < p.N) store_out<EPI, float>(p, m, n, acc[i][j]);
+        }
+    }
+}
+
+template <int BM, int BN>
+hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
+{
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    dim3 grid(tiles), block(kThreads);
+    switch (epi) {
+        case Epi::BiasGelu:
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::BiasGelu>), grid, block, 0, s, p);
+            break;
+        case Epi::F32:
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::F32>), grid, block, 0, s, p);
+            break;
+        case Epi::Qkv:
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::Qkv>), grid, block, 0, s, p);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Choose the tile that minimises (waves of 256 workgroups) x (tile area) x (per-flop cost of
+// the tile shape); larger tiles re-read less operand data per MFMA.
+GemmTile gemm_bf16_pick_tile(int M, int N, int K)
+{
+    (void)K;
+    struct Cand { int bm, bn; double cost; };
+    const Cand cands[] = {{256, 256, 1.00}, {256, 192, 1.04}, {256, 128, 1.12}, {128, 128, 1.35}};
+    GemmTile best{128, 128};
+    double best_t = 1e300;
+    for (const Cand& c : cands) {
+        const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const long waves = (tiles + 255) / 256;
+        const double t = (double)waves * c.bm * c.bn * c.cost;
+        if (t < best_t - 1e-9) { best_t = t; best = GemmTile{c.bm, c.bn}; }
+    }
+    return best;
+}
+
+// TPSHARD_GEMM_TILE=<bm>x<bn> (one of the compiled shapes) overrides the choice: a tuning
+// and test knob for sweeping tile shapes; unknown values are ignored.
+static bool tile_override(GemmTile& t)
+{
+    const char* e = std::getenv("TPSHARD_GEMM_TILE");
+    if (!e) return false;
+    int bm = 0, bn = 0;
+    if (std::sscanf(e, "%dx%d", &bm, &bn) != 2) return false;
+    const bool known = (bm == 256 && (bn == 256 || bn == 192 || bn == 128)) ||
+                       (bm == 128 && bn == 128);
+    if (known) t = GemmTile{bm, bn};
+    return known;
+}
+
+hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
+{
+    GemmTile t = gemm_bf16_pick_tile(p.M, p.N, p.K);
+    tile_override(t);
+    if (t.bm == 256 && t.bn == 256) return launch_bf16<256, 256>(p, epi, s);
+    if (t.bm == 256 && t.bn == 192) return launch_bf16<256, 192>(p, epi, s);
+    if (t.bm == 256 && t.bn == 128) return launch_bf16<256, 128>(p, epi, s);
+    return launch_bf16<128, 128>(p, epi, s);
+}
+
+hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)
+{
+    constexpr int BM = 32, BN = 64;
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    dim3 grid(tiles), block(kThreads);
+    switch (epi) {
+        case Epi::BiasGelu:
+            hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, Epi::BiasGelu>), grid, block, 0, s, p);
+            break;
+        case Epi::F32:
+            hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, Epi::F32>), grid, block, 0, s, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tps

@@ -1,0 +1,55 @@
+// kernels.hpp -- internal launch interface between the C ABI (tp_shard_abi.hip) and the
+// gfx950 kernels. Shapes reaching these functions have been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tps {
+
+// Output stage of the tensor-core GEMM C[m, n] = sum_k A[m, k] * B[n, k].
+enum class Epi : int {
+    BiasGelu = 0,   // C = GeLU(acc + bias[n])  stored in the GEMM's element type (Y_i)
+    F32 = 1,        // C = acc                   stored as fp32 (row-parallel partial Z_i)
+    Qkv = 2,        // acc + bias[n] scattered to Q / K / V^T per head, bf16
+};
+
+struct GemmProblem {
+    const void* A;        // [M, K] row-major, leading dimension lda (elements)
+    const void* B;        // [N, K] row-major (weight in [out, in] layout), ldb
+    const void* bias;     // [N] or nullptr
+    void* C;              // [M, N] row-major, ldc (BiasGelu / F32)
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    // Qkv scatter: column n = which * Hl*d + head * d + j, row m = b * seq + s
+    void* q;              // [batch, Hl, seq, d]
+    void* k;              // [batch, Hl, seq, d]
+    void* vt;             // [batch, Hl, d, ld_vt]
+    int seq, heads_local, head_dim;
+    int64_t ld_vt;
+};
+
+// Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).
+struct GemmTile { int bm, bn; };
+
+GemmTile gemm_bf16_pick_tile(int M, int N, int K);
+hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t stream);
+hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t stream);
+
+struct AttnProblem {
+    const void* q;        // [batch, Hl, seq, d] bf16
+    const void* k;        // [batch, Hl, seq, d] bf16
+    const void* vt;       // [batch, Hl, d, ld_vt] bf16
+    void* o;              // [batch * seq, Hl * d] bf16
+    int batch, heads_local, seq, head_dim;
+    int64_t ld_vt;
+    int causal;
+    float scale_log2;     // log2(e) / sqrt(d)
+};
+
+hipError_t attention_fwd(const AttnProblem& p, hipStream_t stream);
+
+hipError_t sum_partials(const float* const* parts, int n_parts, int64_t numel, void* out,
+                        bool out_bf16, hipStream_t stream);
+
+}  // namespace tps

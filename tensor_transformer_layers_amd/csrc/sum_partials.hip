@@ -1,0 +1,116 @@
+// sum_partials.hip -- Z = Z_0 + ... + Z_{N-1}: the single-device stand-in for the
+// tensor-parallel all-reduce (llms.blog, Row-Parallel Linear Layer: the true output is the
+// sum of the N partial products, formed by an all-reduce sum).
+//
+// Pure HBM streaming: each element is read once from every partial and written once, so the
+// kernel is bound by (N + 1) x numel x 4 bytes of traffic. Each lane handles 16-byte float4
+// vectors, grid-strided; all N loads of a vector are issued before the adds so that N
+// requests per lane are in flight. The adds run in the fixed order 0, 1, ..., N-1, so the
+// result is bitwise reproducible. Reads and writes are non-temporal: every byte is touched
+// exactly once.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tps {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxParts = 64;
+
+struct Parts {
+    const float* p[kMaxParts];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void put4(void* out, int64_t i4, f32x4 v)
+{
+    if constexpr (BF16) {
+        bf16x4* o = reinterpret_cast<bf16x4*>(out) + i4;
+        __builtin_nontemporal_store(to_bf16x4(v), o);
+    } else {
+        f32x4* o = reinterpret_cast<f32x4*>(out) + i4;
+        __builtin_nontemporal_store(v, o);
+    }
+}
+
+// NP > 0: compile-time part count (fully unrolled); NP == 0: runtime count n.
+template <int NP, bool BF16>
+__global__ __launch_bounds__(kThreads) void sum_kernel(Parts parts, int n, int64_t n4, void* out)
+{
+    const int np = NP > 0 ? NP : n;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+        f32x4 acc;
+        if constexpr (NP > 0) {
+            f32x4 v[NP];
+#pragma unroll
+            for (int r = 0; r < NP; ++r)
+                v[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[r]) + i);
+            acc = v[0];
+#pragma unroll
+            for (int r = 1; r < NP; ++r) acc += v[r];
+        } else {
+            acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + i);
+            for (int r = 1; r < np; ++r)
+                acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[r]) + i);
+        }
+        put4<BF16>(out, i, acc);
+    }
+}
+
+// The numel % 4 trailing elements.
+template <bool BF16>
+__global__ void sum_tail_kernel(Parts parts, int n, int64_t start, int64_t numel, void* out)
+{
+    const int64_t i = start + threadIdx.x;
+    if (i >= numel) return;
+    float acc = parts.p[0][i];
+    for (int r = 1; r < n; ++r) acc += parts.p[r][i];
+    if constexpr (BF16)
+        reinterpret_cast<bf16*>(out)[i] = to_bf16(acc);
+    else
+        reinterpret_cast<float*>(out)[i] = acc;
+}
+
+template <bool BF16>
+hipError_t launch(const Parts& parts, int n, int64_t numel, void* out, hipStream_t s)
+{
+    const int64_t n4 = numel / 4;
+    if (n4 > 0) {
+        // Enough workgroups to keep every CU's queues full: 256 CUs x 8 groups.
+        const int64_t want = (n4 + kThreads - 1) / kThreads;
+        const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
+        switch (n) {
+#define TPS_CASE(K) \
+    case K: hipLaunchKernelGGL((sum_kernel<K, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n, n4, out); break;
+            TPS_CASE(1) TPS_CASE(2) TPS_CASE(3) TPS_CASE(4)
+            TPS_CASE(5) TPS_CASE(6) TPS_CASE(7) TPS_CASE(8)
+#undef TPS_CASE
+            default:
+                hipLaunchKernelGGL((sum_kernel<0, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n,
+                                   n4, out);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (numel % 4) {
+        hipLaunchKernelGGL((sum_tail_kernel<BF16>), dim3(1), dim3(4), 0, s, parts, n, n4 * 4, numel,
+                           out);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t sum_partials(const float* const* parts, int n_parts, int64_t numel, void* out,
+                        bool out_bf16, hipStream_t s)
+{
+    if (n_parts < 1 || n_parts > kMaxParts) return hipErrorInvalidValue;
+    Parts pp{};
+    for (int r = 0; r < n_parts; ++r) pp.p[r] = parts[r];
+    return out_bf16 ? launch<true>(pp, n_parts, numel, out, s)
+                    : launch<false>(pp, n_parts, numel, out, s);
+}
+
+}  // namespace tps

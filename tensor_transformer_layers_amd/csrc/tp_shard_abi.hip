@@ -1,0 +1,281 @@
+// tp_shard_abi.hip -- the extern "C" boundary of libtpshard (declared in include/tp_shard.h).
+//
+// Every entry point validates its arguments on the host before any HIP call, returns a
+// tp_status and records a message for tp_last_error(); no exception crosses the boundary.
+// Valid calls enqueue the kernels on the caller's stream and return without synchronising.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/tp_shard.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tp_status fail(tp_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+tp_status ok()
+{
+    g_err[0] = '\0';
+    return TP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t dt_size(tp_dtype dt) { return dt == TP_F32 ? 4 : 2; }
+
+// The kernels are built for gfx950 only; check the current device once per device ordinal.
+tp_status check_device()
+{
+    static std::mutex mu;
+    static int checked[64] = {0};   // 0 unknown, 1 ok, 2 wrong arch
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(TP_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (checked[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(TP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        checked[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (checked[dev] == 2)
+            return fail(TP_ERR_DEVICE, "device %d is %s; libtpshard is built for gfx950 only", dev,
+                        prop.gcnArchName);
+    }
+    if (checked[dev] == 2) return fail(TP_ERR_DEVICE, "device %d is not gfx950", dev);
+    return TP_OK;
+}
+
+tp_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---- MLP --------------------------------------------------------------------------------
+tp_status validate_mlp_sizes(int64_t tokens, int64_t hidden, int64_t ffn, int n, tp_dtype dt)
+{
+    if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "MLP dtype %d not supported", (int)dt);
+    if (n < 1) return fail(TP_ERR_SHAPE, "n_shards %d < 1", n);
+    if (tokens < 1 || hidden < 1 || ffn < 1)
+        return fail(TP_ERR_SHAPE, "tokens=%lld hidden=%lld ffn=%lld must be >= 1", (long long)tokens,
+                    (long long)hidden, (long long)ffn);
+    if (ffn % n != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "ffn=%lld not divisible by n_shards=%d", (long long)ffn, n);
+    if (tokens > INT32_MAX || hidden > INT32_MAX || ffn > INT32_MAX)
+        return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
+    if (hidden % 8 != 0 || (ffn / n) % 8 != 0)
+        return fail(TP_ERR_ALIGN, "hidden=%lld and ffn/N=%lld must be multiples of 8",
+                    (long long)hidden, (long long)(ffn / n));
+    return TP_OK;
+}
+
+// ---- attention ---------------------------------------------------------------------------
+struct AttnLayout {
+    int hl, d;
+    int64_t ld_vt;
+    size_t q, k, vt, o, total;
+};
+
+tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_heads, int n,
+                              tp_dtype dt, AttnLayout* L)
+{
+    if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports TP_BF16 only (got %d)", (int)dt);
+    if (n < 1) return fail(TP_ERR_SHAPE, "n_shards %d < 1", n);
+    if (batch < 1 || seq < 1 || hidden < 1 || n_heads < 1)
+        return fail(TP_ERR_SHAPE, "batch, seq, hidden and n_heads must be >= 1");
+    if (batch * seq > INT32_MAX || hidden > INT32_MAX)
+        return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
+    if (hidden % n_heads != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "hidden=%lld not divisible by n_heads=%d", (long long)hidden,
+                    n_heads);
+    if (n_heads % n != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d not divisible by n_shards=%d", n_heads, n);
+    const int64_t d = hidden / n_heads;
+    if (d != 64 && d != 128) return fail(TP_ERR_SHAPE, "head dim %lld not supported (64 or 128)", (long long)d);
+    if (hidden % 8 != 0) return fail(TP_ERR_ALIGN, "hidden=%lld must be a multiple of 8", (long long)hidden);
+    L->hl = n_heads / n;
+    L->d = (int)d;
+    L->ld_vt = (int64_t)round_up((size_t)seq, 8);
+    const size_t head_elems = (size_t)batch * L->hl * seq * d;
+    L->q = 0;
+    L->k = round_up(L->q + head_elems * 2, 256);
+    L->vt = round_up(L->k + head_elems * 2, 256);
+    L->o = round_up(L->vt + (size_t)batch * L->hl * d * L->ld_vt * 2, 256);
+    L->total = round_up(L->o + (size_t)batch * seq * L->hl * d * 2, 256);
+    return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_SHARD_ABI_VERSION; }
+
+const char* tp_last_error(void) { return g_err; }
+
+size_t tp_mlp_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, tp_dtype dt)
+{
+    if (validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt) != TP_OK) return 0;
+    return round_up((size_t)tokens * (size_t)(ffn / n_shards) * dt_size(dt), 256);
+}
+
+tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                           float* Z_i, int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                           int rank, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                           void* stream)
+{
+    if (!X || !A_i || !B_i || !Z_i) return fail(TP_ERR_NULL, "X, A_i, B_i and Z_i must be non-NULL");
+    tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Z_i) ||
+        (a_i && !aligned16(a_i)) || (workspace && !aligned16(workspace)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t need = tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    st = check_device();
+    if (st != TP_OK) return st;
+
+    const int64_t fl = ffn / n_shards;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // Column-parallel: Y_i = GeLU(X A_i + a_i), [tokens, F/N] (no communication).
+    tps::GemmProblem g1{};
+    g1.A = X; g1.lda = hidden;
+    g1.B = A_i; g1.ldb = hidden;
+    g1.bias = a_i;
+    g1.C = workspace; g1.ldc = fl;
+    g1.M = (int)tokens; g1.N = (int)fl; g1.K = (int)hidden;
+    // Row-parallel: Z_i = Y_i B_i, [tokens, hidden] fp32 partial.
+    tps::GemmProblem g2{};
+    g2.A = workspace; g2.lda = fl;
+    g2.B = B_i; g2.ldb = fl;
+    g2.C = Z_i; g2.ldc = hidden;
+    g2.M = (int)tokens; g2.N = (int)hidden; g2.K = (int)fl;
+    hipError_t e;
+    if (dt == TP_BF16) {
+        e = tps::gemm_bf16(g1, tps::Epi::BiasGelu, s);
+        if (e == hipSuccess) e = tps::gemm_bf16(g2, tps::Epi::F32, s);
+    } else {
+        e = tps::gemm_f32(g1, tps::Epi::BiasGelu, s);
+        if (e == hipSuccess) e = tps::gemm_f32(g2, tps::Epi::F32, s);
+    }
+    return hip_status(e, "MLP shard kernel launch");
+}
+
+size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                               int n_shards, tp_dtype dt)
+{
+    AttnLayout L;
+    if (validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L) != TP_OK) return 0;
+    return L.total;
+}
+
+tp_status tp_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                   int n_shards, tp_dtype dt, size_t* q_off, size_t* k_off,
+                                   size_t* vt_off, size_t* o_off)
+{
+    AttnLayout L;
+    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L);
+    if (st != TP_OK) return st;
+    if (q_off) *q_off = L.q;
+    if (k_off) *k_off = L.k;
+    if (vt_off) *vt_off = L.vt;
+    if (o_off) *o_off = L.o;
+    return ok();
+}
+
+tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                            const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
+                            int64_t hidden, int n_heads, int causal, int n_shards, int rank,
+                            tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!X || !Wqkv_i || !Wo_i || !Z_i)
+        return fail(TP_ERR_NULL, "X, Wqkv_i, Wo_i and Z_i must be non-NULL");
+    AttnLayout L;
+    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(Wqkv_i) || !aligned16(Wo_i) || !aligned16(Z_i) ||
+        (bqkv_i && !aligned16(bqkv_i)) || (workspace && !aligned16(workspace)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    if (!workspace || workspace_bytes < L.total)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    st = check_device();
+    if (st != TP_OK) return st;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = reinterpret_cast<char*>(workspace);
+    const int T = (int)(batch * seq);
+    const int w = L.hl * L.d;   // local width h / N
+    // 1. Column-parallel QKV projection of the local heads, scattered per head (V transposed).
+    tps::GemmProblem g{};
+    g.A = X; g.lda = hidden;
+    g.B = Wqkv_i; g.ldb = hidden;
+    g.bias = bqkv_i;
+    g.M = T; g.N = 3 * w; g.K = (int)hidden;
+    g.q = ws + L.q; g.k = ws + L.k; g.vt = ws + L.vt;
+    g.seq = (int)seq; g.heads_local = L.hl; g.head_dim = L.d; g.ld_vt = L.ld_vt;
+    hipError_t e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
+    if (e != hipSuccess) return hip_status(e, "QKV projection launch");
+    // 2. Head-local attention; heads concatenated locally into O_i.
+    tps::AttnProblem a{};
+    a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;
+    a.batch = (int)batch; a.heads_local = L.hl; a.seq = (int)seq; a.head_dim = L.d;
+    a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
+    a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    e = tps::attention_fwd(a, s);
+    if (e != hipSuccess) return hip_status(e, "attention launch");
+    // 3. Row-parallel output projection: Z_i = O_i W_O,i (fp32 partial).
+    tps::GemmProblem g3{};
+    g3.A = ws + L.o; g3.lda = w;
+    g3.B = Wo_i; g3.ldb = w;
+    g3.C = Z_i; g3.ldc = hidden;
+    g3.M = T; g3.N = (int)hidden; g3.K = w;
+    e = tps::gemm_bf16(g3, tps::Epi::F32, s);
+    return hip_status(e, "output projection launch");
+}
+
+tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel, void* Z,
+                          tp_dtype out_dt, void* stream)
+{
+    if (!Z_parts || !Z) return fail(TP_ERR_NULL, "Z_parts and Z must be non-NULL");
+    if (n_parts < 1 || n_parts > 64)
+        return fail(TP_ERR_SHAPE, "n_parts=%d outside [1, 64]", n_parts);
+    if (numel < 1) return fail(TP_ERR_SHAPE, "numel=%lld must be >= 1", (long long)numel);
+    if (out_dt != TP_F32 && out_dt != TP_BF16)
+        return fail(TP_ERR_DTYPE, "out_dt %d not supported", (int)out_dt);
+    for (int r = 0; r < n_parts; ++r) {
+        if (!Z_parts[r]) return fail(TP_ERR_NULL, "partial %d is NULL (missing rank)", r);
+        if (!aligned16(Z_parts[r])) return fail(TP_ERR_ALIGN, "partial %d is not 16-byte aligned", r);
+    }
+    if (!aligned16(Z)) return fail(TP_ERR_ALIGN, "Z is not 16-byte aligned");
+    tp_status st = check_device();
+    if (st != TP_OK) return st;
+    hipError_t e = tps::sum_partials(Z_parts, n_parts, numel, Z, out_dt == TP_BF16,
+                                     reinterpret_cast<hipStream_t>(stream));
+    return hip_status(e, "sum kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+"""PyTorch-facing calls of one tensor-parallel rank's shard.
+
+PyTorch supplies device memory and streams only: these functions allocate outputs and
+workspaces with torch and pass pointers to the C ABI (``binding``). Every arithmetic step
+runs in libtpshard's HIP kernels.
+
+* ``mlp_shard``       Z_i = GeLU(X A_i + a_i) B_i            (tp_mlp_shard_fwd)
+* ``attn_shard``      Z_i = concat_j Head_j  W_O,i            (tp_attn_shard_fwd)
+* ``sum_partials``    Z = sum_r Z_r, the all-reduce stand-in  (tp_sum_partials)
+* ``layer_shard``     one rank's layer: attention partial, sum over the N partials,
+                      MLP partial on that sum, sum again -- one sum per block, as the
+                      pages count one all-reduce per block in the forward pass.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+_DT = {torch.float32: B.TP_F32, torch.bfloat16: B.TP_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+# ---- MLP ------------------------------------------------------------------------------------
+def mlp_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, dtype, device="cuda"):
+    nbytes = B.tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, _DT[dtype])
+    if nbytes == 0:
+        raise B.TPError(B.TP_ERR_SHAPE, B.tp_last_error())
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mlp_hidden_view(workspace: torch.Tensor, tokens: int, ffn_local: int, dtype) -> torch.Tensor:
+    """Y_i = GeLU(X A_i + a_i), [tokens, ffn/N], stored at offset 0 of the MLP workspace."""
+    esz = torch.tensor([], dtype=dtype).element_size()
+    return workspace[: tokens * ffn_local * esz].view(dtype).view(tokens, ffn_local)
+
+
+def mlp_shard(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor], B_i: torch.Tensor,
+              n_shards: int, rank: int, Z: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """Rank ``rank``'s MLP partial. A_i [F/N, h], B_i [h, F/N] (see include/tp_shard.h).
+
+    Returns (Z_i fp32 [tokens, hidden], workspace).
+    """
+    _require_cuda(X, A_i, a_i, B_i)
+    tokens, hidden = X.shape
+    fl = A_i.shape[0]
+    ffn = fl * n_shards
+    dt = _dt(X)
+    if Z is None:
+        Z = torch.empty(tokens, hidden, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = mlp_workspace(tokens, hidden, ffn, n_shards, X.dtype, X.device)
+    st = B.tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z, tokens, hidden, ffn, n_shards, rank, dt,
+                            workspace, workspace.numel(), _stream(stream))
+    B.check(st)
+    return Z, workspace
+
+
+# ---- attention ---------------------------------------------------------------------------
+def attn_workspace(batch: int, seq: int, hidden: int, n_heads: int, n_shards: int, device="cuda"):
+    nbytes = B.tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, B.TP_BF16)
+    if nbytes == 0:
+        st, _ = B.tp_attn_workspace_layout(batch, seq, hidden, n_heads, n_shards, B.TP_BF16)
+        B.check(st)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_views(workspace: torch.Tensor, batch: int, seq: int, hidden: int, n_heads: int,
+               n_shards: int) -> Dict[str, torch.Tensor]:
+    """Views of the attention workspace: q, k [b, Hl, s, d], vt [b, Hl, d, ld_vt], o [b*s, Hl*d]."""
+    st, off = B.tp_attn_workspace_layout(batch, seq, hidden, n_heads, n_shards, B.TP_BF16)
+    B.check(st)
+    hl = n_heads // n_shards
+    d = hidden // n_heads
+    ld_vt = (seq + 7) // 8 * 8
+
+    def view(o, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        return workspace[o:o + 2 * n].view(torch.bfloat16).view(*shape)
+
+    return dict(q=view(off["q"], (batch, hl, seq, d)), k=view(off["k"], (batch, hl, seq, d)),
+                vt=view(off["vt"], (batch, hl, d, ld_vt)), o=view(off["o"], (batch * seq, hl * d)))
+
+
+def attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch.Tensor],
+               Wo_i: torch.Tensor, batch: int, seq: int, n_heads: int, n_shards: int, rank: int,
+               causal: bool = True, Z: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Rank ``rank``'s attention partial. Returns (Z_i fp32 [batch*seq, hidden], workspace)."""
+    _require_cuda(X, Wqkv_i, bqkv_i, Wo_i)
+    hidden = X.shape[1]
+    if Z is None:
+        Z = torch.empty(batch * seq, hidden, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = attn_workspace(batch, seq, hidden, n_heads, n_shards, X.device)
+    st = B.tp_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z, batch, seq, hidden, n_heads, causal,
+                             n_shards, rank, _dt(X), workspace, workspace.numel(),
+                             _stream(stream))
+    B.check(st)
+    return Z, workspace
+
+
+# ---- partial sum ------------------------------------------------------------------------------
+def sum_partials(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _require_cuda(*parts)
+    numel = parts[0].numel()
+    if out is None:
+        out = torch.empty(parts[0].shape, dtype=out_dtype, device=parts[0].device)
+    st = B.tp_sum_partials(list(parts), len(parts), numel, out, _DT[out.dtype], _stream(stream))
+    B.check(st)
+    return out
+
+
+# ---- one rank's Transformer layer ------------------------------------------------------------
+class LayerShard:
+    """Rank ``rank`` of an N-way tensor-parallel layer: attention block then MLP block.
+
+    The other ranks' partials are supplied by the caller (on one device they are computed
+    by running the other shards); each block ends in exactly one partial sum. Buffers are
+    allocated once so that repeated calls allocate nothing.
+    """
+
+    def __init__(self, batch: int, seq: int, hidden: int, n_heads: int, ffn: int,
+                 n_shards: int, rank: int, causal: bool = True, device="cuda"):
+        self.batch, self.seq, self.hidden = batch, seq, hidden
+        self.n_heads, self.ffn, self.n_shards, self.rank = n_heads, ffn, n_shards, rank
+        self.causal = causal
+        T = batch * seq
+        self.attn_ws = attn_workspace(batch, seq, hidden, n_heads, n_shards, device)
+        self.mlp_ws = mlp_workspace(T, hidden, ffn, n_shards, torch.bfloat16, device)
+        self.Z_attn = torch.empty(T, hidden, dtype=torch.float32, device=device)
+        self.H = torch.empty(T, hidden, dtype=torch.bfloat16, device=device)
+        self.Z_mlp = torch.empty(T, hidden, dtype=torch.float32, device=device)
+        self.out = torch.empty(T, hidden, dtype=torch.float32, device=device)
+
+    def forward(self, X, Wqkv_i, bqkv_i, Wo_i, A_i, a_i, B_i,
+                attn_partials_other: List[torch.Tensor], mlp_partials_other: List[torch.Tensor],
+                stream=None) -> torch.Tensor:
+        """attn partial -> H = bf16(sum of N attention partials) -> MLP partial on H -> sum."""
+        r = self.rank
+        attn_shard(X, Wqkv_i, bqkv_i, Wo_i, self.batch, self.seq, self.n_heads, self.n_shards, r,
+                   self.causal, Z=self.Z_attn, workspace=self.attn_ws, stream=stream)
+        parts = list(attn_partials_other)
+        parts.insert(r, self.Z_attn)
+        sum_partials(parts, out=self.H, stream=stream)
+        mlp_shard(self.H, A_i, a_i, B_i, self.n_shards, r, Z=self.Z_mlp, workspace=self.mlp_ws,
+                  stream=stream)
+        parts = list(mlp_partials_other)
+        parts.insert(r, self.Z_mlp)
+        sum_partials(parts, out=self.out, stream=stream)
+        return self.out

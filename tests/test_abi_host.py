@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every declared symbol,
+and its validation rejects bad arguments with the documented status before any HIP call.
+
+The pointers passed here are fake non-NULL values: every call is expected to fail
+validation, so none of them is ever dereferenced and no kernel is launched.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from tensor_transformer_layers_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+P = 0x10000          # a fake, 16-byte aligned, non-NULL address (never dereferenced)
+BIG = 1 << 40        # "large enough" workspace size
+BF16, F32 = B.TP_BF16, B.TP_F32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(B.LIB_PATH):
+        from tensor_transformer_layers_amd import build
+        build.build()
+    B.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(B.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tp_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(B.lib(), f)
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define TP_SHARD_ABI_VERSION (\d+)", text).group(1))
+    assert B.tp_abi_version() == v
+
+
+def _mlp(**kw):
+    a = dict(X=P, A_i=P, a_i=P, B_i=P, Z_i=P, tokens=32, hidden=1024, ffn=4096, n_shards=2,
+             rank=0, dt=F32, workspace=P, workspace_bytes=BIG)
+    a.update(kw)
+    return B.tp_mlp_shard_fwd(**a)
+
+
+def _attn(**kw):
+    a = dict(X=P, Wqkv_i=P, bqkv_i=None, Wo_i=P, Z_i=P, batch=4, seq=2048, hidden=4096,
+             n_heads=32, causal=1, n_shards=8, rank=0, dt=BF16, workspace=P,
+             workspace_bytes=BIG)
+    a.update(kw)
+    return B.tp_attn_shard_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), 1), (dict(A_i=None), 1), (dict(B_i=None), 1), (dict(Z_i=None), 1),
+    (dict(n_shards=3), 3),                 # 4096 % 3 != 0 (pages only use exact shards)
+    (dict(n_shards=0), 2), (dict(tokens=0), 2), (dict(hidden=-1), 2),
+    (dict(rank=2), 4), (dict(rank=-1), 4),
+    (dict(dt=7), 5),
+    (dict(X=P + 8), 6), (dict(a_i=P + 4), 6), (dict(hidden=1020), 6),
+    (dict(ffn=4096 + 2 * 4), 6),           # ffn/N = 2052 is not a multiple of 8
+    (dict(workspace=None), 7), (dict(workspace_bytes=100), 7),
+])
+def test_mlp_validation(kw, status):
+    assert _mlp(**kw) == status
+    assert B.tp_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), 1), (dict(Wqkv_i=None), 1), (dict(Wo_i=None), 1), (dict(Z_i=None), 1),
+    (dict(n_heads=30), 3),                 # 4096 % 30 != 0
+    (dict(n_shards=3), 3),                 # 32 heads over 3 ranks
+    (dict(n_heads=16), 2),                 # d = 256: unsupported head width
+    (dict(rank=8), 4),
+    (dict(dt=F32), 5),
+    (dict(bqkv_i=P + 2), 6),
+    (dict(workspace_bytes=1), 7),
+    (dict(seq=0), 2),
+])
+def test_attn_validation(kw, status):
+    assert _attn(**kw) == status
+    assert B.tp_last_error() != ""
+
+
+def test_sum_validation():
+    assert B.tp_sum_partials([P, P], 0, 10, P, F32) == 2
+    assert B.tp_sum_partials([P] * 65, 65, 10, P, F32) == 2
+    assert B.tp_sum_partials([P, P], 2, 0, P, F32) == 2
+    assert B.tp_sum_partials([P, None, P], 3, 10, P, F32) == 1   # a missing rank
+    assert "partial 1" in B.tp_last_error()
+    assert B.tp_sum_partials([P, P + 4], 2, 10, P, F32) == 6
+    assert B.tp_sum_partials([P, P], 2, 10, P, 3) == 5
+    assert B.tp_sum_partials([P, P], 2, 10, None, F32) == 1
+
+
+def test_workspace_sizes():
+    # MLP: Y_i [tokens, ffn/N] of the element type, rounded up to 256 bytes
+    assert B.tp_mlp_workspace_bytes(32, 1024, 4096, 2, F32) == 32 * 2048 * 4
+    assert B.tp_mlp_workspace_bytes(8192, 3072, 12288, 8, BF16) == 8192 * 1536 * 2
+    assert B.tp_mlp_workspace_bytes(3, 8, 16, 2, BF16) == 256
+    assert B.tp_mlp_workspace_bytes(32, 1024, 4096, 3, F32) == 0
+    # attention: Q, K, V^T (seq padded to 8), O, each 256-byte aligned
+    st, off = B.tp_attn_workspace_layout(4, 2048, 4096, 32, 8, BF16)
+    assert st == 0
+    e = 4 * 4 * 2048 * 128 * 2
+    assert off == dict(q=0, k=e, vt=2 * e, o=3 * e)
+    assert B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16) == 4 * e
+    st, off = B.tp_attn_workspace_layout(1, 5, 256, 2, 1, BF16)
+    # 2 heads of d = 128, seq 5: Q and K are 2560 bytes; V^T rows are padded to 8 keys
+    assert st == 0 and off == dict(q=0, k=2560, vt=5120, o=5120 + 2 * 128 * 8 * 2)
+    assert B.tp_attn_workspace_bytes(1, 5, 256, 2, 1, F32) == 0

@@ -1,0 +1,70 @@
+"""GPU parity of tp_sum_partials, the on-device stand-in for the all-reduce sum."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import canary_tensor, dev, host, torch_cuda
+from synth import partials_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(P, out_dtype_name="f32", alias=False):
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    parts = [dev(p, "f32") for p in P]
+    odt = torch.float32 if out_dtype_name == "f32" else torch.bfloat16
+    if alias:
+        out = shard.sum_partials(parts, out=parts[0])
+        return host(out), None
+    c = canary_tensor((P.shape[1],), odt)
+    shard.sum_partials(parts, out=c.tensor)
+    torch.cuda.synchronize()
+    return host(c.tensor), c
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8, 13, 64])
+@pytest.mark.parametrize("numel", [1, 3, 4, 4099, 1 << 20])
+def test_sum_integer_partials_exact(n, numel):
+    """Integer-valued partials: any summation order is exact, so the result must be too."""
+    if n * numel > 8 << 20:
+        numel = (8 << 20) // n + 3
+    P = partials_inputs(n, numel, seed=n * 31 + numel, integer=True)
+    got, c = _run(P)
+    assert c.intact(), "write outside the output buffer"
+    assert np.array_equal(got, oracle.sum_partials(P))
+
+
+def test_sum_float_partials_against_oracle_and_repeatable():
+    P = partials_inputs(8, 3 * (1 << 20) + 5, seed=3)
+    ref = oracle.sum_partials(P)
+    got, c = _run(P)
+    assert c.intact()
+    err = oracle.rel_frobenius(got, ref)
+    print("sum fp32 rel err %.3e" % err)
+    assert err < 1e-6
+    got2, _ = _run(P)
+    assert np.array_equal(got, got2)
+
+
+def test_sum_bf16_output():
+    P = partials_inputs(4, (1 << 18) + 2, seed=4)
+    ref = oracle.sum_partials(P)
+    got, c = _run(P, "bf16")
+    assert c.intact()
+    err = oracle.rel_frobenius(got, ref)
+    print("sum bf16 rel err %.3e" % err)
+    assert err < 1e-2
+    # small integers are exact in bf16
+    Pi = partials_inputs(3, 1001, seed=5, integer=True) / 10.0
+    Pi = np.round(Pi).astype(np.float32)
+    got_i, _ = _run(Pi, "bf16")
+    ref_i = oracle.sum_partials(Pi)
+    small = np.abs(ref_i) <= 256
+    assert np.array_equal(got_i[small], ref_i[small])
+
+
+def test_sum_in_place_on_first_partial():
+    P = partials_inputs(3, 10007, seed=6, integer=True)
+    got, _ = _run(P, alias=True)
+    assert np.array_equal(got, oracle.sum_partials(P))
