@@ -70,6 +70,43 @@ typedef enum {
     TP_ERR_DEVICE = 9          /* the current device is not gfx950                         */
 } tp_status;
 
+typedef enum {
+    TP_ACT_NONE = 0,   /* identity                                     */
+    TP_ACT_GELU = 1    /* exact GeLU, x * Phi(x) = x/2 (1 + erf(x/sqrt 2)) */
+} tp_activation;
+
+/* ------------------------------------------------------------------------------------------
+ * Column-parallel linear layer of rank r (llms.blog, "The Core Primitives", 1. Column-Parallel
+ * Linear Layer): W = [W_1 ... W_N] split on its output dimension, the replicated X times the
+ * rank's slice, no communication; an element-wise activation applies to the local slice.
+ *   Y_i = act(X W_i + b_i)
+ *
+ *   X    [rows, in_features]          dt   replicated input
+ *   W_i  [out_features/N, in_features] dt   W_i[j][k] = W[k][rank*out_features/N + j]
+ *   b_i  [out_features/N]             dt   or NULL for no bias
+ *   Y_i  [rows, out_features/N]       dt
+ * dt: TP_F32 or TP_BF16. in_features and out_features/N must be multiples of 8.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_column_parallel_fwd(const void* X, const void* W_i, const void* b_i, void* Y_i,
+                                 int64_t rows, int64_t in_features, int64_t out_features,
+                                 int n_shards, int rank, tp_activation act, tp_dtype dt,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Row-parallel linear layer of rank r (same page, 2. Row-Parallel Linear Layer): W split on
+ * its input dimension, the rank's channel slice X_i of the input times W_i gives a partial
+ * that must be summed over the N ranks (tp_sum_partials).
+ *   Z_i = X_i W_i
+ *
+ *   X_i  [rows, in_features/N]        dt   the rank's channel slice (a column-parallel output)
+ *   W_i  [out_features, in_features/N] dt   W_i[o][j] = W[rank*in_features/N + j][o]
+ *   Z_i  [rows, out_features]         fp32 partial
+ * dt: TP_F32 or TP_BF16. in_features/N and out_features must be multiples of 8.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_row_parallel_fwd(const void* X_i, const void* W_i, float* Z_i, int64_t rows,
+                              int64_t in_features, int64_t out_features, int n_shards, int rank,
+                              tp_dtype dt, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * MLP shard: Z_i = GeLU(X A_i + a_i) B_i          (ai360xpert.com "How It Works", steps 1-2;
  *                                                  llms.blog MLP block, steps 1-3)
@@ -84,7 +121,8 @@ typedef enum {
  *   Z_i  [tokens, hidden]       fp32 rank's partial (to be summed over ranks)
  *   workspace: Y_i = GeLU(X A_i + a_i) [tokens, ffn/N] in dt at byte offset 0.
  * A row-parallel output bias, if a model has one, is added once after the sum, not here.
- * dt: TP_F32 or TP_BF16.
+ * dt: TP_F32 or TP_BF16. Equivalent to tp_column_parallel_fwd(TP_ACT_GELU) into the
+ * workspace followed by tp_row_parallel_fwd (the same two kernels).
  * ---------------------------------------------------------------------------------------- */
 size_t tp_mlp_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
                               tp_dtype dt);
@@ -151,7 +189,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 1
+#define TP_SHARD_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -5,13 +5,14 @@ of ``include/tp_shard.h``). This package holds its ctypes binding (``binding``),
 extraction helpers (``layout``) and the PyTorch-facing calls (``shard``). Importing the package
 does not load the library; the first call does, and raises if it has not been built.
 """
+import importlib
+
 from . import binding, layout  # noqa: F401
 
 __all__ = ["binding", "layout", "shard"]
 
 
 def __getattr__(name):
-    if name == "shard":
-        from . import shard
-        return shard
+    if name == "shard":   # imported lazily: it needs torch
+        return importlib.import_module(__name__ + ".shard")
     raise AttributeError(name)

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(PKG, "lib", "libtpshard.so")
 TP_F32 = 0
 TP_BF16 = 1
 TP_ERR_SHAPE = 2
+TP_ACT_NONE = 0
+TP_ACT_GELU = 1
 
 STATUS_NAMES = {
     0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_NOT_DIVISIBLE", 4: "TP_ERR_RANK",
@@ -26,7 +28,7 @@ STATUS_NAMES = {
 
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
-    "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd", "tp_attn_workspace_bytes",
+    "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_last_error",
     "tp_abi_version",
 )
@@ -60,6 +62,11 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     L.tp_abi_version.restype = _int
     L.tp_last_error.restype = ctypes.c_char_p
+    L.tp_column_parallel_fwd.restype = _int
+    L.tp_column_parallel_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                         _int, _vp]
+    L.tp_row_parallel_fwd.restype = _int
+    L.tp_row_parallel_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]
     L.tp_mlp_workspace_bytes.restype = _sz
     L.tp_mlp_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
     L.tp_mlp_shard_fwd.restype = _int
@@ -103,6 +110,19 @@ def tp_last_error() -> str:
 
 def tp_abi_version() -> int:
     return lib().tp_abi_version()
+
+
+def tp_column_parallel_fwd(X, W_i, b_i, Y_i, rows, in_features, out_features, n_shards, rank,
+                           act, dt, stream=None) -> int:
+    return lib().tp_column_parallel_fwd(_ptr(X), _ptr(W_i), _ptr(b_i), _ptr(Y_i), rows,
+                                        in_features, out_features, n_shards, rank, act, dt,
+                                        _stream(stream))
+
+
+def tp_row_parallel_fwd(X_i, W_i, Z_i, rows, in_features, out_features, n_shards, rank, dt,
+                        stream=None) -> int:
+    return lib().tp_row_parallel_fwd(_ptr(X_i), _ptr(W_i), _ptr(Z_i), rows, in_features,
+                                     out_features, n_shards, rank, dt, _stream(stream))
 
 
 def tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:

@@ -6,6 +6,7 @@
 // chunk of 8 bf16 (or 4 fp32) consecutive K values per lane. The output stage is fused:
 //   BiasGelu  Y_i = GeLU(X A_i + a_i)                   column-parallel MLP layer
 //   F32       Z_i = Y_i B_i  (fp32 partial)             row-parallel layers (MLP, W_O)
+//   Bias      Y = X W_i + b_i                           column-parallel, no activation
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
 //             per head, V written transposed for the attention kernel's P V product.
 //
@@ -66,9 +67,11 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
                 v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.bias) + n);
             }
         }
-        if constexpr (EPI == Epi::BiasGelu) {
+        if constexpr (EPI == Epi::BiasGelu || EPI == Epi::Bias) {
+            if constexpr (EPI == Epi::BiasGelu) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+                for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+            }
             if constexpr (sizeof(T) == 2) {
                 bf16* c = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc + n;
                 *reinterpret_cast<bf16x4*>(c) = to_bf16x4(v);
@@ -344,6 +347,9 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         case Epi::Qkv:
             hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::Qkv>), grid, block, 0, s, p);
             break;
+        case Epi::Bias:
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::Bias>), grid, block, 0, s, p);
+            break;
     }
     return hipGetLastError();
 }
@@ -403,6 +409,9 @@ hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)
             break;
         case Epi::F32:
             hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, Epi::F32>), grid, block, 0, s, p);
+            break;
+        case Epi::Bias:
+            hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, Epi::Bias>), grid, block, 0, s, p);
             break;
         default:
             return hipErrorInvalidValue;

@@ -12,6 +12,7 @@ enum class Epi : int {
     BiasGelu = 0,   // C = GeLU(acc + bias[n])  stored in the GEMM's element type (Y_i)
     F32 = 1,        // C = acc                   stored as fp32 (row-parallel partial Z_i)
     Qkv = 2,        // acc + bias[n] scattered to Q / K / V^T per head, bf16
+    Bias = 3,       // C = acc + bias[n]         stored in the GEMM's element type
 };
 
 struct GemmProblem {

@@ -86,6 +86,57 @@ tp_status validate_mlp_sizes(int64_t tokens, int64_t hidden, int64_t ffn, int n,
     return TP_OK;
 }
 
+// ---- column / row-parallel linear layers ---------------------------------------------------
+// column: split dimension is out_features; row: split dimension is in_features.
+tp_status validate_linear(int64_t rows, int64_t in_f, int64_t out_f, int n, int rank, tp_dtype dt,
+                          bool column)
+{
+    if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    if (n < 1) return fail(TP_ERR_SHAPE, "n_shards %d < 1", n);
+    if (rows < 1 || in_f < 1 || out_f < 1)
+        return fail(TP_ERR_SHAPE, "rows=%lld in=%lld out=%lld must be >= 1", (long long)rows,
+                    (long long)in_f, (long long)out_f);
+    if (rows > INT32_MAX || in_f > INT32_MAX || out_f > INT32_MAX)
+        return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
+    const int64_t split = column ? out_f : in_f;
+    if (split % n != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "%s_features=%lld not divisible by n_shards=%d",
+                    column ? "out" : "in", (long long)split, n);
+    if (rank < 0 || rank >= n) return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n);
+    const int64_t k = column ? in_f : in_f / n;     // reduced dimension
+    const int64_t w = column ? out_f / n : out_f;   // output width
+    if (k % 8 != 0 || w % 8 != 0)
+        return fail(TP_ERR_ALIGN, "reduced dimension %lld and output width %lld must be multiples of 8",
+                    (long long)k, (long long)w);
+    return TP_OK;
+}
+
+// Y[rows, width] = act(X[rows, k] W[width, k]^T + b)
+hipError_t launch_column(const void* X, const void* W, const void* b, void* Y, int64_t rows,
+                         int64_t k, int64_t width, tp_activation act, tp_dtype dt, hipStream_t s)
+{
+    tps::GemmProblem g{};
+    g.A = X; g.lda = k;
+    g.B = W; g.ldb = k;
+    g.bias = b;
+    g.C = Y; g.ldc = width;
+    g.M = (int)rows; g.N = (int)width; g.K = (int)k;
+    const tps::Epi epi = act == TP_ACT_GELU ? tps::Epi::BiasGelu : tps::Epi::Bias;
+    return dt == TP_BF16 ? tps::gemm_bf16(g, epi, s) : tps::gemm_f32(g, epi, s);
+}
+
+// Z[rows, width] (fp32) = X[rows, k] W[width, k]^T
+hipError_t launch_row(const void* X, const void* W, float* Z, int64_t rows, int64_t k,
+                      int64_t width, tp_dtype dt, hipStream_t s)
+{
+    tps::GemmProblem g{};
+    g.A = X; g.lda = k;
+    g.B = W; g.ldb = k;
+    g.C = Z; g.ldc = width;
+    g.M = (int)rows; g.N = (int)width; g.K = (int)k;
+    return dt == TP_BF16 ? tps::gemm_bf16(g, tps::Epi::F32, s) : tps::gemm_f32(g, tps::Epi::F32, s);
+}
+
 // ---- attention ---------------------------------------------------------------------------
 struct AttnLayout {
     int hl, d;
@@ -155,31 +206,49 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
                     workspace ? workspace_bytes : (size_t)0);
     st = check_device();
     if (st != TP_OK) return st;
-
-    const int64_t fl = ffn / n_shards;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // Column-parallel: Y_i = GeLU(X A_i + a_i), [tokens, F/N] (no communication).
-    tps::GemmProblem g1{};
-    g1.A = X; g1.lda = hidden;
-    g1.B = A_i; g1.ldb = hidden;
-    g1.bias = a_i;
-    g1.C = workspace; g1.ldc = fl;
-    g1.M = (int)tokens; g1.N = (int)fl; g1.K = (int)hidden;
+    hipError_t e = launch_column(X, A_i, a_i, workspace, tokens, hidden, ffn / n_shards,
+                                 TP_ACT_GELU, dt, s);
+    if (e != hipSuccess) return hip_status(e, "column-parallel kernel launch");
     // Row-parallel: Z_i = Y_i B_i, [tokens, hidden] fp32 partial.
-    tps::GemmProblem g2{};
-    g2.A = workspace; g2.lda = fl;
-    g2.B = B_i; g2.ldb = fl;
-    g2.C = Z_i; g2.ldc = hidden;
-    g2.M = (int)tokens; g2.N = (int)hidden; g2.K = (int)fl;
-    hipError_t e;
-    if (dt == TP_BF16) {
-        e = tps::gemm_bf16(g1, tps::Epi::BiasGelu, s);
-        if (e == hipSuccess) e = tps::gemm_bf16(g2, tps::Epi::F32, s);
-    } else {
-        e = tps::gemm_f32(g1, tps::Epi::BiasGelu, s);
-        if (e == hipSuccess) e = tps::gemm_f32(g2, tps::Epi::F32, s);
-    }
-    return hip_status(e, "MLP shard kernel launch");
+    e = launch_row(workspace, B_i, Z_i, tokens, ffn / n_shards, hidden, dt, s);
+    return hip_status(e, "row-parallel kernel launch");
+}
+
+tp_status tp_column_parallel_fwd(const void* X, const void* W_i, const void* b_i, void* Y_i,
+                                 int64_t rows, int64_t in_features, int64_t out_features,
+                                 int n_shards, int rank, tp_activation act, tp_dtype dt,
+                                 void* stream)
+{
+    if (!X || !W_i || !Y_i) return fail(TP_ERR_NULL, "X, W_i and Y_i must be non-NULL");
+    tp_status st = validate_linear(rows, in_features, out_features, n_shards, rank, dt, true);
+    if (st != TP_OK) return st;
+    if (act != TP_ACT_NONE && act != TP_ACT_GELU)
+        return fail(TP_ERR_SHAPE, "activation %d not supported", (int)act);
+    if (!aligned16(X) || !aligned16(W_i) || !aligned16(Y_i) || (b_i && !aligned16(b_i)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    st = check_device();
+    if (st != TP_OK) return st;
+    hipError_t e = launch_column(X, W_i, b_i, Y_i, rows, in_features, out_features / n_shards,
+                                 act, dt, reinterpret_cast<hipStream_t>(stream));
+    return hip_status(e, "column-parallel kernel launch");
+}
+
+tp_status tp_row_parallel_fwd(const void* X_i, const void* W_i, float* Z_i, int64_t rows,
+                              int64_t in_features, int64_t out_features, int n_shards, int rank,
+                              tp_dtype dt, void* stream)
+{
+    if (!X_i || !W_i || !Z_i) return fail(TP_ERR_NULL, "X_i, W_i and Z_i must be non-NULL");
+    tp_status st = validate_linear(rows, in_features, out_features, n_shards, rank, dt, false);
+    if (st != TP_OK) return st;
+    if (!aligned16(X_i) || !aligned16(W_i) || !aligned16(Z_i))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    st = check_device();
+    if (st != TP_OK) return st;
+    hipError_t e = launch_row(X_i, W_i, Z_i, rows, in_features / n_shards, out_features, dt,
+                              reinterpret_cast<hipStream_t>(stream));
+    return hip_status(e, "row-parallel kernel launch");
 }
 
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,

@@ -7,13 +7,14 @@ runs in libtpshard's HIP kernels.
 * ``mlp_shard``       Z_i = GeLU(X A_i + a_i) B_i            (tp_mlp_shard_fwd)
 * ``attn_shard``      Z_i = concat_j Head_j  W_O,i            (tp_attn_shard_fwd)
 * ``sum_partials``    Z = sum_r Z_r, the all-reduce stand-in  (tp_sum_partials)
-* ``layer_shard``     one rank's layer: attention partial, sum over the N partials,
+* ``column_parallel`` / ``row_parallel``  the two linear primitives on their own
+* ``LayerShard``      one rank's layer: attention partial, sum over the N partials,
                       MLP partial on that sum, sum again -- one sum per block, as the
                       pages count one all-reduce per block in the forward pass.
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence
+from typing import Callable, Dict, List, Optional, Sequence
 
 import torch
 
@@ -36,6 +37,37 @@ def _require_cuda(*ts):
 
 def _stream(stream):
     return torch.cuda.current_stream() if stream is None else stream
+
+
+# ---- column / row-parallel linear layers ----------------------------------------------------
+def column_parallel(X: torch.Tensor, W_i: torch.Tensor, b_i: Optional[torch.Tensor],
+                    n_shards: int, rank: int, gelu: bool = False, Y: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Y_i = act(X W_i + b_i), W_i [out/N, in] (tp_column_parallel_fwd)."""
+    _require_cuda(X, W_i, b_i)
+    rows, k = X.shape
+    width = W_i.shape[0]
+    if Y is None:
+        Y = torch.empty(rows, width, dtype=X.dtype, device=X.device)
+    st = B.tp_column_parallel_fwd(X, W_i, b_i, Y, rows, k, width * n_shards, n_shards, rank,
+                                  B.TP_ACT_GELU if gelu else B.TP_ACT_NONE, _dt(X),
+                                  _stream(stream))
+    B.check(st)
+    return Y
+
+
+def row_parallel(X_i: torch.Tensor, W_i: torch.Tensor, n_shards: int, rank: int,
+                 Z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Z_i = X_i W_i (fp32 partial), W_i [out, in/N] (tp_row_parallel_fwd)."""
+    _require_cuda(X_i, W_i)
+    rows, k = X_i.shape
+    width = W_i.shape[0]
+    if Z is None:
+        Z = torch.empty(rows, width, dtype=torch.float32, device=X_i.device)
+    st = B.tp_row_parallel_fwd(X_i, W_i, Z, rows, k * n_shards, width, n_shards, rank, _dt(X_i),
+                               _stream(stream))
+    B.check(st)
+    return Z
 
 
 # ---- MLP ------------------------------------------------------------------------------------
@@ -151,22 +183,35 @@ class LayerShard:
         self.mlp_ws = mlp_workspace(T, hidden, ffn, n_shards, torch.bfloat16, device)
         self.Z_attn = torch.empty(T, hidden, dtype=torch.float32, device=device)
         self.H = torch.empty(T, hidden, dtype=torch.bfloat16, device=device)
+        self.Y = torch.empty(T, ffn // n_shards, dtype=torch.bfloat16, device=device)
         self.Z_mlp = torch.empty(T, hidden, dtype=torch.float32, device=device)
         self.out = torch.empty(T, hidden, dtype=torch.float32, device=device)
 
+    STAGES = ("attention_shard", "sum_attention", "mlp_column", "mlp_row", "sum_mlp")
+
     def forward(self, X, Wqkv_i, bqkv_i, Wo_i, A_i, a_i, B_i,
                 attn_partials_other: List[torch.Tensor], mlp_partials_other: List[torch.Tensor],
-                stream=None) -> torch.Tensor:
-        """attn partial -> H = bf16(sum of N attention partials) -> MLP partial on H -> sum."""
-        r = self.rank
-        attn_shard(X, Wqkv_i, bqkv_i, Wo_i, self.batch, self.seq, self.n_heads, self.n_shards, r,
+                stream=None, on_stage: Optional[Callable[[str], None]] = None) -> torch.Tensor:
+        """attn partial -> H = bf16(sum of N attention partials) -> MLP partial on H -> sum.
+
+        ``on_stage(name)`` (optional) is called after each stage's launches are enqueued,
+        with the names in ``STAGES`` (used to bracket stages with stream events).
+        """
+        mark = on_stage or (lambda name: None)
+        r, N = self.rank, self.n_shards
+        attn_shard(X, Wqkv_i, bqkv_i, Wo_i, self.batch, self.seq, self.n_heads, N, r,
                    self.causal, Z=self.Z_attn, workspace=self.attn_ws, stream=stream)
+        mark("attention_shard")
         parts = list(attn_partials_other)
         parts.insert(r, self.Z_attn)
         sum_partials(parts, out=self.H, stream=stream)
-        mlp_shard(self.H, A_i, a_i, B_i, self.n_shards, r, Z=self.Z_mlp, workspace=self.mlp_ws,
-                  stream=stream)
+        mark("sum_attention")
+        column_parallel(self.H, A_i, a_i, N, r, gelu=True, Y=self.Y, stream=stream)
+        mark("mlp_column")
+        row_parallel(self.Y, B_i, N, r, Z=self.Z_mlp, stream=stream)
+        mark("mlp_row")
         parts = list(mlp_partials_other)
         parts.insert(r, self.Z_mlp)
         sum_partials(parts, out=self.out, stream=stream)
+        mark("sum_mlp")
         return self.out

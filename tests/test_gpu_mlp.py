@@ -140,3 +140,29 @@ def test_mlp_bf16_full_size_shard_sampled_rows(rank):
     if rank == 0:
         _, Z2 = run_shard(d, N, rank, "bf16")
         assert np.array_equal(Z, Z2), "results must be bitwise repeatable"
+
+
+def test_column_and_row_primitives_reproduce_mlp_shard():
+    """tp_column_parallel_fwd (GeLU) then tp_row_parallel_fwd give the MLP shard's exact bits;
+    the column primitive without activation matches the oracle's linear layer."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    w = Workload(name="prim", kind="mlp", dtype="bf16", tokens=333, hidden=520, ffn=2048,
+                 n_shards=4)
+    d = mlp_inputs(w, seed=9)
+    N, r = 4, 2
+    X = dev(d["X"], "bf16")
+    A_i = dev(layout.column_shard(d["A"], N, r), "bf16")
+    a_i = dev(layout.bias_shard(d["a"], N, r), "bf16")
+    B_i = dev(layout.row_shard(d["B"], N, r), "bf16")
+    Z, ws = shard.mlp_shard(X, A_i, a_i, B_i, N, r)
+    Y = shard.column_parallel(X, A_i, a_i, N, r, gelu=True)
+    Z2 = shard.row_parallel(Y, B_i, N, r)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, shard.mlp_hidden_view(ws, 333, 512, torch.bfloat16))
+    assert torch.equal(Z, Z2)
+    P = host(shard.column_parallel(X, A_i, a_i, N, r, gelu=False))
+    cols = slice(r * 512, (r + 1) * 512)
+    e = oracle.rel_frobenius(P, oracle.linear(d["X"], d["A"][:, cols], d["a"][cols]))
+    print("column-parallel (no activation) err %.2e" % e)
+    assert e < TOL["bf16"]
