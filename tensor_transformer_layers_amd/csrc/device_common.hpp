@@ -48,6 +48,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D = A * B + C on a 32x32 output block with K = 16 (bf16 in, fp32 accumulate).
+// Lane l supplies A row (l & 31) and B column (l & 31), 8 consecutive K values each, and
+// receives D rows 8 * j + 4 * (l >> 5) + i (accumulator element 4 j + i) of column (l & 31).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Same block shape with fp32 operands and K = 4: lane l supplies one K value, (l >> 4).
 __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c)
 {

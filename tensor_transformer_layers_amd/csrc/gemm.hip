@@ -10,18 +10,24 @@
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
 //             per head, V written transposed for the attention kernel's P V product.
 //
-// Block = 4 waves (256 lanes) in a 2 x 2 grid, each wave owning a (BM/2) x (BN/2) output
-// tile of 16 x 16 MFMA blocks. The K loop streams BK-wide slabs of A and B through a
-// double-buffered LDS ring: the next slab is fetched into registers while the MFMAs run on
-// the current one, then written to the other buffer; one barrier per slab. LDS rows are
-// 128 bytes (8 chunks of 16 B); chunk c of row r is stored at chunk c ^ (r & 7), so the
-// 16 lanes of an MFMA operand read (16 rows, same chunk) hit 8 distinct bank groups.
+// Block = 8 waves (512 lanes, two per SIMD) in a WM x WN grid (4 waves in 2 x 2 for the fp32
+// kernel and as a tuning option), each wave owning a (BM/WM) x (BN/WN) output tile of
+// 32 x 32 MFMA blocks (16 x 16 for the fp32 kernel). The K loop streams BK-wide slabs of A and B through a
+// double-buffered LDS ring: the next slab is loaded from global memory directly into the
+// other LDS buffer while the MFMAs run on the current one; one barrier per slab; the MFMA
+// operand fragments are double-buffered in registers so LDS reads overlap the MFMAs. LDS rows are
+// 128 bytes (8 chunks of 16 B). The LDS serves a 16-byte-per-lane read 16 lanes at a time
+// from 64 four-byte banks (256 bytes), i.e. two consecutive 128-byte rows; chunk c of row r
+// is stored at chunk c ^ ((r >> 1) & 7), so the 16 rows of one MFMA operand read (same
+// logical chunk) land on 16 distinct 16-byte bank groups. (The fp32 kernel, which is not on
+// the bf16 path, keeps c ^ (r & 7).)
 //
 // The MFMA is issued as D = B_frag * A_frag (weight rows as the "M" side), so each lane's
 // four accumulator values are four consecutive output COLUMNS of one row: epilogue stores
 // are 16-byte (fp32) or 8-byte (bf16) vectors, and the bias is one vector load.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -103,22 +109,39 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
 }
 
 // ---- bf16 GEMM ---------------------------------------------------------------------------
-template <int BM, int BN, Epi EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmProblem p)
+// Operand tiles are fetched with buffer loads: the descriptor's range ends at the last valid
+// row of the tile, and a chunk past K is given an offset beyond the range, so out-of-range
+// chunks read as zero with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t row0,
+                                                            int rows_valid, int64_t ld, int esz)
 {
-    constexpr int BK = 64;                 // K per LDS slab: 128-byte rows
-    constexpr int WTM = BM / 2, WTN = BN / 2;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int ACH = BM * 8 / kThreads;  // 16-byte chunks of the A slab per lane
-    constexpr int BCH = BN * 8 / kThreads;
-    static_assert(BM % 32 == 0 && BN % 32 == 0 && ACH >= 1 && BCH >= 1, "tile");
+    const char* p = reinterpret_cast<const char*>(base) + row0 * ld * esz;
+    const int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * esz : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0,
+                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                             0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int BM, int BN, int WM, int WN, Epi EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
+{
+    constexpr int NW = WM * WN;             // waves per workgroup
+    constexpr int BK = 64;                  // K per LDS slab: 128-byte rows, four MFMA K-steps
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;   // 32 x 32 MFMA blocks per wave
+    constexpr int ACH = BM / 8 / NW;        // 8-row groups of the A slab per wave
+    constexpr int BCH = BN / 8 / NW;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "tile");
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && NW % 2 == 0, "slab split");
 
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = (p.N + BN - 1) / BN;
@@ -126,95 +149,124 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmProblem p)
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const bf16* __restrict__ gA = reinterpret_cast<const bf16*>(p.A);
-    const bf16* __restrict__ gB = reinterpret_cast<const bf16*>(p.B);
+    const __amdgpu_buffer_rsrc_t rA = tile_rsrc(p.A, m0, min(BM, p.M - m0), p.lda, 2);
+    const __amdgpu_buffer_rsrc_t rB = tile_rsrc(p.B, n0, min(BN, p.N - n0), p.ldb, 2);
 
-    // Lane tid loads chunk (tid & 7) of rows (tid >> 3) + 32 i.
-    const int lc = tid & 7;
-    const int lr = tid >> 3;
-    u32x4 ra[ACH], rb[BCH];
+    // Slabs go from global memory straight into LDS (buffer_load ... lds): one instruction
+    // moves 8 rows x 128 bytes, lane l writing the 16 bytes at byte 16 l of its wave's
+    // destination, i.e. row (l >> 3), physical chunk (l & 7). The lane therefore fetches the
+    // logical chunk that the XOR swizzle stores there: (l & 7) ^ ((row >> 1) & 7). Wave w
+    // moves the 8-row groups w, w + NW, ... of each operand.
+    const int grp_row = lane >> 3;
+    // row = 8 (wave + NW i) + grp_row with NW even, so (row >> 1) & 7 = 4 (wave & 1) + (lane >> 4)
+    const int lchunk = (lane & 7) ^ (((wave & 1) << 2) + (lane >> 4));
+    const uint32_t offA = (uint32_t)((wave * 8 + grp_row) * p.lda + lchunk * 8) * 2u;
+    const uint32_t offB = (uint32_t)((wave * 8 + grp_row) * p.ldb + lchunk * 8) * 2u;
+    const uint32_t stepA = (uint32_t)(8 * NW * p.lda) * 2u;
+    const uint32_t stepB = (uint32_t)(8 * NW * p.ldb) * 2u;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
 
-    auto fetch = [&](int k0) {
-        const int kk = k0 + lc * 8;
-        const bool kin = kk < p.K;
+    auto fetch = [&](int k0, int buf) {
+        const bool kin = k0 + lchunk * 8 < p.K;
+        const uint32_t kb = (uint32_t)k0 * 2u;
+        bf16* sA = smem + buf * (BM + BN) * BK + wave * 8 * BK;
+        bf16* sB = smem + buf * (BM + BN) * BK + BM * BK + wave * 8 * BK;
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int gm = m0 + lr + 32 * i;
-            ra[i] = (kin && gm < p.M) ? ld16(gA + (int64_t)gm * p.lda + kk) : zero16();
-        }
+        for (int i = 0; i < ACH; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rA, (lds_ptr)(sA + i * 8 * NW * BK), 16,
+                kin ? offA + i * stepA + kb : kOutOfRange, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int gn = n0 + lr + 32 * i;
-            rb[i] = (kin && gn < p.N) ? ld16(gB + (int64_t)gn * p.ldb + kk) : zero16();
-        }
-    };
-    auto stash = [&](int buf) {
-        bf16* sA = smem + buf * (BM + BN) * BK;
-        bf16* sB = sA + BM * BK;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int r = lr + 32 * i;
-            st16(sA + r * BK + ((lc ^ (r & 7)) << 3), ra[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int r = lr + 32 * i;
-            st16(sB + r * BK + ((lc ^ (r & 7)) << 3), rb[i]);
-        }
+        for (int i = 0; i < BCH; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rB, (lds_ptr)(sB + i * 8 * NW * BK), 16,
+                kin ? offB + i * stepB + kb : kOutOfRange, 0, 0, 0);
     };
 
-    f32x4 acc[FN][FM];
+    const int fr = lane & 31;   // operand row within a 32-row block
+    const int fg = lane >> 5;   // which 8-wide half of the 16-wide MFMA K-step
+    // Fragments of K-step ks (K = 16 ks ... 16 ks + 15 of the slab): chunk 2 ks + fg.
+    auto read_frags = [&](int buf, int ks, bf16x8* fa, bf16x8* fb) {
+        const bf16* sA = smem + buf * (BM + BN) * BK;
+        const bf16* sB = sA + BM * BK;
+        const int ch = ks * 2 + fg;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WTM + i * 32 + fr;
+            fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ ((r >> 1) & 7)) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int r = wn * WTN + i * 32 + fr;
+            fb[i] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ ((r >> 1) & 7)) << 3));
+        }
+    };
+
+    f32x16 acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16(fb[i], fa[j], acc[i][j]);
+    };
 
+    // Software pipeline over slabs of four K-steps. Entering iteration kt, slab kt sits in
+    // LDS buffer kt & 1 and the fragments of its K-step 0 are in set 0:
+    //   start loading slab kt+1 into the other buffer (last read before the previous
+    //   barrier) | read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
+    //   MFMAs step 2 | wait for the slab, barrier | read slab kt+1 step 0 | MFMAs step 3.
+    // Each fragment read overlaps a K-step of MFMAs, and the slab load three of them.
+    bf16x8 fa[2][FM], fb[2][FN];
     const int KT = (p.K + BK - 1) / BK;
-    fetch(0);
-    stash(0);
+    fetch(0, 0);
     __syncthreads();
-
-    const int fr = lane & 15;   // operand row within a 16-row block
-    const int fg = lane >> 4;   // which 8-wide K group of the 32-wide MFMA step
-
+    read_frags(0, 0, fa[0], fb[0]);
+    // sched_barrier(0) pins that order: without it the scheduler folds both fragment sets into
+    // one and waits on each read right before its MFMA.
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) fetch((kt + 1) * BK);
-        const bf16* sA = smem + cur * (BM + BN) * BK;
-        const bf16* sB = sA + BM * BK;
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const int ch = ks * 4 + fg;
-            bf16x8 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WTM + i * 16 + fr;
-                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ (r & 7)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const int r = wn * WTN + i * 16 + fr;
-                fb[i] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ (r & 7)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = mfma16x16x32(fb[i], fa[j], acc[i][j]);
-        }
-        if (kt + 1 < KT) stash(cur ^ 1);
+        const bool more = kt + 1 < KT;
+        if (more) fetch((kt + 1) * BK, cur ^ 1);
+        read_frags(cur, 1, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(cur, 2, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(cur, 3, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // acc[i][j][v] = C[m0 + wm*WTM + j*16 + fr][n0 + wn*WTN + i*16 + 4*fg + v]
+    // acc[i][j][4 q + v] = C[m0 + wm*WTM + 32 j + fr][n0 + wn*WTN + 32 i + 8 q + 4 fg + v]
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 16 + fr;
+        const int m = m0 + wm * WTM + j * 32 + fr;
         if (m >= p.M) continue;
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int n = n0 + wn * WTN + i * 16 + 4 * fg;
-            if (n < p.N) store_out<EPI, bf16>(p, m, n, acc[i][j]);
-        }
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * fg;
+                if (n < p.N)
+                    store_out<EPI, bf16>(p, m, n,
+                                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+            }
     }
 }
 
@@ -332,23 +384,23 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    dim3 grid(tiles), block(kThreads);
+    dim3 grid(tiles), block(64 * WM * WN);
     switch (epi) {
         case Epi::BiasGelu:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::BiasGelu>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::BiasGelu>), grid, block, 0, s, p);
             break;
         case Epi::F32:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::F32>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::F32>), grid, block, 0, s, p);
             break;
         case Epi::Qkv:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::Qkv>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::Qkv>), grid, block, 0, s, p);
             break;
         case Epi::Bias:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, Epi::Bias>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::Bias>), grid, block, 0, s, p);
             break;
     }
     return hipGetLastError();
@@ -374,9 +426,10 @@ GemmTile gemm_bf16_pick_tile(int M, int N, int K)
     return best;
 }
 
-// TPSHARD_GEMM_TILE=<bm>x<bn> (one of the compiled shapes) overrides the choice: a tuning
-// and test knob for sweeping tile shapes; unknown values are ignored.
-static bool tile_override(GemmTile& t)
+// TPSHARD_GEMM_TILE=<bm>x<bn>[w4] (one of the compiled shapes; "w4" selects the 4-wave
+// layout instead of the default 8-wave one) overrides the choice: a tuning and test knob for
+// sweeping tile shapes; unknown values are ignored.
+static bool tile_override(GemmTile& t, bool& w4)
 {
     const char* e = std::getenv("TPSHARD_GEMM_TILE");
     if (!e) return false;
@@ -384,18 +437,26 @@ static bool tile_override(GemmTile& t)
     if (std::sscanf(e, "%dx%d", &bm, &bn) != 2) return false;
     const bool known = (bm == 256 && (bn == 256 || bn == 192 || bn == 128)) ||
                        (bm == 128 && bn == 128);
-    if (known) t = GemmTile{bm, bn};
-    return known;
+    if (!known) return false;
+    t = GemmTile{bm, bn};
+    w4 = std::strstr(e, "w4") != nullptr;
+    return true;
 }
 
+// Eight waves (two per SIMD) per workgroup by default: while one wave of a SIMD waits on
+// LDS or the slab barrier, the other keeps the matrix core busy.
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     GemmTile t = gemm_bf16_pick_tile(p.M, p.N, p.K);
-    tile_override(t);
-    if (t.bm == 256 && t.bn == 256) return launch_bf16<256, 256>(p, epi, s);
-    if (t.bm == 256 && t.bn == 192) return launch_bf16<256, 192>(p, epi, s);
-    if (t.bm == 256 && t.bn == 128) return launch_bf16<256, 128>(p, epi, s);
-    return launch_bf16<128, 128>(p, epi, s);
+    bool w4 = false;
+    tile_override(t, w4);
+    if (t.bm == 256 && t.bn == 256)
+        return w4 ? launch_bf16<256, 256, 2, 2>(p, epi, s) : launch_bf16<256, 256, 2, 4>(p, epi, s);
+    if (t.bm == 256 && t.bn == 192)
+        return w4 ? launch_bf16<256, 192, 2, 2>(p, epi, s) : launch_bf16<256, 192, 4, 2>(p, epi, s);
+    if (t.bm == 256 && t.bn == 128)
+        return w4 ? launch_bf16<256, 128, 2, 2>(p, epi, s) : launch_bf16<256, 128, 4, 2>(p, epi, s);
+    return w4 ? launch_bf16<128, 128, 2, 2>(p, epi, s) : launch_bf16<128, 128, 2, 4>(p, epi, s);
 }
 
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)

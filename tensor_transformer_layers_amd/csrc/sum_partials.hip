@@ -8,6 +8,8 @@
 // requests per lane are in flight. The adds run in the fixed order 0, 1, ..., N-1, so the
 // result is bitwise reproducible. Reads and writes are non-temporal: every byte is touched
 // exactly once.
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -33,28 +35,46 @@ __device__ __forceinline__ void put4(void* out, int64_t i4, f32x4 v)
     }
 }
 
-// NP > 0: compile-time part count (fully unrolled); NP == 0: runtime count n.
-template <int NP, bool BF16>
+// NP > 0: compile-time part count (fully unrolled); NP == 0: runtime count n. Each lane
+// handles U consecutive-by-stride float4 vectors per iteration, so N * U loads are in flight.
+template <int NP, int U, bool BF16>
 __global__ __launch_bounds__(kThreads) void sum_kernel(Parts parts, int n, int64_t n4, void* out)
 {
     const int np = NP > 0 ? NP : n;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-        f32x4 acc;
+    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < n4; i0 += stride * U) {
         if constexpr (NP > 0) {
-            f32x4 v[NP];
+            f32x4 v[U][NP];
 #pragma unroll
-            for (int r = 0; r < NP; ++r)
-                v[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[r]) + i);
-            acc = v[0];
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * stride;
+                if (i < n4) {
 #pragma unroll
-            for (int r = 1; r < NP; ++r) acc += v[r];
+                    for (int r = 0; r < NP; ++r)
+                        v[u][r] = __builtin_nontemporal_load(
+                            reinterpret_cast<const f32x4*>(parts.p[r]) + i);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * stride;
+                if (i < n4) {
+                    f32x4 acc = v[u][0];
+#pragma unroll
+                    for (int r = 1; r < NP; ++r) acc += v[u][r];
+                    put4<BF16>(out, i, acc);
+                }
+            }
         } else {
-            acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + i);
-            for (int r = 1; r < np; ++r)
-                acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[r]) + i);
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + u * stride;
+                if (i >= n4) break;
+                f32x4 acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + i);
+                for (int r = 1; r < np; ++r)
+                    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[r]) + i);
+                put4<BF16>(out, i, acc);
+            }
         }
-        put4<BF16>(out, i, acc);
     }
 }
 
@@ -72,24 +92,47 @@ __global__ void sum_tail_kernel(Parts parts, int n, int64_t start, int64_t numel
         reinterpret_cast<float*>(out)[i] = acc;
 }
 
+// Launch shape: TPSHARD_SUM_GRID (workgroups) and TPSHARD_SUM_UNROLL (1, 2 or 4 vectors per
+// lane per iteration) override the defaults -- tuning knobs for sweeping the launch shape.
+static int env_int(const char* name, int dflt)
+{
+    const char* e = std::getenv(name);
+    return e ? std::atoi(e) : dflt;
+}
+
+template <int U, bool BF16>
+void launch_u(const Parts& parts, int n, int64_t n4, void* out, unsigned grid, hipStream_t s)
+{
+    switch (n) {
+#define TPS_CASE(K)                                                                              \
+    case K:                                                                                      \
+        hipLaunchKernelGGL((sum_kernel<K, U, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n, \
+                           n4, out);                                                             \
+        break;
+        TPS_CASE(1) TPS_CASE(2) TPS_CASE(3) TPS_CASE(4)
+        TPS_CASE(5) TPS_CASE(6) TPS_CASE(7) TPS_CASE(8)
+#undef TPS_CASE
+        default:
+            hipLaunchKernelGGL((sum_kernel<0, U, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n,
+                               n4, out);
+    }
+}
+
 template <bool BF16>
 hipError_t launch(const Parts& parts, int n, int64_t numel, void* out, hipStream_t s)
 {
     const int64_t n4 = numel / 4;
     if (n4 > 0) {
-        // Enough workgroups to keep every CU's queues full: 256 CUs x 8 groups.
+        const int unroll = env_int("TPSHARD_SUM_UNROLL", 1);
         const int64_t want = (n4 + kThreads - 1) / kThreads;
-        const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-        switch (n) {
-#define TPS_CASE(K) \
-    case K: hipLaunchKernelGGL((sum_kernel<K, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n, n4, out); break;
-            TPS_CASE(1) TPS_CASE(2) TPS_CASE(3) TPS_CASE(4)
-            TPS_CASE(5) TPS_CASE(6) TPS_CASE(7) TPS_CASE(8)
-#undef TPS_CASE
-            default:
-                hipLaunchKernelGGL((sum_kernel<0, BF16>), dim3(grid), dim3(kThreads), 0, s, parts, n,
-                                   n4, out);
-        }
+        const int64_t cap = env_int("TPSHARD_SUM_GRID", 2048);
+        const unsigned grid = (unsigned)(want < cap ? want : (cap > 0 ? cap : 1));
+        if (unroll >= 4)
+            launch_u<4, BF16>(parts, n, n4, out, grid, s);
+        else if (unroll == 2)
+            launch_u<2, BF16>(parts, n, n4, out, grid, s);
+        else
+            launch_u<1, BF16>(parts, n, n4, out, grid, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

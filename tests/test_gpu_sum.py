@@ -68,3 +68,16 @@ def test_sum_in_place_on_first_partial():
     P = partials_inputs(3, 10007, seed=6, integer=True)
     got, _ = _run(P, alias=True)
     assert np.array_equal(got, oracle.sum_partials(P))
+
+
+@pytest.mark.parametrize("unroll", ["1", "2", "4"])
+@pytest.mark.parametrize("grid", ["1", "7", "2048"])
+def test_sum_launch_shapes_exact(unroll, grid, monkeypatch):
+    """Every launch shape (grid-stride loop, vectors per lane) gives the exact integer sum."""
+    monkeypatch.setenv("TPSHARD_SUM_UNROLL", unroll)
+    monkeypatch.setenv("TPSHARD_SUM_GRID", grid)
+    for n, numel in ((8, 100003), (3, 4 * 1031 + 2), (13, 777)):
+        P = partials_inputs(n, numel, seed=numel + n, integer=True)
+        got, c = _run(P)
+        assert c.intact()
+        assert np.array_equal(got, oracle.sum_partials(P))
