@@ -182,6 +182,15 @@ tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_
 tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel,
                           void* Z, tp_dtype out_dt, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Which bf16 GEMM tile the library launches for C[M, N] = A[M, K] B[N, K]^T: block tile
+ * rows x columns and waves per workgroup (honours the TPSHARD_GEMM_TILE override). A query
+ * for profiling and tuning; it launches nothing. Returns TP_ERR_NULL / TP_ERR_SHAPE on bad
+ * arguments.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* tile_n,
+                            int* waves);
+
 /* Description of the last non-OK status returned on the calling thread ("" if none).
    The string is owned by the library and valid until the next call on that thread. */
 const char* tp_last_error(void);
@@ -189,7 +198,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 2
+#define TP_SHARD_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

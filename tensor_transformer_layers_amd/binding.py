@@ -29,8 +29,8 @@ STATUS_NAMES = {
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
     "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd", "tp_attn_workspace_bytes",
-    "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_last_error",
-    "tp_abi_version",
+    "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
+    "tp_last_error", "tp_abi_version",
 )
 
 
@@ -81,6 +81,9 @@ def lib():
     L.tp_attn_shard_fwd.restype = _int
     L.tp_attn_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                     _int, _int, _vp, _sz, _vp]
+    L.tp_gemm_tile_info.restype = _int
+    L.tp_gemm_tile_info.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                    ctypes.POINTER(_int)]
     L.tp_sum_partials.restype = _int
     L.tp_sum_partials.argtypes = [ctypes.POINTER(_vp), _int, _i64, _vp, _int, _vp]
     _lib = L
@@ -158,6 +161,13 @@ def tp_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z_i, batch, seq, hidden, n_heads,
 def tp_sum_partials(Z_parts: Sequence, n_parts, numel, Z, out_dt, stream=None) -> int:
     arr = (_vp * max(1, len(Z_parts)))(*[_ptr(z) for z in Z_parts])
     return lib().tp_sum_partials(arr, n_parts, numel, _ptr(Z), out_dt, _stream(stream))
+
+
+def tp_gemm_tile_info(M, N, K):
+    """(status, tile_m, tile_n, waves) of the bf16 GEMM launched for this shape."""
+    a, b, c = _int(0), _int(0), _int(0)
+    st = lib().tp_gemm_tile_info(M, N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return st, a.value, b.value, c.value
 
 
 def check(status: int) -> None:

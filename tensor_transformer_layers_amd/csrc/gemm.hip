@@ -443,6 +443,15 @@ static bool tile_override(GemmTile& t, bool& w4)
     return true;
 }
 
+GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves)
+{
+    GemmTile t = gemm_bf16_pick_tile(M, N, K);
+    bool w4 = false;
+    tile_override(t, w4);
+    if (waves) *waves = w4 ? 4 : 8;
+    return t;
+}
+
 // Eight waves (two per SIMD) per workgroup by default: while one wave of a SIMD waits on
 // LDS or the slab barrier, the other keeps the matrix core busy.
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)

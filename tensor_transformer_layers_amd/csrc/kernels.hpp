@@ -34,6 +34,8 @@ struct GemmProblem {
 struct GemmTile { int bm, bn; };
 
 GemmTile gemm_bf16_pick_tile(int M, int N, int K);
+// Tile and wave count gemm_bf16 launches for this shape (after the environment override).
+GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves);
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t stream);
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t stream);
 

@@ -326,6 +326,17 @@ tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_
     return hip_status(e, "output projection launch");
 }
 
+tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* tile_n, int* waves)
+{
+    if (!tile_m || !tile_n || !waves) return fail(TP_ERR_NULL, "output pointers must be non-NULL");
+    if (M < 1 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(TP_ERR_SHAPE, "M, N, K must be in [1, 2^31-1]");
+    const tps::GemmTile t = tps::gemm_bf16_launch_tile((int)M, (int)N, (int)K, waves);
+    *tile_m = t.bm;
+    *tile_n = t.bn;
+    return ok();
+}
+
 tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel, void* Z,
                           tp_dtype out_dt, void* stream)
 {

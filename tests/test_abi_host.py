@@ -124,3 +124,11 @@ def test_workspace_sizes():
     # 2 heads of d = 128, seq 5: Q and K are 2560 bytes; V^T rows are padded to 8 keys
     assert st == 0 and off == dict(q=0, k=2560, vt=5120, o=5120 + 2 * 128 * 8 * 2)
     assert B.tp_attn_workspace_bytes(1, 5, 256, 2, 1, F32) == 0
+
+
+def test_gemm_tile_info():
+    st, bm, bn, w = B.tp_gemm_tile_info(4096, 4096, 8192)
+    assert st == 0 and (bm, bn, w) == (256, 256, 8)
+    st, bm, bn, w = B.tp_gemm_tile_info(4096, 3072, 8192)
+    assert st == 0 and (bm, bn) == (256, 192)
+    assert B.tp_gemm_tile_info(0, 1, 1)[0] == 2
