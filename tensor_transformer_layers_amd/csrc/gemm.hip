@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -124,6 +125,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Scheduling groups of one pipeline phase: after MFMA I come NR (I+1)/NM - NR I/NM fragment
+// reads and NV (I+1)/NM - NV I/NM slab loads, spreading both evenly between the phase's NM
+// MFMAs. Masks: 0x8 MFMA, 0x100 LDS read, 0x20 global read.
+template <int I, int NM, int NR, int NV>
+struct InterleaveGroups {
+    __device__ __forceinline__ static void emit()
+    {
+        if constexpr (I < NM) {
+            constexpr int nr = NR * (I + 1) / NM - NR * I / NM;
+            constexpr int nv = NV * (I + 1) / NM - NV * I / NM;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+            if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);
+            InterleaveGroups<I + 1, NM, NR, NV>::emit();
+        }
+    }
+};
+
 template <int BM, int BN, int WM, int WN, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
 {
@@ -166,6 +185,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     const uint32_t stepB = (uint32_t)(8 * NW * p.ldb) * 2u;
     typedef __attribute__((address_space(3))) void* lds_ptr;
 
+    // fetch(k0 >= K) moves no memory (every offset is out of range) and zero-fills the
+    // buffer: the loop issues it unconditionally so that the loads stay in the same basic
+    // block as the MFMAs they are scheduled between.
     auto fetch = [&](int k0, int buf) {
         const bool kin = k0 + lchunk * 8 < p.K;
         const uint32_t kb = (uint32_t)k0 * 2u;
@@ -221,37 +243,206 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     //   start loading slab kt+1 into the other buffer (last read before the previous
     //   barrier) | read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
     //   MFMAs step 2 | wait for the slab, barrier | read slab kt+1 step 0 | MFMAs step 3.
-    // Each fragment read overlaps a K-step of MFMAs, and the slab load three of them.
+    // Within each phase the fragment reads (and, in the first, the slab loads) are threaded
+    // one by one between the MFMAs (sched_group_barrier), so the matrix core never waits for
+    // a burst of memory instructions to issue; sched_barrier(0) fences the phases.
+    constexpr int NM = FM * FN;          // MFMAs per K-step
+    constexpr int NR = FM + FN;          // fragment reads per K-step
+    constexpr int NV = ACH + BCH;        // slab load instructions per wave
+    auto interleave = [&](auto loads) {
+        InterleaveGroups<0, NM, NR, decltype(loads)::value ? NV : 0>::emit();
+    };
     bf16x8 fa[2][FM], fb[2][FN];
     const int KT = (p.K + BK - 1) / BK;
     fetch(0, 0);
     __syncthreads();
     read_frags(0, 0, fa[0], fb[0]);
-    // sched_barrier(0) pins that order: without it the scheduler folds both fragment sets into
-    // one and waits on each read right before its MFMA.
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) fetch((kt + 1) * BK, cur ^ 1);
-        read_frags(cur, 1, fa[1], fb[1]);
         __builtin_amdgcn_sched_barrier(0);
+        fetch((kt + 1) * BK, cur ^ 1);
+        read_frags(cur, 1, fa[1], fb[1]);
         mma(fa[0], fb[0]);
+        interleave(std::true_type{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(cur, 2, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
         mma(fa[1], fb[1]);
+        interleave(std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(cur, 3, fa[1], fb[1]);
-        __builtin_amdgcn_sched_barrier(0);
         mma(fa[0], fb[0]);
+        interleave(std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        if (more) read_frags(cur ^ 1, 0, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
+        read_frags(cur ^ 1, 0, fa[0], fb[0]);   // after the last slab: reads zeros, unused
         mma(fa[1], fb[1]);
+        interleave(std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // acc[i][j][4 q + v] = C[m0 + wm*WTM + 32 j + fr][n0 + wn*WTN + 32 i + 8 q + 4 fg + v]
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * WTM + j * 32 + fr;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * fg;
+                if (n < p.N)
+                    store_out<EPI, bf16>(p, m, n,
+                                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+            }
+    }
+}
+
+// ---- bf16 GEMM, 32-wide slabs in a 4-stage LDS ring -------------------------------------
+// Same tile, waves and epilogue as gemm_bf16_kernel; the K loop instead streams 32-wide slabs
+// (64-byte rows, two MFMA K-steps each) through FOUR LDS buffers and loads each slab three
+// slabs ahead, so a slab's global loads have five K-steps of MFMAs to land. Each wave waits
+// only for the slab about to be read (s_waitcnt vmcnt(2 slabs of its own loads)) before the
+// barrier; the two newer slabs stay in flight across it.
+// Swizzle for 64-byte rows: chunk c of row r is stored at c ^ ((r >> 2) & 3), so the 16 rows
+// of one MFMA operand read (same logical chunk) hit 16 distinct 16-byte groups of the banks.
+template <int BM, int BN, int WM, int WN, Epi EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem p)
+{
+    constexpr int NW = WM * WN;
+    constexpr int BK = 32;
+    constexpr int ST = 4;                   // LDS stages
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int GA = BM / 16, GB = BN / 16;   // 16-row load groups of the A and B slabs
+    constexpr int G = GA + GB;
+    constexpr int LMAX = (G + NW - 1) / NW;     // load instructions per wave per slab (max)
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "tile");
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && 2 * LMAX < 64, "slab split");
+
+    __shared__ __attribute__((aligned(16))) bf16 smem[ST * (BM + BN) * BK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int wm = wave / WN, wn = wave % WN;
+    const int tiles_m = (p.M + BM - 1) / BM;
+    const int tiles_n = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const __amdgpu_buffer_rsrc_t rA = tile_rsrc(p.A, m0, min(BM, p.M - m0), p.lda, 2);
+    const __amdgpu_buffer_rsrc_t rB = tile_rsrc(p.B, n0, min(BN, p.N - n0), p.ldb, 2);
+
+    // One load instruction moves 16 rows x 64 bytes: lane l writes row (l >> 2), physical
+    // chunk (l & 3) of its destination, so it fetches logical chunk (l & 3) ^ ((row >> 2) & 3)
+    // = (l & 3) ^ (l >> 4). The G = GA + GB row groups of the two operands are dealt to the
+    // waves round-robin: wave w moves groups w, w + NW, ... (L_w of them).
+    const int grp_row = lane >> 2;
+    const int lchunk = (lane & 3) ^ (lane >> 4);
+    const int L_w = (G - wave + NW - 1) / NW;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    // fetch(k0 >= K) moves no memory (out-of-range offsets) but still issues L_w loads, which
+    // keeps the vmcnt arithmetic uniform.
+    auto fetch = [&](int k0, int buf) {
+        const bool kin = k0 + lchunk * 8 < p.K;
+        const uint32_t kb = (uint32_t)k0 * 2u;
+        bf16* slab = smem + buf * (BM + BN) * BK;
+#pragma unroll
+        for (int i = 0; i < LMAX; ++i) {
+            const int g = wave + i * NW;
+            // With GA and GB multiples of NW, group i of every wave is in A iff i < GA / NW: a
+            // compile-time choice (no branch splits the loop body).
+            constexpr bool even = GA % NW == 0 && GB % NW == 0;
+            if (even ? i < GA / NW : g < GA) {
+                const uint32_t off = (uint32_t)((16 * g + grp_row) * p.lda + lchunk * 8) * 2u + kb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(slab + 16 * g * BK), 16,
+                                                         kin ? off : kOutOfRange, 0, 0, 0);
+            } else if (even || g < G) {
+                const int gb = g - GA;
+                const uint32_t off = (uint32_t)((16 * gb + grp_row) * p.ldb + lchunk * 8) * 2u + kb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16, kin ? off : kOutOfRange, 0,
+                    0, 0);
+            }
+        }
+    };
+    const int fr = lane & 31;
+    const int fg = lane >> 5;
+    auto read_frags = [&](int buf, int ks, bf16x8* fa, bf16x8* fb) {
+        const bf16* sA = smem + buf * (BM + BN) * BK;
+        const bf16* sB = sA + BM * BK;
+        const int ch = ks * 2 + fg;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WTM + i * 32 + fr;
+            fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ ((r >> 2) & 3)) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int r = wn * WTN + i * 32 + fr;
+            fb[i] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ ((r >> 2) & 3)) << 3));
+        }
+    };
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16(fb[i], fa[j], acc[i][j]);
+    };
+    constexpr int NM = FM * FN;
+    constexpr int NR = FM + FN;
+    auto interleave = [&](auto loads) {
+        InterleaveGroups<0, NM, NR, decltype(loads)::value ? LMAX : 0>::emit();
+    };
+    // Wait until this wave's loads of all but the two newest slabs have landed: s_waitcnt with
+    // vmcnt = 2 L_w, expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+    constexpr int kWaitHi = ((2 * LMAX) & 15) | (((2 * LMAX) >> 4) << 14) | (7 << 4) | (15 << 8);
+    constexpr int kWaitLo =
+        ((2 * (LMAX - 1)) & 15) | (((2 * (LMAX - 1)) >> 4) << 14) | (7 << 4) | (15 << 8);
+    auto wait_two_slabs = [&]() {
+        if (G % NW == 0 || L_w == LMAX)
+            __builtin_amdgcn_s_waitcnt(kWaitHi);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitLo);
+    };
+
+    bf16x8 fa[2][FM], fb[2][FN];
+    const int KT = (p.K + BK - 1) / BK;
+    fetch(0, 0);
+    fetch(BK, 1);
+    fetch(2 * BK, 2);
+    wait_two_slabs();    // slab 0 has landed (slabs 1, 2 may be in flight)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, 0, fa[0], fb[0]);
+    // Iteration kt: slab kt in buffer kt % 4, its K-step 0 fragments in set 0.
+    //   load slab kt+3 into buffer (kt+3) % 4 (last read before the previous barrier) |
+    //   read step 1 | MFMAs step 0 | wait for slab kt+1, barrier | read slab kt+1 step 0 |
+    //   MFMAs step 1.
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 3;
+        __builtin_amdgcn_sched_barrier(0);
+        fetch((kt + 3) * BK, (kt + 3) & 3);
+        read_frags(cur, 1, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        interleave(std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_two_slabs();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags((kt + 1) & 3, 0, fa[0], fb[0]);   // past the last slab: zeros, unused
+        mma(fa[1], fb[1]);
+        interleave(std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+    }
     // acc[i][j][4 q + v] = C[m0 + wm*WTM + 32 j + fr][n0 + wn*WTN + 32 i + 8 q + 4 fg + v]
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -384,25 +575,23 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool S4>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     dim3 grid(tiles), block(64 * WM * WN);
+#define TPS_LAUNCH(E)                                                                        \
+    if constexpr (S4)                                                                        \
+        hipLaunchKernelGGL((gemm_bf16_s4_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);  \
+    else                                                                                     \
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);
     switch (epi) {
-        case Epi::BiasGelu:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::BiasGelu>), grid, block, 0, s, p);
-            break;
-        case Epi::F32:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::F32>), grid, block, 0, s, p);
-            break;
-        case Epi::Qkv:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::Qkv>), grid, block, 0, s, p);
-            break;
-        case Epi::Bias:
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, Epi::Bias>), grid, block, 0, s, p);
-            break;
+        case Epi::BiasGelu: TPS_LAUNCH(Epi::BiasGelu) break;
+        case Epi::F32: TPS_LAUNCH(Epi::F32) break;
+        case Epi::Qkv: TPS_LAUNCH(Epi::Qkv) break;
+        case Epi::Bias: TPS_LAUNCH(Epi::Bias) break;
     }
+#undef TPS_LAUNCH
     return hipGetLastError();
 }
 
@@ -426,10 +615,11 @@ GemmTile gemm_bf16_pick_tile(int M, int N, int K)
     return best;
 }
 
-// TPSHARD_GEMM_TILE=<bm>x<bn>[w4] (one of the compiled shapes; "w4" selects the 4-wave
-// layout instead of the default 8-wave one) overrides the choice: a tuning and test knob for
-// sweeping tile shapes; unknown values are ignored.
-static bool tile_override(GemmTile& t, bool& w4)
+// TPSHARD_GEMM_TILE=<bm>x<bn>[w4][s4] (one of the compiled shapes; "w4" selects the 4-wave
+// layout instead of the default 8-wave one, "s4" the 4-stage 32-wide-slab pipeline instead of
+// the default 2-stage 64-wide one) overrides the choice: a tuning and test knob for sweeping
+// tile shapes; unknown values are ignored.
+static bool tile_override(GemmTile& t, bool& w4, bool& s4)
 {
     const char* e = std::getenv("TPSHARD_GEMM_TILE");
     if (!e) return false;
@@ -440,16 +630,29 @@ static bool tile_override(GemmTile& t, bool& w4)
     if (!known) return false;
     t = GemmTile{bm, bn};
     w4 = std::strstr(e, "w4") != nullptr;
+    s4 = std::strstr(e, "s4") != nullptr;
     return true;
 }
 
 GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves)
 {
     GemmTile t = gemm_bf16_pick_tile(M, N, K);
-    bool w4 = false;
-    tile_override(t, w4);
+    bool w4 = false, s4 = false;
+    tile_override(t, w4, s4);
     if (waves) *waves = w4 ? 4 : 8;
     return t;
+}
+
+template <bool S4>
+hipError_t gemm_bf16_tile(const GemmProblem& p, Epi epi, hipStream_t s, GemmTile t, bool w4)
+{
+    if (t.bm == 256 && t.bn == 256)
+        return w4 ? launch_bf16<256, 256, 2, 2, S4>(p, epi, s) : launch_bf16<256, 256, 2, 4, S4>(p, epi, s);
+    if (t.bm == 256 && t.bn == 192)
+        return w4 ? launch_bf16<256, 192, 2, 2, S4>(p, epi, s) : launch_bf16<256, 192, 4, 2, S4>(p, epi, s);
+    if (t.bm == 256 && t.bn == 128)
+        return w4 ? launch_bf16<256, 128, 2, 2, S4>(p, epi, s) : launch_bf16<256, 128, 4, 2, S4>(p, epi, s);
+    return w4 ? launch_bf16<128, 128, 2, 2, S4>(p, epi, s) : launch_bf16<128, 128, 2, 4, S4>(p, epi, s);
 }
 
 // Eight waves (two per SIMD) per workgroup by default: while one wave of a SIMD waits on
@@ -457,15 +660,9 @@ GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves)
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     GemmTile t = gemm_bf16_pick_tile(p.M, p.N, p.K);
-    bool w4 = false;
-    tile_override(t, w4);
-    if (t.bm == 256 && t.bn == 256)
-        return w4 ? launch_bf16<256, 256, 2, 2>(p, epi, s) : launch_bf16<256, 256, 2, 4>(p, epi, s);
-    if (t.bm == 256 && t.bn == 192)
-        return w4 ? launch_bf16<256, 192, 2, 2>(p, epi, s) : launch_bf16<256, 192, 4, 2>(p, epi, s);
-    if (t.bm == 256 && t.bn == 128)
-        return w4 ? launch_bf16<256, 128, 2, 2>(p, epi, s) : launch_bf16<256, 128, 4, 2>(p, epi, s);
-    return w4 ? launch_bf16<128, 128, 2, 2>(p, epi, s) : launch_bf16<128, 128, 2, 4>(p, epi, s);
+    bool w4 = false, s4 = false;
+    tile_override(t, w4, s4);
+    return s4 ? gemm_bf16_tile<true>(p, epi, s, t, w4) : gemm_bf16_tile<false>(p, epi, s, t, w4);
 }
 
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)

@@ -64,7 +64,8 @@ RAGGED = [(1, 64, 64, 1), (37, 200, 240, 2), (300, 264, 1040, 2), (513, 520, 206
 
 
 @pytest.mark.parametrize("tile", [None, "256x256", "256x192", "256x128", "128x128",
-                                  "256x256w4", "256x192w4", "256x128w4", "128x128w4"])
+                                  "256x256w4", "256x192w4", "256x128w4", "128x128w4",
+                                  "256x256s4", "256x192s4", "256x128w4s4", "128x128s4"])
 @pytest.mark.parametrize("shape", RAGGED)
 def test_mlp_bf16_ragged_tiles(shape, tile, monkeypatch):
     if tile:
