@@ -124,8 +124,10 @@ def cpu_baseline(w, d, rows_n: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The shader clock settles over the first tens of milliseconds of sustained MFMA work
+    # (the chip is power-limited under these GEMMs), so the default warm-up is long.
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows in the CPU-oracle sample (default: the whole shard)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

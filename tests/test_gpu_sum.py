@@ -71,7 +71,7 @@ def test_sum_in_place_on_first_partial():
 
 
 @pytest.mark.parametrize("unroll", ["1", "2", "4"])
-@pytest.mark.parametrize("grid", ["1", "7", "2048"])
+@pytest.mark.parametrize("grid", ["0", "1", "7", "2048"])
 def test_sum_launch_shapes_exact(unroll, grid, monkeypatch):
     """Every launch shape (grid-stride loop, vectors per lane) gives the exact integer sum."""
     monkeypatch.setenv("TPSHARD_SUM_UNROLL", unroll)
