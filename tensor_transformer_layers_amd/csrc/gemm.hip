@@ -143,6 +143,86 @@ struct InterleaveGroups {
     }
 };
 
+// ---- bf16 kernels' output stage -----------------------------------------------------------
+// acc[i][j][4 q + v] of a wave holds C[r0 + 32 j + fr][c0 + 32 i + 8 q + 4 fg + v] (fr = lane & 31,
+// fg = lane >> 5). Stored as it lies, one 16-byte vector per lane would put the 32 lanes of an
+// instruction in 32 different rows. Instead each wave stages its tile through its own slice of
+// the (now idle) operand LDS, FM / R block-rows at a time, and reads it back row-contiguously:
+// consecutive lanes take consecutive 4-column vectors of one row, so every store instruction
+// writes whole row segments. The staging rows are padded by 16 bytes, which puts the 16 rows
+// written by one 16-lane pass on 16 distinct bank groups. The Qkv scatter keeps the direct
+// path (its destination is three per-head arrays, one of them transposed).
+// Fewest rounds R (a divisor of the FM block-rows) whose FM / R block-rows of every wave fit
+// in the LDS at once; bytes_per_block_row covers all the waves.
+constexpr int staging_rounds(int fm, int bytes_per_block_row, int lds_bytes)
+{
+    for (int r = 1; r <= fm; ++r)
+        if (fm % r == 0 && (fm / r) * bytes_per_block_row <= lds_bytes) return r;
+    return fm + 1;   // does not fit even one block-row at a time: caught by the static_assert
+}
+
+template <Epi EPI, int WTM, int WTN, int NW, int LDS_BYTES>
+__device__ __forceinline__ void store_tile(const GemmProblem& p, f32x16 (&acc)[WTN / 32][WTM / 32],
+                                           char* lds, int r0, int c0, int wave, int lane)
+{
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    const int fr = lane & 31, fg = lane >> 5;
+    if constexpr (EPI == Epi::Qkv) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = r0 + j * 32 + fr;
+            if (m >= p.M) continue;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = c0 + i * 32 + 8 * q + 4 * fg;
+                    if (n < p.N)
+                        store_out<EPI, bf16>(p, m, n,
+                                             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                   acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+                }
+        }
+    } else {
+        constexpr int PITCH = WTN * 4 + 16;                 // bytes per staged row
+        constexpr int R = staging_rounds(FM, NW * 32 * PITCH, LDS_BYTES);   // rounds
+        constexpr int FMR = FM / R, RR = FMR * 32;          // block-rows and rows per round
+        static_assert(NW * RR * PITCH <= LDS_BYTES, "staging does not fit");
+        constexpr int V4 = WTN / 4;                         // 4-column vectors per row
+        constexpr int PER_LANE = RR * V4 / 64;
+        char* region = lds + wave * RR * PITCH;
+        // Every wave is past its last operand read, and this wave's slab loads (including the
+        // unused one past the end of K) have landed, before the operand LDS is overwritten.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+            for (int jj = 0; jj < FMR; ++jj)
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j = rr * FMR + jj;
+                        *reinterpret_cast<f32x4*>(region + (jj * 32 + fr) * PITCH +
+                                                  (i * 32 + 8 * q + 4 * fg) * 4) =
+                            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]};
+                    }
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < PER_LANE; ++t) {
+                const int idx = lane + 64 * t;
+                const int row = idx / V4, v4 = idx - row * V4;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(region + row * PITCH + v4 * 16);
+                const int m = r0 + rr * RR + row, n = c0 + v4 * 4;
+                if (m < p.M && n < p.N) store_out<EPI, bf16>(p, m, n, v);
+            }
+            if (rr + 1 < R) __syncthreads();
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
 {
@@ -280,22 +360,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // acc[i][j][4 q + v] = C[m0 + wm*WTM + 32 j + fr][n0 + wn*WTN + 32 i + 8 q + 4 fg + v]
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 32 + fr;
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * fg;
-                if (n < p.N)
-                    store_out<EPI, bf16>(p, m, n,
-                                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
-            }
-    }
+    store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
+                                                   m0 + wm * WTM, n0 + wn * WTN, wave, lane);
 }
 
 // ---- bf16 GEMM, 32-wide slabs in a 4-stage LDS ring -------------------------------------
@@ -342,14 +408,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
     const int lchunk = (lane & 3) ^ (lane >> 4);
     const int L_w = (G - wave + NW - 1) / NW;
     typedef __attribute__((address_space(3))) void* lds_ptr;
-    // fetch(k0 >= K) moves no memory (out-of-range offsets) but still issues L_w loads, which
-    // keeps the vmcnt arithmetic uniform.
-    auto fetch = [&](int k0, int buf) {
+    // fetch_part(k0, buf, LO, HI) issues this wave's loads LO .. HI-1 of a slab; fetch(k0 >= K)
+    // moves no memory (out-of-range offsets) but still issues L_w loads, which keeps the vmcnt
+    // arithmetic uniform.
+    auto fetch_part = [&](int k0, int buf, auto lo_c, auto hi_c) {
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
         const bool kin = k0 + lchunk * 8 < p.K;
         const uint32_t kb = (uint32_t)k0 * 2u;
         bf16* slab = smem + buf * (BM + BN) * BK;
 #pragma unroll
-        for (int i = 0; i < LMAX; ++i) {
+        for (int i = LO; i < HI; ++i) {
             const int g = wave + i * NW;
             // With GA and GB multiples of NW, group i of every wave is in A iff i < GA / NW: a
             // compile-time choice (no branch splits the loop body).
@@ -366,6 +434,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
                     0, 0);
             }
         }
+    };
+    auto fetch = [&](int k0, int buf) {
+        fetch_part(k0, buf, std::integral_constant<int, 0>{}, std::integral_constant<int, LMAX>{});
     };
     const int fr = lane & 31;
     const int fg = lane >> 5;
@@ -399,66 +470,67 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
     };
     constexpr int NM = FM * FN;
     constexpr int NR = FM + FN;
-    auto interleave = [&](auto loads) {
-        InterleaveGroups<0, NM, NR, decltype(loads)::value ? LMAX : 0>::emit();
+    // A slab's loads are split between the two MFMA phases of an iteration (SPLIT before the
+    // barrier, the rest after it), so that the waves' global loads reach the address unit
+    // spread over the whole iteration rather than in one burst.
+    constexpr int SPLIT = (LMAX + 1) / 2;
+    auto interleave = [&](auto nv) {
+        InterleaveGroups<0, NM, NR, decltype(nv)::value>::emit();
     };
-    // Wait until this wave's loads of all but the two newest slabs have landed: s_waitcnt with
-    // vmcnt = 2 L_w, expcnt and lgkmcnt left at their maxima (gfx9 encoding).
-    constexpr int kWaitHi = ((2 * LMAX) & 15) | (((2 * LMAX) >> 4) << 14) | (7 << 4) | (15 << 8);
-    constexpr int kWaitLo =
-        ((2 * (LMAX - 1)) & 15) | (((2 * (LMAX - 1)) >> 4) << 14) | (7 << 4) | (15 << 8);
-    auto wait_two_slabs = [&]() {
+    // s_waitcnt immediate with vmcnt = n, expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+#define TPS_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+    // Prologue: slab 0 has landed once at most the two newer slabs' loads are outstanding.
+    auto wait_prologue = [&]() {
         if (G % NW == 0 || L_w == LMAX)
-            __builtin_amdgcn_s_waitcnt(kWaitHi);
+            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(2 * LMAX));
         else
-            __builtin_amdgcn_s_waitcnt(kWaitLo);
+            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(2 * (LMAX - 1)));
     };
+    // In iteration kt, slab kt+1 has landed once at most slab kt+2's loads and the first part
+    // of slab kt+3's are outstanding.
+    auto wait_next_slab = [&]() {
+        if (G % NW == 0 || L_w == LMAX)
+            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(LMAX + SPLIT));
+        else
+            __builtin_amdgcn_s_waitcnt(TPS_VMCNT((LMAX - 1) + (SPLIT < LMAX - 1 ? SPLIT : LMAX - 1)));
+    };
+#undef TPS_VMCNT
 
     bf16x8 fa[2][FM], fb[2][FN];
     const int KT = (p.K + BK - 1) / BK;
     fetch(0, 0);
     fetch(BK, 1);
     fetch(2 * BK, 2);
-    wait_two_slabs();    // slab 0 has landed (slabs 1, 2 may be in flight)
+    wait_prologue();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, fa[0], fb[0]);
     // Iteration kt: slab kt in buffer kt % 4, its K-step 0 fragments in set 0.
-    //   load slab kt+3 into buffer (kt+3) % 4 (last read before the previous barrier) |
-    //   read step 1 | MFMAs step 0 | wait for slab kt+1, barrier | read slab kt+1 step 0 |
-    //   MFMAs step 1.
+    //   first part of slab kt+3's loads into buffer (kt+3) % 4 (last read before the previous
+    //   barrier) | read step 1 | MFMAs step 0 | wait for slab kt+1, barrier | rest of slab
+    //   kt+3's loads | read slab kt+1 step 0 | MFMAs step 1.
+    using Split = std::integral_constant<int, SPLIT>;
+    using Rest = std::integral_constant<int, LMAX - SPLIT>;
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 3;
+        const int k3 = (kt + 3) * BK, b3 = (kt + 3) & 3;
         __builtin_amdgcn_sched_barrier(0);
-        fetch((kt + 3) * BK, (kt + 3) & 3);
+        fetch_part(k3, b3, std::integral_constant<int, 0>{}, Split{});
         read_frags(cur, 1, fa[1], fb[1]);
         mma(fa[0], fb[0]);
-        interleave(std::true_type{});
+        interleave(Split{});
         __builtin_amdgcn_sched_barrier(0);
-        wait_two_slabs();
+        wait_next_slab();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        fetch_part(k3, b3, Split{}, std::integral_constant<int, LMAX>{});
         read_frags((kt + 1) & 3, 0, fa[0], fb[0]);   // past the last slab: zeros, unused
         mma(fa[1], fb[1]);
-        interleave(std::false_type{});
+        interleave(Rest{});
         __builtin_amdgcn_sched_barrier(0);
     }
-    // acc[i][j][4 q + v] = C[m0 + wm*WTM + 32 j + fr][n0 + wn*WTN + 32 i + 8 q + 4 fg + v]
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 32 + fr;
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * fg;
-                if (n < p.N)
-                    store_out<EPI, bf16>(p, m, n,
-                                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
-            }
-    }
+    store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
+                                                   m0 + wm * WTM, n0 + wn * WTN, wave, lane);
 }
 
 // ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
