@@ -11,10 +11,15 @@
 // output; a new key tile with maximum m' rescales both by exp(m - m'). This gives exactly
 // the softmax result (up to rounding) without materialising the seq x seq score matrix.
 //
-// Work decomposition: one workgroup = 4 waves = BQ = 128 queries of one (sequence, head);
-// each wave owns 32 queries (two 16-query MFMA columns). Keys stream through LDS in tiles
-// of 64 (K tile [64][d], V^T tile [d][64], double-buffered, loaded from global memory
-// directly into LDS during the previous tile's work). Per tile, a wave computes
+// Work decomposition: one workgroup = BQ = 128 queries of one (sequence, head), run by two
+// sets of 4 waves; in each set a wave owns 32 queries (two 16-query MFMA columns). The key
+// tiles (64 keys: K tile [64][d], V^T tile [d][64]) are dealt to the sets alternately (set 0
+// the even tiles, set 1 the odd ones), each set streaming its own tiles through its own
+// double-buffered LDS ring (loaded from global memory directly into LDS during the previous
+// tile's work). Every SIMD thus runs two independent waves, one of each set, so one wave's
+// softmax arithmetic overlaps the other's matrix products. At the end the two partial
+// results of each query (running max, denominator, unnormalised output) are merged through
+// LDS with the same max-rescaling, which keeps the result exact. Per tile, a wave computes
 //   S^T = K Q^T      (MFMA "M" = keys, "N" = queries, K = d)
 //   O^T += V^T P^T   (MFMA "M" = d,    "N" = queries, K = keys)
 // With keys on the MFMA's row side, each lane's accumulator values of S^T all belong to ONE
@@ -24,14 +29,16 @@
 // tiles that cross a wave's diagonal or the end of the sequence; the scale is folded into the
 // exponent's FMA; the output is rescaled only when some running maximum grew. Queries are
 // dispatched longest-first (highest query tile first) to shorten the causal tail.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace tps {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BQ = 128;     // queries per workgroup
+constexpr int kThreads = 512;   // two sets of 4 waves
+constexpr int BQ = 128;     // queries per workgroup (per set)
 constexpr int BKV = 64;     // keys per tile
 constexpr int QPW = 32;     // queries per wave
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -46,7 +53,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, in
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
 {
     constexpr int KS = D / 32;            // MFMA K-steps of the S product
     constexpr int DB = D / 16;            // 16-row blocks of O^T
@@ -55,19 +62,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
     constexpr int KI = BKV / KRPI / 4;    // K load instructions per wave per tile
     constexpr int VI = D / 8 / 4;         // V^T load instructions per wave per tile (8 rows each)
 
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * D];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][D * BKV];
+    // [set][buffer][K tile | V^T tile]; reused for the merge of the two sets' partials.
+    __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * 2 * BKV * D];
+    auto tileK = [&](int set, int buf) { return lds + ((set * 2 + buf) * 2) * BKV * D; };
+    auto tileV = [&](int set, int buf) { return lds + ((set * 2 + buf) * 2 + 1) * BKV * D; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int set = __builtin_amdgcn_readfirstlane(tid >> 8);   // which half of the key tiles
+    // query group within the set; scalar, so that the per-tile causal tests below (whole tile
+    // visible, tile crossing this wave's diagonal) are wave-uniform branches
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     const int fr = lane & 15;
     const int fg = lane >> 4;
     // 16-byte chunk swizzle of a tile row: the 16 rows of one MFMA operand read (same logical
     // chunk) land on 16 distinct 16-byte groups of the LDS's 64 banks. 256-byte rows (K, d =
     // 128) fill the 256 bytes the banks serve per pass on their own; 128-byte rows (K for
     // d = 64, V^T) share it with their neighbour row.
-    auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    // MFMA row r of S^T block kb holds key krow(kb, r) of the tile: blocks 2j and 2j + 1 cover
+    // keys 32j .. 32j + 31 such that the probabilities a lane ends up holding for one P V^T
+    // operand (rows 4fg .. 4fg + 3 of both blocks) are the 8 consecutive keys 32j + 8fg + 0..7,
+    // i.e. one 16-byte V^T chunk. Rows read together (fixed kb, r = 0..15) are
+    // 32j + 4h + 8a + b (a, b = 0..3), which the K swizzles below keep on distinct bank groups.
+    auto krow = [](int kb, int r) { return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3); };
+    auto kswz = [](int row) {
+        return D == 128 ? ((row & 3) | (((row >> 3) & 3) << 2))
+                        : (((row >> 1) & 1) | (((row >> 3) & 3) << 1));
+    };
     auto vswz = [](int row) { return (row >> 1) & 7; };
 
     // Longest-first: block 0 takes the last query tile of every (sequence, head) first.
@@ -106,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
     // 16 bytes at byte 16 l of its destination, so the lane fetches the logical chunk that the
     // swizzle places there. K tile: wave w loads rows KRPI (w + 4 i) + ...; V^T tile: rows
     // (d) 8 (w + 4 i) + (l >> 3).
-    auto fetch = [&](int k0, int buf) {
+    auto fetchK = [&](int k0, int buf) {
+        bf16* sK = tileK(set, buf);
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
             const int rbase = KRPI * (wave + 4 * i);
@@ -115,15 +137,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
             const int c = phys ^ kswz(row);
             const uint32_t off = (uint32_t)((k0 + row) * KROW + c * 16);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rK, (lds_ptr)(&sK[buf][rbase * D]), 16, k0 + row < p.seq ? off : kOutOfRange, 0, 0, 0);
+                rK, (lds_ptr)(sK + rbase * D), 16, k0 + row < p.seq ? off : kOutOfRange, 0, 0, 0);
         }
+    };
+    auto fetchV = [&](int k0, int buf) {
+        bf16* sV = tileV(set, buf);
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int rbase = 8 * (wave + 4 * i);
             const int row = rbase + (lane >> 3);
             const int c = (lane & 7) ^ vswz(row);
             const uint32_t off = (uint32_t)(((int64_t)row * p.ld_vt + k0 + c * 8) * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr)(&sV[buf][rbase * BKV]), 16, off,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr)(sV + rbase * BKV), 16, off,
                                                      0, 0, 0);
         }
     };
@@ -135,118 +160,180 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
     float l_run[2] = {0.f, 0.f};               // this lane's share of the denominator
     const float sl2 = p.scale_log2;
 
-    fetch(0, 0);
-    __syncthreads();
+    // The running maximum is raised only when a tile's maximum exceeds it by more than
+    // 2^kLazy in probability (FlashAttention's result does not depend on which maximum is
+    // subtracted, as long as numerator and denominator use the same one); in between, the
+    // probabilities stay below 2^kLazy and the rescale of the output is skipped.
+    constexpr float kLazy = 8.0f;
+    const float lazy_raw = kLazy / sl2;
 
-    for (int t = 0; t < n_kv; ++t) {
-        const int cur = t & 1;
-        const int k0 = t * BKV;
-        if (t + 1 < n_kv) fetch(k0 + BKV, cur ^ 1);
-
-        // A wave whose queries all precede this key tile has nothing to add (causal).
-        const bool active = !CAUSAL || k0 <= qw0 + QPW - 1;
-        if (active) {
-            // ---- S^T = K Q^T : s[kb][qb][i] = score(key k0+16kb+4fg+i, query qw0+16qb+fr)
-            f32x4 s[4][2];
+    // ---- the three phases of one key tile
+    // S^T = K Q^T : s[kb][qb][i] = score(key k0 + krow(kb, 4fg + i), query qw0 + 16qb + fr),
+    // masked (keys past the query or past the end of the sequence) when MASKED.
+    auto scores = [&](const bf16* sKc, int k0, auto masked_c, f32x4 (&s)[4][2]) {
+        constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int row = kb * 16 + fr;
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int row = krow(kb, fr);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int c = ks * 4 + fg;
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                        &sK[cur][row * D + ((c ^ kswz(row)) << 3)]);
-                    s[kb][0] = mfma16x16x32(kf, qf[0][ks], s[kb][0]);
-                    s[kb][1] = mfma16x16x32(kf, qf[1][ks], s[kb][1]);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = ks * 4 + fg;
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8*>(&sKc[row * D + ((c ^ kswz(row)) << 3)]);
+                s[kb][0] = mfma16x16x32(kf, qf[0][ks], s[kb][0]);
+                s[kb][1] = mfma16x16x32(kf, qf[1][ks], s[kb][1]);
             }
-            // ---- mask (only tiles crossing this wave's diagonal or the end of the sequence)
-            const bool partial = k0 + BKV > p.seq || (CAUSAL && k0 + BKV - 1 > qw0);
-            if (partial) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const int q = qw0 + qb * 16 + fr;
-                    const int lim = CAUSAL ? min(q, p.seq - 1) : p.seq - 1;   // last visible key
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (k0 + kb * 16 + 4 * fg + i > lim) s[kb][qb][i] = -INFINITY;
-                }
-            }
-            // ---- running max (raw scores; the positive scale preserves order)
-            float mx[2];
+        }
+        if constexpr (MASKED) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                float m = s[0][qb][0];
+                const int q = qw0 + qb * 16 + fr;
+                const int lim = CAUSAL ? min(q, p.seq - 1) : p.seq - 1;   // last visible key
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kb][qb][i]);
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                mx[qb] = fmaxf(m_run[qb], m);
+                    for (int i = 0; i < 4; ++i)
+                        if (k0 + krow(kb, 4 * fg + i) > lim) s[kb][qb][i] = -INFINITY;
             }
-            // ---- rescale only if some lane's maximum moved (then alpha < 1 for that query)
-            const bool grew = (mx[0] > m_run[0]) || (mx[1] > m_run[1]);
-            if (__any(grew)) {
+        }
+    };
+    // Running max, (lazy) rescale of the output and denominator, P = exp2((s - m) scale
+    // log2 e) <= 2^kLazy packed as bf16 B-operands: pf[qb][j] = keys 32j + 8fg + 0..7.
+    auto softmax = [&](f32x4 (&s)[4][2], bf16x8 (&pf)[2][2]) {
+        float mx[2];
+        bool grew = false;
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const float alpha = m_run[qb] == -INFINITY
-                                            ? 0.f
-                                            : __builtin_amdgcn_exp2f((m_run[qb] - mx[qb]) * sl2);
-                    l_run[qb] *= alpha;
+        for (int qb = 0; qb < 2; ++qb) {
+            float m = s[0][qb][0];
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-                }
-            }
-            // ---- P = exp2((s - m) scale log2 e), packed as bf16 B-operands
-            bf16x8 pf[2][2];   // [qb][j]: keys k0+32j+{4fg..4fg+3, 16+4fg..16+4fg+3}
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kb][qb][i]);
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            mx[qb] = m;
+            grew = grew || m > m_run[qb] + lazy_raw;
+        }
+        if (__any(grew)) {
+            // (a scheduling fence keeps this a real branch: the rescale is rare, and
+            // speculating it would put 64 multiplies on every tile)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                m_run[qb] = mx[qb];
-                const float mo = mx[qb] == -INFINITY ? 0.f : -mx[qb] * sl2;
-                float ls = 0.f;
+                const float mn = fmaxf(m_run[qb], mx[qb]);
+                const float alpha =
+                    m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[qb] - mn) * sl2);
+                m_run[qb] = mn;
+                l_run[qb] *= alpha;
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], sl2, mo));
-                        s[kb][qb][i] = e;
-                        ls += e;
-                    }
-                l_run[qb] += ls;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pf[qb][j][i] = to_bf16(s[2 * j][qb][i]);
-                        pf[qb][j][4 + i] = to_bf16(s[2 * j + 1][qb][i]);
-                    }
-                }
+                for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
             }
-            // ---- O^T += V^T P^T
+        }
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int row = db * 16 + fr;
-                const int x = vswz(row);
+        for (int qb = 0; qb < 2; ++qb) {
+            const float mo = m_run[qb] == -INFINITY ? 0.f : -m_run[qb] * sl2;
+            float ls = 0.f;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    // keys 32j + 4fg + (0..3): 8-byte slot 8j + fg; keys + 16: slot 8j + 4 + fg
-                    const int s0 = 8 * j + fg, s1 = 8 * j + 4 + fg;
-                    const int a0 = row * BKV + ((((s0 >> 1) ^ x) << 1) + (s0 & 1)) * 4;
-                    const int a1 = row * BKV + ((((s1 >> 1) ^ x) << 1) + (s1 & 1)) * 4;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(&sV[cur][a0]);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(&sV[cur][a1]);
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    acc[db][0] = mfma16x16x32(vf, pf[0][j], acc[db][0]);
-                    acc[db][1] = mfma16x16x32(vf, pf[1][j], acc[db][1]);
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], sl2, mo));
+                    s[kb][qb][i] = e;
+                    ls += e;
+                }
+            l_run[qb] += ls;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[qb][j][i] = to_bf16(s[2 * j][qb][i]);
+                    pf[qb][j][4 + i] = to_bf16(s[2 * j + 1][qb][i]);
                 }
             }
         }
-        __syncthreads();   // the next tile has landed (the compiler waits for the loads first)
+    };
+    // O^T += V^T P^T
+    auto pv = [&](const bf16* sVc, const bf16x8 (&pf)[2][2]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int row = db * 16 + fr;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+                    &sVc[row * BKV + (((4 * j + fg) ^ vswz(row)) << 3)]);
+                acc[db][0] = mfma16x16x32(vf, pf[0][j], acc[db][0]);
+                acc[db][1] = mfma16x16x32(vf, pf[1][j], acc[db][1]);
+            }
+        }
+    };
+    // A tile is needed by a wave unless all the wave's queries precede it (causal).
+    auto needed = [&](int t) { return t < n_kv && (!CAUSAL || t * BKV <= qw0 + QPW - 1); };
+
+    // Set s takes key tiles s, s + 2, s + 4, ...: in iteration it both sets score, weight and
+    // accumulate one tile each (2 it + s) from their own double-buffered LDS ring, loading the
+    // tile after next meanwhile; the iterations end in the shared workgroup barrier, set 1
+    // idling in the last one when n_kv is odd. (Rotating set 1's phases against set 0's so
+    // that one set's exponentials meet the other's matrix products measured slower.)
+    const int n_it = (n_kv + 1) / 2;
+    if (set < n_kv) {
+        fetchK(set * BKV, 0);
+        fetchV(set * BKV, 0);
     }
+    __syncthreads();
+
+    auto window = [&](int it, auto masked_c) {
+        const int cur = it & 1, t = 2 * it + set, k0 = t * BKV;
+        if (t + 2 < n_kv) {
+            fetchK(k0 + 2 * BKV, cur ^ 1);
+            fetchV(k0 + 2 * BKV, cur ^ 1);
+        }
+        // Unmasked windows only meet tiles that every query of the workgroup sees in full.
+        if (!decltype(masked_c)::value || needed(t)) {
+            f32x4 s[4][2];
+            bf16x8 pf[2][2];
+            scores(tileK(set, cur), k0, masked_c, s);
+            softmax(s, pf);
+            pv(tileV(set, cur), pf);
+        }
+        __syncthreads();   // the next tile has landed (the compiler waits for the loads first)
+    };
+    // Windows whose two tiles lie inside the sequence and wholly before the workgroup's first
+    // query (causal) need no mask; the rest (the diagonal, a ragged end) do.
+    const int full_tiles = min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV);
+    const int n_full_it = min(full_tiles / 2, n_it);
+    int it = 0;
+    for (; it < n_full_it; ++it) window(it, std::false_type{});
+    for (; it < n_it; ++it) window(it, std::true_type{});
+
+    // ---- merge the two sets' partials: set 1 publishes (output, max, denominator) of each of
+    // its lanes; the set-0 wave with the same queries (same wave index, same lane) combines
+    // them, rescaling each side by exp(m_side - m) with m the larger maximum.
+    float lq[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float l = l_run[qb];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        lq[qb] = l;
+    }
+    constexpr int NF = DB * 2 * 4 + 4;   // floats per lane: output, 2 maxima, 2 denominators
+    static_assert(4 * NF * 64 * 4 <= (int)sizeof(lds), "merge area");
+    float* xch = reinterpret_cast<float*>(lds) + wave * NF * 64 + lane;   // [wave][field][lane]
+    if (set == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xch[((db * 2 + qb) * 4 + i) * 64] = acc[db][qb][i];
+        xch[(NF - 4) * 64] = m_run[0];
+        xch[(NF - 3) * 64] = m_run[1];
+        xch[(NF - 2) * 64] = lq[0];
+        xch[(NF - 1) * 64] = lq[1];
+    }
+    __syncthreads();
+    if (set == 1) return;
 
     // ---- normalise and store O[token][head*D + d], 4 consecutive d per lane
     const int b = bh / p.heads_local;
@@ -255,16 +342,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnProblem p)
     bf16* __restrict__ gO = reinterpret_cast<bf16*>(p.o);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        float l = l_run[qb];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const float inv = 1.0f / l;
+        const float m1 = xch[(NF - 4 + qb) * 64];
+        const float l1 = xch[(NF - 2 + qb) * 64];
+        const float m0 = m_run[qb];
+        const float m = fmaxf(m0, m1);
+        // set 0 always holds key 0, which every query sees, so m0 and m are finite
+        const float a0 = __builtin_amdgcn_exp2f((m0 - m) * sl2);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * sl2);
+        const float inv = 1.0f / (lq[qb] * a0 + l1 * a1);
         const int q = qw0 + qb * 16 + fr;
         if (q >= p.seq) continue;
         bf16* dst = gO + ((int64_t)b * p.seq + q) * ldo + head * D + 4 * fg;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<bf16x4*>(dst + db * 16) = to_bf16x4(acc[db][qb] * inv);
+        for (int db = 0; db < DB; ++db) {
+            f32x4 o1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
+            *reinterpret_cast<bf16x4*>(dst + db * 16) = to_bf16x4((acc[db][qb] * a0 + o1 * a1) * inv);
+        }
     }
 }
 
