@@ -24,6 +24,27 @@ softmax attention (query by query) and the partial sum are plain loops in ``orac
                                 W_V and the same rows of W_O (llms.blog, "Partitioning
                                 Multi-Head and Grouped-Query Attention", steps 1-3).
 * ``sum_partials``              the all-reduce's sum (llms.blog, "Row-Parallel Linear Layer").
+* ``silu``/``swiglu_column``/``swiglu_shard``
+                                gated MLP shard SiLU(X W_gate,r) * (X W_up,r) W_down,r with the
+                                gate and up projections split by columns and W_down by rows
+                                (llms.blog, "Partitioning the MLP Block", steps 2-3).
+* ``layernorm``/``sp_rows``/``reduce_scatter``/``all_gather``/``sp_boundary``
+                                sequence parallelism: the row-parallel partials are summed onto
+                                rank r's s/N slice of every sequence (reduce-scatter), the
+                                residual is added and LayerNorm runs on the slice; an
+                                all-gather restores the full sequence (llms.blog, "Sequence
+                                Parallelism"; reduce-scatter then all-gather is the all-reduce).
+* ``kv_heads_of_rank``/``attn_shard_gqa``
+                                grouped-query attention: H_kv key/value heads, each shared by
+                                H / H_kv query heads; a rank holds H_kv / N of them, or one
+                                duplicated head when N > H_kv (llms.blog, "Grouped-Query
+                                Attention (GQA) Constraints").
+* ``gelu_grad``/``mlp_shard_backward``
+                                rank r's gradients of the MLP shard: dY = dZ B_r^T, dP = dY *
+                                GeLU'(P), dA_r = X^T dP, da_r = column sums of dP,
+                                dB_r = Y_r^T dZ and the input-gradient partial dX_r = dP A_r^T,
+                                whose sum over ranks is the backward all-reduce (llms.blog,
+                                "Partitioning the MLP Block", closing paragraph).
 
 Unequal splits raise ``OracleError``: the pages only use exact shards. Every function is
 pinned in ``tests/test_oracle.py``.
@@ -79,6 +100,17 @@ def _load():
     lib.oracle_gelu_array.argtypes = [_d, _d, _i64]
     lib.oracle_attention.argtypes = [_d, _d, _d, _d, _i64, _i64, _int, _i64, _int, _i64p, _i64]
     lib.oracle_attention.restype = _int
+    lib.oracle_gelu_grad.restype = ctypes.c_double
+    lib.oracle_gelu_grad.argtypes = [ctypes.c_double]
+    lib.oracle_gelu_grad_array.argtypes = [_d, _d, _i64]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_silu_array.argtypes = [_d, _d, _i64]
+    lib.oracle_layernorm.argtypes = [_d, _d, _d, ctypes.c_double, _i64, _i64, _d]
+    lib.oracle_layernorm.restype = _int
+    lib.oracle_attention_gqa.argtypes = [_d, _d, _d, _d, _i64, _i64, _int, _int, _i64, _int,
+                                         _i64p, _i64]
+    lib.oracle_attention_gqa.restype = _int
     lib.oracle_sum_partials.argtypes = [_f, _int, _i64, _d]
     lib.oracle_sum_partials.restype = _int
     lib.oracle_max_threads.restype = _int
@@ -120,6 +152,35 @@ def gelu(x):
     x = _as_d(x)
     y = np.empty_like(x)
     _load().oracle_gelu_array(_dp(x), _dp(y), x.size)
+    return y
+
+
+def gelu_grad(x):
+    """GeLU'(x) = Phi(x) + x phi(x)."""
+    x = _as_d(x)
+    y = np.empty_like(x)
+    _load().oracle_gelu_grad_array(_dp(x), _dp(y), x.size)
+    return y
+
+
+def silu(x):
+    """SiLU(x) = x sigmoid(x)."""
+    x = _as_d(x)
+    y = np.empty_like(x)
+    _load().oracle_silu_array(_dp(x), _dp(y), x.size)
+    return y
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5):
+    """Row-wise (x - mean) / sqrt(var + eps) * gamma + beta over the last dimension."""
+    x = _as_d(x)
+    cols = x.shape[-1]
+    g, b = _as_d(gamma), _as_d(beta)
+    if g.shape != (cols,) or b.shape != (cols,):
+        raise OracleError("layernorm: gamma/beta must have %d entries" % cols)
+    y = np.empty_like(x)
+    _check(_load().oracle_layernorm(_dp(x), _dp(g), _dp(b), float(eps), x.size // cols, cols,
+                                    _dp(y)), "layernorm")
     return y
 
 
@@ -178,17 +239,21 @@ def qkv_shard(X, Wq, Wk, Wv, bq=None, bk=None, bv=None, H: int = 1, N: int = 1, 
 
 
 def attention(Q, K, V, batch: int, seq: int, n_heads: int, causal: bool = True,
-              rows=None) -> np.ndarray:
-    """softmax(Q_j K_j^T / sqrt(d) + mask) V_j per head j, heads concatenated, on query rows."""
+              rows=None, n_kv_heads: Optional[int] = None) -> np.ndarray:
+    """softmax(Q_j K_g^T / sqrt(d) + mask) V_g per query head j, heads concatenated, on query
+    rows; g = j / (n_heads / n_kv_heads) is the key/value head (g = j when n_kv_heads is None)."""
     Q, K, V = _as_d(Q), _as_d(K), _as_d(V)
     T, w = Q.shape
     d = w // n_heads
+    hkv = n_heads if n_kv_heads is None else int(n_kv_heads)
+    if K.shape != (T, hkv * d) or V.shape != (T, hkv * d):
+        raise OracleError("attention: K and V must be [%d, %d]" % (T, hkv * d))
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     nq = T if rws is None else rws.size
     O = np.empty((nq, w), dtype=np.float64)
-    _check(_load().oracle_attention(_dp(Q), _dp(K), _dp(V), _dp(O), batch, seq, n_heads, d,
-                                    int(bool(causal)),
-                                    None if rws is None else rws.ctypes.data_as(_i64p), nq),
+    _check(_load().oracle_attention_gqa(_dp(Q), _dp(K), _dp(V), _dp(O), batch, seq, n_heads,
+                                        hkv, d, int(bool(causal)),
+                                        None if rws is None else rws.ctypes.data_as(_i64p), nq),
            "attention")
     return O
 
@@ -232,6 +297,137 @@ def attn_shard(X, Wq, Wk, Wv, bq, bk, bv, Wo, batch: int, seq: int, H: int, N: i
     O = attention(Q, K, V, batch, seq, Hl, causal, rows=rws)
     Z = out_proj_shard(O, Wo, H, N, r)
     return (Z, O) if want_heads else Z
+
+
+# ---- grouped-query attention ------------------------------------------------------------------
+def kv_heads_of_rank(H: int, H_kv: int, N: int, r: int) -> range:
+    """Global key/value heads rank r holds: H_kv / N contiguous heads when N divides H_kv,
+    else (N a multiple of H_kv: the heads are duplicated) the one head its query heads read."""
+    if H_kv < 1 or H % H_kv != 0:
+        raise OracleError("%d query heads are not a multiple of %d key/value heads" % (H, H_kv))
+    if H % N != 0 or N < 1 or r < 0 or r >= N:
+        raise OracleError("%d query heads cannot be split over N=%d for rank %d" % (H, N, r))
+    if H_kv % N == 0:
+        n = H_kv // N
+        return range(r * n, (r + 1) * n)
+    if N % H_kv == 0:
+        g = (r * (H // N)) // (H // H_kv)
+        return range(g, g + 1)
+    raise OracleError("%d key/value heads neither divide nor are divided by N=%d" % (H_kv, N))
+
+
+def attn_shard_gqa(X, Wq, Wk, Wv, bq, bk, bv, Wo, batch: int, seq: int, H: int, H_kv: int,
+                   N: int = 1, r: int = 0, causal: bool = True, rows=None,
+                   want_heads: bool = False):
+    """Rank r's grouped-query attention partial on the requested token rows.
+
+    Wq [h, H d] and Wo [H d, h] as in ``attn_shard``; Wk, Wv [h, H_kv d]. Rank r owns query
+    heads r H/N .. and the key/value heads of ``kv_heads_of_rank``; local query head j reads
+    local key/value head (global j) / (H / H_kv) - (first local key/value head).
+    """
+    X = np.asarray(X)
+    T, h = X.shape
+    if T != batch * seq:
+        raise OracleError("X has %d rows, batch*seq = %d" % (T, batch * seq))
+    if h % H != 0:
+        raise OracleError("hidden %d is not divisible by %d heads" % (h, H))
+    d = h // H
+    kvr = kv_heads_of_rank(H, H_kv, N, r)
+    Hl = H // N
+    qc = slice(r * Hl * d, (r + 1) * Hl * d)
+    kc = slice(kvr.start * d, kvr.stop * d)
+    rws = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if rws.size and (rws.min() < 0 or rws.max() >= T):
+        raise OracleError("row index out of range")
+    sl = lambda b, c: None if b is None else b[c]
+    nkv = len(kvr)
+    Q = np.zeros((T, Hl * d))
+    K = np.zeros((T, nkv * d))
+    V = np.zeros((T, nkv * d))
+    for b in np.unique(rws // seq):
+        pos = rws[rws // seq == b] % seq
+        need = int(pos.max()) + 1 if causal else seq
+        blk = slice(b * seq, b * seq + need)
+        K[blk] = linear(X[blk], Wk[:, kc], sl(bk, kc))
+        V[blk] = linear(X[blk], Wv[:, kc], sl(bv, kc))
+    Q[rws] = linear(X[rws], Wq[:, qc], sl(bq, qc))
+    # The global map (query head -> key/value head = head / (H / H_kv)) restricted to this
+    # rank is local query head j -> local key/value head j / (Hl / nkv), which is what
+    # ``attention`` applies with nkv key/value heads.
+    group = H // H_kv
+    loc = [(r * Hl + j) // group - kvr.start for j in range(Hl)]
+    if Hl % nkv != 0 or loc != [j // (Hl // nkv) for j in range(Hl)]:
+        raise OracleError("rank %d's query heads read key/value heads it does not hold" % r)
+    O = attention(Q, K, V, batch, seq, Hl, causal, rows=rws, n_kv_heads=nkv)
+    Z = linear(O, Wo[qc, :])
+    return (Z, O) if want_heads else Z
+
+
+# ---- sequence parallelism --------------------------------------------------------------------
+def sp_rows(batch: int, seq: int, N: int, r: int) -> np.ndarray:
+    """Token rows (t = b seq + s) of rank r's sequence slice s in [r seq/N, (r+1) seq/N)."""
+    sl = _split(seq, N, r, "seq")
+    return (np.arange(batch, dtype=np.int64)[:, None] * seq
+            + np.arange(sl.start, sl.stop, dtype=np.int64)[None, :]).ravel()
+
+
+def reduce_scatter(parts, batch: int, seq: int, N: int, r: int) -> np.ndarray:
+    """sum_q parts[q] on rank r's rows only: [batch seq/N, h] (fp64)."""
+    P = np.asarray(parts, dtype=np.float32)
+    rows = sp_rows(batch, seq, N, r)
+    return sum_partials(np.ascontiguousarray(P[:, rows, :]))
+
+
+def all_gather(slices, batch: int, seq: int) -> np.ndarray:
+    """Concatenate the N ranks' sequence slices back into [batch seq, h]."""
+    N = len(slices)
+    h = np.shape(slices[0])[-1]
+    out = np.empty((batch * seq, h), dtype=np.asarray(slices[0]).dtype)
+    for r, s in enumerate(slices):
+        out[sp_rows(batch, seq, N, r)] = s
+    return out
+
+
+def sp_boundary(parts, residual_r, gamma, beta, batch: int, seq: int, N: int, r: int,
+                eps: float = 1e-5):
+    """Rank r's block boundary: H_r = reduce_scatter(parts) + residual_r, Y_r = LayerNorm(H_r)."""
+    Hr = reduce_scatter(parts, batch, seq, N, r) + _as_d(residual_r)
+    return Hr, layernorm(Hr, gamma, beta, eps)
+
+
+# ---- SwiGLU MLP shard --------------------------------------------------------------------------
+def swiglu_column(X, Wg, Wu, N: int, r: int) -> np.ndarray:
+    """A_r = SiLU(X Wg_r) * (X Wu_r) with Wg_r, Wu_r the r-th column slices."""
+    cols = _split(np.shape(Wg)[1], N, r, "F")
+    if np.shape(Wu) != np.shape(Wg):
+        raise OracleError("gate and up projections differ in shape")
+    return silu(linear(X, Wg[:, cols])) * linear(X, Wu[:, cols])
+
+
+def swiglu_shard(X, Wg, Wu, Wd, N: int = 1, r: int = 0) -> np.ndarray:
+    """Rank r's partial A_r Wd_r with Wd_r = Wd[r F/N:(r+1) F/N, :]; N = 1 is the whole block."""
+    rows = _split(np.shape(Wd)[0], N, r, "F")
+    return linear(swiglu_column(X, Wg, Wu, N, r), Wd[rows, :])
+
+
+# ---- backward pass of the MLP shard ------------------------------------------------------------
+def mlp_shard_backward(X, A, a, B, dZ, N: int = 1, r: int = 0) -> dict:
+    """Gradients of rank r's MLP partial Z_r = GeLU(X A_r + a_r) B_r for an upstream dZ.
+
+    The loss sees Z = sum_r Z_r, so every rank receives the same dZ; dX is the sum over ranks
+    of the returned dX partials. Returns dX [T, h] (rank r's partial), dA [h, F/N], da [F/N]
+    and dB [F/N, h].
+    """
+    cols = _split(np.shape(A)[1], N, r, "F")
+    X = _as_d(X)
+    dZ = _as_d(dZ)
+    Ar = _as_d(A[:, cols])
+    Br = _as_d(B[cols, :])
+    P = linear(X, Ar, None if a is None else a[cols])
+    Y = gelu(P)
+    dY = dZ @ Br.T
+    dP = dY * gelu_grad(P)
+    return {"dX": dP @ Ar.T, "dA": X.T @ dP, "da": dP.sum(axis=0), "dB": Y.T @ dZ}
 
 
 # ---- partial sum ----------------------------------------------------------------------------
