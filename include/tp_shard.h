@@ -133,6 +133,34 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Gated (SwiGLU) MLP shard:
+ *   Z_i = (SiLU(X W_gate,i) * (X W_up,i)) W_down,i     (llms.blog, "Partitioning the MLP
+ *                                                      Block", steps 2-3: gate and up
+ *                                                      projections split by columns, the
+ *                                                      element-wise product local, the
+ *                                                      down projection split by rows)
+ * SiLU(x) = x sigmoid(x) = x / (1 + exp(-x)); the gated product * is element-wise.
+ *
+ *   X        [tokens, hidden]   bf16  replicated input
+ *   Wgate_i  [ffn/N, hidden]    bf16  rank's column shard of W_gate, stored transposed:
+ *                                     Wgate_i[j][k] = W_gate[k][rank*ffn/N + j]
+ *   Wup_i    [ffn/N, hidden]    bf16  the same for W_up
+ *   Wdown_i  [hidden, ffn/N]    bf16  rank's row shard of W_down, stored transposed:
+ *                                     Wdown_i[o][j] = W_down[rank*ffn/N + j][o]
+ *   Z_i      [tokens, hidden]   fp32  rank's partial (to be summed over ranks)
+ *   workspace: A_i = SiLU(X W_gate,i) * (X W_up,i) [tokens, ffn/N] bf16 at byte offset 0.
+ * dt: TP_BF16 only (TP_ERR_DTYPE otherwise). No biases (the gated layers of the models the
+ * page names have none). hidden and ffn/N must be multiples of 8.
+ * ---------------------------------------------------------------------------------------- */
+size_t tp_swiglu_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                                 tp_dtype dt);
+
+tp_status tp_swiglu_shard_fwd(const void* X, const void* Wgate_i, const void* Wup_i,
+                              const void* Wdown_i, float* Z_i, int64_t tokens, int64_t hidden,
+                              int64_t ffn, int n_shards, int rank, tp_dtype dt,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Attention shard: Z_i = concat_j(Head_j) W_O,i over the rank's heads j, with
  *   Head_j = softmax(Q_j K_j^T / sqrt(d) + M) V_j      (llms.blog attention, steps 1-3)
  * d = hidden / n_heads; Hl = n_heads / N local heads, rank r owning heads r*Hl ... r*Hl+Hl-1.
@@ -198,7 +226,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 3
+#define TP_SHARD_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

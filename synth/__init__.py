@@ -10,7 +10,10 @@ from .inputs import (  # noqa: F401
     bf16_round,
     bf16_bits,
     attn_inputs,
+    gqa_inputs,
+    layernorm_params,
     mlp_inputs,
+    swiglu_inputs,
     normal_matrix,
     partials_inputs,
     sample_rows,

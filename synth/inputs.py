@@ -64,6 +64,7 @@ class Workload:
     hidden: int               # h
     ffn: int = 0              # F (MLP width)
     heads: int = 0            # H (attention heads); head dim d = h / H
+    kv_heads: int = 0         # H_kv (grouped-query attention; 0 = H)
     batch: int = 1
     seq: int = 0
     n_shards: int = 1         # TP degree N
@@ -101,6 +102,32 @@ WORKLOADS: Dict[str, Workload] = {
             name="mlp_block_bf16_t2048_h12288_f49152", kind="mlp", dtype="bf16",
             tokens=2048, hidden=12288, ffn=49152, n_shards=8,
             description="all N shards of one bf16 MLP block plus on-device sum, N in {1,2,4,8}"),
+        # Paths next to the core shard (none of these is among the measured configurations
+        # above; the shapes follow the model family the pages name for each feature).
+        Workload(
+            name="swiglu_shard_bf16_t4096_h8192_f28672_n8", kind="swiglu", dtype="bf16",
+            tokens=4096, batch=1, seq=4096, hidden=8192, ffn=28672, n_shards=8,
+            description="one rank's gated (SwiGLU) MLP shard of a LLaMA-style layer: W_gate,i and "
+                        "W_up,i 8192x3584, W_down,i 3584x8192, fp32 partial"),
+        Workload(
+            name="gqa_shard_bf16_b1_s4096_h8192_H64_kv8_n8", kind="gqa", dtype="bf16",
+            tokens=4096, batch=1, seq=4096, hidden=8192, heads=64, kv_heads=8, n_shards=8,
+            description="one rank's grouped-query attention shard: 8 local query heads sharing "
+                        "one local key/value head (64 query and 8 key/value heads, d=128)"),
+        Workload(
+            name="gqa_shard_bf16_b1_s4096_h8192_H64_kv4_n8", kind="gqa", dtype="bf16",
+            tokens=4096, batch=1, seq=4096, hidden=8192, heads=64, kv_heads=4, n_shards=8,
+            description="the same with 4 key/value heads on N=8 ranks: each key/value head is "
+                        "duplicated on 2 ranks"),
+        Workload(
+            name="sp_boundary_bf16_b1_s4096_h8192_n8", kind="sp", dtype="bf16",
+            tokens=4096, batch=1, seq=4096, hidden=8192, n_shards=8,
+            description="sequence-parallel block boundary of one rank: reduce-scatter of 8 fp32 "
+                        "partials onto its 512-token slice, residual add, LayerNorm"),
+        Workload(
+            name="mlp_bwd_bf16_t4096_h8192_f32768_n8", kind="mlp_bwd", dtype="bf16",
+            tokens=4096, batch=1, seq=4096, hidden=8192, ffn=32768, n_shards=8,
+            description="backward pass of one rank's bf16 MLP shard (the layer's ffn shard 4096)"),
     ]
 }
 
@@ -161,6 +188,51 @@ def attn_inputs(w: Workload, seed: int = 0, with_bias: bool = True,
     if w.dtype == "bf16":
         out = {k: bf16_round(v) for k, v in out.items()}
     return out
+
+
+def swiglu_inputs(w: Workload, seed: int = 0, tokens: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Full gated-MLP tensors in the pages' layout, drawn in the order X, W_gate, W_up, W_down:
+    X [T, h], Wg and Wu [h, F], Wd [F, h]; float32, bf16-exact for bf16 workloads."""
+    T = w.tokens if tokens is None else tokens
+    h, F = w.hidden, w.ffn
+    rng = np.random.default_rng(seed)
+    out = dict(X=normal_matrix(rng, (T, h), w.x_std))
+    out["Wg"] = normal_matrix(rng, (h, F), _std(w, h))
+    out["Wu"] = normal_matrix(rng, (h, F), _std(w, h))
+    out["Wd"] = normal_matrix(rng, (F, h), _std(w, F))
+    if w.dtype == "bf16":
+        out = {k: bf16_round(v) for k, v in out.items()}
+    return out
+
+
+def gqa_inputs(w: Workload, seed: int = 0, batch: Optional[int] = None,
+               seq: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Grouped-query attention tensors, drawn in the order X, W_Q, W_K, W_V, b_Q, b_K, b_V,
+    W_O: W_Q [h, H d], W_K and W_V [h, H_kv d], W_O [H d, h] (d = h / H)."""
+    b = w.batch if batch is None else batch
+    s = w.seq if seq is None else seq
+    h, H = w.hidden, w.heads
+    hkv = w.kv_heads or H
+    d = h // H
+    rng = np.random.default_rng(seed)
+    out = dict(X=normal_matrix(rng, (b * s, h), w.x_std))
+    out["Wq"] = normal_matrix(rng, (h, H * d), _std(w, h))
+    out["Wk"] = normal_matrix(rng, (h, hkv * d), _std(w, h))
+    out["Wv"] = normal_matrix(rng, (h, hkv * d), _std(w, h))
+    out["bq"] = normal_matrix(rng, (H * d,), _std(w, h))
+    out["bk"] = normal_matrix(rng, (hkv * d,), _std(w, h))
+    out["bv"] = normal_matrix(rng, (hkv * d,), _std(w, h))
+    out["Wo"] = normal_matrix(rng, (H * d, h), _std(w, h))
+    if w.dtype == "bf16":
+        out = {k: bf16_round(v) for k, v in out.items()}
+    return out
+
+
+def layernorm_params(h: int, seed: int = 0) -> Dict[str, np.ndarray]:
+    """LayerNorm gain and shift of width h: gamma ~ 1 + N(0, 0.1), beta ~ N(0, 0.1), fp32."""
+    rng = np.random.default_rng(seed + 104729)
+    return dict(gamma=(1.0 + 0.1 * rng.standard_normal(h)).astype(np.float32),
+                beta=(0.1 * rng.standard_normal(h)).astype(np.float32))
 
 
 def partials_inputs(n_parts: int, numel: int, seed: int = 0, integer: bool = False) -> np.ndarray:

@@ -28,7 +28,8 @@ STATUS_NAMES = {
 
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
-    "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd", "tp_attn_workspace_bytes",
+    "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
+    "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
     "tp_last_error", "tp_abi_version",
 )
@@ -72,6 +73,11 @@ def lib():
     L.tp_mlp_shard_fwd.restype = _int
     L.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                    _vp, _sz, _vp]
+    L.tp_swiglu_workspace_bytes.restype = _sz
+    L.tp_swiglu_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
+    L.tp_swiglu_shard_fwd.restype = _int
+    L.tp_swiglu_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                      _int, _vp, _sz, _vp]
     L.tp_attn_workspace_bytes.restype = _sz
     L.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int]
     L.tp_attn_workspace_layout.restype = _int
@@ -137,6 +143,17 @@ def tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z_i, tokens, hidden, ffn, n_shards, rank,
     return lib().tp_mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(Z_i), tokens,
                                   hidden, ffn, n_shards, rank, dt, _ptr(workspace),
                                   workspace_bytes, _stream(stream))
+
+
+def tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:
+    return lib().tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, dt)
+
+
+def tp_swiglu_shard_fwd(X, Wgate_i, Wup_i, Wdown_i, Z_i, tokens, hidden, ffn, n_shards, rank,
+                        dt, workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_swiglu_shard_fwd(_ptr(X), _ptr(Wgate_i), _ptr(Wup_i), _ptr(Wdown_i),
+                                     _ptr(Z_i), tokens, hidden, ffn, n_shards, rank, dt,
+                                     _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, dt) -> int:

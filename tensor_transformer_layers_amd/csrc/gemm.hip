@@ -9,6 +9,10 @@
 //   Bias      Y = X W_i + b_i                           column-parallel, no activation
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
 //             per head, V written transposed for the attention kernel's P V product.
+//   SwiGlu    A_i = SiLU(X W_gate,i) * (X W_up,i)       gated column-parallel MLP layer: the
+//             block's B slab interleaves gate and up rows in 32-row blocks (loaded from the
+//             two weights), so each wave's pairs of 32-column MFMA blocks hold the gate and
+//             up products of the same features and the gate is applied in registers.
 //
 // Block = 8 waves (512 lanes, two per SIMD) in a WM x WN grid (4 waves in 2 x 2 for the fp32
 // kernel and as a tuning option), each wave owning a (BM/WM) x (BN/WN) output tile of
@@ -107,6 +111,21 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
             }
         }
     }
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// SwiGlu: the wave's 32-column blocks alternate gate (even) and up (odd) for the same 32
+// features; combine each pair in place into the gated activation.
+template <int FN, int FM>
+__device__ __forceinline__ void swiglu_combine(f32x16 (&acc)[FN][FM], f32x16 (&out)[FN / 2][FM])
+{
+#pragma unroll
+    for (int k = 0; k < FN / 2; ++k)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) out[k][j][v] = silu(acc[2 * k][j][v]) * acc[2 * k + 1][j][v];
 }
 
 // ---- bf16 GEMM ---------------------------------------------------------------------------
@@ -242,14 +261,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     const int wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
+    // SwiGlu: the B tile's BN rows are BN / 2 gate rows and the same BN / 2 up rows.
+    constexpr bool GLU = EPI == Epi::SwiGlu;
+    static_assert(!GLU || FN % 2 == 0, "SwiGlu pairs the wave's 32-column blocks");
     const int tiles_m = (p.M + BM - 1) / BM;
-    const int tiles_n = (p.N + BN - 1) / BN;
+    const int tiles_n = ((GLU ? 2 * p.N : p.N) + BN - 1) / BN;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int f0 = GLU ? n0 / 2 : n0;       // first B row (output feature) of the tile
 
     const __amdgpu_buffer_rsrc_t rA = tile_rsrc(p.A, m0, min(BM, p.M - m0), p.lda, 2);
-    const __amdgpu_buffer_rsrc_t rB = tile_rsrc(p.B, n0, min(BN, p.N - n0), p.ldb, 2);
+    const __amdgpu_buffer_rsrc_t rB =
+        tile_rsrc(p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
+    const __amdgpu_buffer_rsrc_t rB2 =
+        tile_rsrc(GLU ? p.B2 : p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
 
     // Slabs go from global memory straight into LDS (buffer_load ... lds): one instruction
     // moves 8 rows x 128 bytes, lane l writing the 16 bytes at byte 16 l of its wave's
@@ -257,6 +283,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     // logical chunk that the XOR swizzle stores there: (l & 7) ^ ((row >> 1) & 7). Wave w
     // moves the 8-row groups w, w + NW, ... of each operand.
     const int grp_row = lane >> 3;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // scalar copy (descriptor choice)
     // row = 8 (wave + NW i) + grp_row with NW even, so (row >> 1) & 7 = 4 (wave & 1) + (lane >> 4)
     const int lchunk = (lane & 7) ^ (((wave & 1) << 2) + (lane >> 4));
     const uint32_t offA = (uint32_t)((wave * 8 + grp_row) * p.lda + lchunk * 8) * 2u;
@@ -279,10 +306,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
                 rA, (lds_ptr)(sA + i * 8 * NW * BK), 16,
                 kin ? offA + i * stepA + kb : kOutOfRange, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BCH; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rB, (lds_ptr)(sB + i * 8 * NW * BK), 16,
-                kin ? offB + i * stepB + kb : kOutOfRange, 0, 0, 0);
+        for (int i = 0; i < BCH; ++i) {
+            if constexpr (GLU) {
+                // LDS row group gi = wave + i NW lies in 32-row block gi / 4: even blocks hold
+                // gate rows, odd ones the up rows of the same features.
+                const int gi = wave_u + i * NW;
+                const int blk = gi >> 2;
+                const uint32_t off =
+                    (uint32_t)((((blk >> 1) * 32 + (gi & 3) * 8 + grp_row) * p.ldb + lchunk * 8) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    (blk & 1) ? rB2 : rB, (lds_ptr)(sB + i * 8 * NW * BK), 16,
+                    kin ? off + kb : kOutOfRange, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (lds_ptr)(sB + i * 8 * NW * BK), 16,
+                    kin ? offB + i * stepB + kb : kOutOfRange, 0, 0, 0);
+            }
+        }
     };
 
     const int fr = lane & 31;   // operand row within a 32-row block
@@ -360,8 +400,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
-                                                   m0 + wm * WTM, n0 + wn * WTN, wave, lane);
+    if constexpr (GLU) {
+        f32x16 gacc[FN / 2][FM];
+        swiglu_combine<FN, FM>(acc, gacc);
+        store_tile<Epi::Bias, WTM, WTN / 2, NW, (int)sizeof(smem)>(
+            p, gacc, reinterpret_cast<char*>(smem), m0 + wm * WTM, f0 + wn * (WTN / 2), wave, lane);
+    } else {
+        store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
+                                                       m0 + wm * WTM, n0 + wn * WTN, wave, lane);
+    }
 }
 
 // ---- bf16 GEMM, 32-wide slabs in a 4-stage LDS ring -------------------------------------
@@ -392,13 +439,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int wm = wave / WN, wn = wave % WN;
+    constexpr bool GLU = EPI == Epi::SwiGlu;
+    static_assert(!GLU || FN % 2 == 0, "SwiGlu pairs the wave's 32-column blocks");
     const int tiles_m = (p.M + BM - 1) / BM;
-    const int tiles_n = (p.N + BN - 1) / BN;
+    const int tiles_n = ((GLU ? 2 * p.N : p.N) + BN - 1) / BN;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int f0 = GLU ? n0 / 2 : n0;       // first B row (output feature) of the tile
     const __amdgpu_buffer_rsrc_t rA = tile_rsrc(p.A, m0, min(BM, p.M - m0), p.lda, 2);
-    const __amdgpu_buffer_rsrc_t rB = tile_rsrc(p.B, n0, min(BN, p.N - n0), p.ldb, 2);
+    const __amdgpu_buffer_rsrc_t rB =
+        tile_rsrc(p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
+    const __amdgpu_buffer_rsrc_t rB2 =
+        tile_rsrc(GLU ? p.B2 : p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
 
     // One load instruction moves 16 rows x 64 bytes: lane l writes row (l >> 2), physical
     // chunk (l & 3) of its destination, so it fetches logical chunk (l & 3) ^ ((row >> 2) & 3)
@@ -428,10 +481,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
                                                          kin ? off : kOutOfRange, 0, 0, 0);
             } else if (even || g < G) {
                 const int gb = g - GA;
-                const uint32_t off = (uint32_t)((16 * gb + grp_row) * p.ldb + lchunk * 8) * 2u + kb;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16, kin ? off : kOutOfRange, 0,
-                    0, 0);
+                if constexpr (GLU) {
+                    // 16-row group gb lies in 32-row block gb / 2: gate rows in even blocks,
+                    // the up rows of the same features in odd ones
+                    const int blk = gb >> 1;
+                    const uint32_t off = (uint32_t)((((blk >> 1) * 32 + (gb & 1) * 16 + grp_row) *
+                                                         p.ldb + lchunk * 8) * 2) + kb;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        (blk & 1) ? rB2 : rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16,
+                        kin ? off : kOutOfRange, 0, 0, 0);
+                } else {
+                    const uint32_t off =
+                        (uint32_t)((16 * gb + grp_row) * p.ldb + lchunk * 8) * 2u + kb;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16, kin ? off : kOutOfRange,
+                        0, 0, 0);
+                }
             }
         }
     };
@@ -529,8 +594,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem 
         interleave(Rest{});
         __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
-                                                   m0 + wm * WTM, n0 + wn * WTN, wave, lane);
+    if constexpr (GLU) {
+        f32x16 gacc[FN / 2][FM];
+        swiglu_combine<FN, FM>(acc, gacc);
+        store_tile<Epi::Bias, WTM, WTN / 2, NW, (int)sizeof(smem)>(
+            p, gacc, reinterpret_cast<char*>(smem), m0 + wm * WTM, f0 + wn * (WTN / 2), wave, lane);
+    } else {
+        store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
+                                                       m0 + wm * WTM, n0 + wn * WTN, wave, lane);
+    }
 }
 
 // ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
@@ -650,7 +722,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
 template <int BM, int BN, int WM, int WN, bool S4>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
-    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int ncols = epi == Epi::SwiGlu ? 2 * p.N : p.N;   // gate and up columns
+    const int tiles = ((p.M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
     dim3 grid(tiles), block(64 * WM * WN);
 #define TPS_LAUNCH(E)                                                                        \
     if constexpr (S4)                                                                        \
@@ -662,6 +735,13 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         case Epi::F32: TPS_LAUNCH(Epi::F32) break;
         case Epi::Qkv: TPS_LAUNCH(Epi::Qkv) break;
         case Epi::Bias: TPS_LAUNCH(Epi::Bias) break;
+        case Epi::SwiGlu:
+            if constexpr ((BN / WN / 32) % 2 == 0) {
+                TPS_LAUNCH(Epi::SwiGlu)
+            } else {
+                return hipErrorInvalidValue;   // the wave's column blocks do not pair up
+            }
+            break;
     }
 #undef TPS_LAUNCH
     return hipGetLastError();
@@ -729,11 +809,45 @@ hipError_t gemm_bf16_tile(const GemmProblem& p, Epi epi, hipStream_t s, GemmTile
 
 // Eight waves (two per SIMD) per workgroup by default: while one wave of a SIMD waits on
 // LDS or the slab barrier, the other keeps the matrix core busy.
+// SwiGlu needs an even number of 32-column blocks per wave (gate / up pairs): the 8-wave
+// 256 x 256 (64 columns per wave) and 256 x 128 (64) layouts and the 4-wave ones except
+// 256 x 192.
+static bool glu_ok(GemmTile t, bool w4)
+{
+    if (w4) return t.bn != 192;
+    return (t.bm == 256 && t.bn == 256) || (t.bm == 256 && t.bn == 128);
+}
+
+static GemmTile glu_pick_tile(int M, int N, bool* w4)
+{
+    // same cost model as gemm_bf16_pick_tile over the 2 N gate and up columns
+    struct Cand { int bm, bn; bool w4; double cost; };
+    const Cand cands[] = {{256, 256, false, 1.00}, {256, 128, false, 1.12}, {128, 128, true, 1.45}};
+    GemmTile best{256, 256};
+    bool bw4 = false;
+    double best_t = 1e300;
+    for (const Cand& c : cands) {
+        const long tiles = (long)((M + c.bm - 1) / c.bm) * ((2L * N + c.bn - 1) / c.bn);
+        const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
+        if (t < best_t - 1e-9) { best_t = t; best = GemmTile{c.bm, c.bn}; bw4 = c.w4; }
+    }
+    *w4 = bw4;
+    return best;
+}
+
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
-    GemmTile t = gemm_bf16_pick_tile(p.M, p.N, p.K);
     bool w4 = false, s4 = false;
-    tile_override(t, w4, s4);
+    GemmTile t;
+    if (epi == Epi::SwiGlu) {
+        t = glu_pick_tile(p.M, p.N, &w4);
+        GemmTile o = t;
+        bool ow4 = false, os4 = false;
+        if (tile_override(o, ow4, os4) && glu_ok(o, ow4)) { t = o; w4 = ow4; s4 = os4; }
+    } else {
+        t = gemm_bf16_pick_tile(p.M, p.N, p.K);
+        tile_override(t, w4, s4);
+    }
     return s4 ? gemm_bf16_tile<true>(p, epi, s, t, w4) : gemm_bf16_tile<false>(p, epi, s, t, w4);
 }
 

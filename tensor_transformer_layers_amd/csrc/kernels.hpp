@@ -13,11 +13,13 @@ enum class Epi : int {
     F32 = 1,        // C = acc                   stored as fp32 (row-parallel partial Z_i)
     Qkv = 2,        // acc + bias[n] scattered to Q / K / V^T per head, bf16
     Bias = 3,       // C = acc + bias[n]         stored in the GEMM's element type
+    SwiGlu = 4,     // C = SiLU(X B^T) * (X B2^T), N output features, bf16 (gated MLP)
 };
 
 struct GemmProblem {
     const void* A;        // [M, K] row-major, leading dimension lda (elements)
     const void* B;        // [N, K] row-major (weight in [out, in] layout), ldb
+    const void* B2;       // SwiGlu: the up projection [N, K] (B is the gate), ldb
     const void* bias;     // [N] or nullptr
     void* C;              // [M, N] row-major, ldc (BiasGelu / F32)
     int64_t lda, ldb, ldc;

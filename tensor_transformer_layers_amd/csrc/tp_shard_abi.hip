@@ -216,6 +216,51 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
     return hip_status(e, "row-parallel kernel launch");
 }
 
+size_t tp_swiglu_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                                 tp_dtype dt)
+{
+    if (dt != TP_BF16) return 0;
+    if (validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt) != TP_OK) return 0;
+    return round_up((size_t)tokens * (size_t)(ffn / n_shards) * 2, 256);
+}
+
+tp_status tp_swiglu_shard_fwd(const void* X, const void* Wgate_i, const void* Wup_i,
+                              const void* Wdown_i, float* Z_i, int64_t tokens, int64_t hidden,
+                              int64_t ffn, int n_shards, int rank, tp_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    if (!X || !Wgate_i || !Wup_i || !Wdown_i || !Z_i)
+        return fail(TP_ERR_NULL, "X, Wgate_i, Wup_i, Wdown_i and Z_i must be non-NULL");
+    if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "the SwiGLU shard supports TP_BF16 only (got %d)", (int)dt);
+    tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(Wgate_i) || !aligned16(Wup_i) || !aligned16(Wdown_i) ||
+        !aligned16(Z_i) || (workspace && !aligned16(workspace)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t need = tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    st = check_device();
+    if (st != TP_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t fl = ffn / n_shards;
+    // Column-parallel gate and up projections with the gate applied locally:
+    // A_i = SiLU(X W_gate,i) * (X W_up,i), [tokens, F/N] (no communication).
+    tps::GemmProblem g{};
+    g.A = X; g.lda = hidden;
+    g.B = Wgate_i; g.B2 = Wup_i; g.ldb = hidden;
+    g.C = workspace; g.ldc = fl;
+    g.M = (int)tokens; g.N = (int)fl; g.K = (int)hidden;
+    hipError_t e = tps::gemm_bf16(g, tps::Epi::SwiGlu, s);
+    if (e != hipSuccess) return hip_status(e, "gated column-parallel kernel launch");
+    // Row-parallel down projection: Z_i = A_i W_down,i, [tokens, hidden] fp32 partial.
+    e = launch_row(workspace, Wdown_i, Z_i, tokens, fl, hidden, dt, s);
+    return hip_status(e, "row-parallel kernel launch");
+}
+
 tp_status tp_column_parallel_fwd(const void* X, const void* W_i, const void* b_i, void* Y_i,
                                  int64_t rows, int64_t in_features, int64_t out_features,
                                  int n_shards, int rank, tp_activation act, tp_dtype dt,

@@ -106,6 +106,37 @@ def mlp_shard(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor], B
     return Z, workspace
 
 
+# ---- gated (SwiGLU) MLP ----------------------------------------------------------------------
+def swiglu_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, device="cuda"):
+    nbytes = B.tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, B.TP_BF16)
+    if nbytes == 0:
+        raise B.TPError(B.TP_ERR_SHAPE, "invalid SwiGLU shard sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def swiglu_shard(X: torch.Tensor, Wg_i: torch.Tensor, Wu_i: torch.Tensor, Wd_i: torch.Tensor,
+                 n_shards: int, rank: int, Z: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Rank ``rank``'s gated MLP partial (SiLU(X Wg_i^T) * (X Wu_i^T)) Wd_i^T.
+
+    Wg_i, Wu_i [F/N, h], Wd_i [h, F/N], bf16 (see include/tp_shard.h). Returns (Z_i fp32
+    [tokens, hidden], workspace); the gated activation A_i [tokens, F/N] bf16 sits at offset
+    0 of the workspace (``mlp_hidden_view``).
+    """
+    _require_cuda(X, Wg_i, Wu_i, Wd_i)
+    tokens, hidden = X.shape
+    fl = Wg_i.shape[0]
+    ffn = fl * n_shards
+    if Z is None:
+        Z = torch.empty(tokens, hidden, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = swiglu_workspace(tokens, hidden, ffn, n_shards, X.device)
+    st = B.tp_swiglu_shard_fwd(X, Wg_i, Wu_i, Wd_i, Z, tokens, hidden, ffn, n_shards, rank,
+                               _dt(X), workspace, workspace.numel(), _stream(stream))
+    B.check(st)
+    return Z, workspace
+
+
 # ---- attention ---------------------------------------------------------------------------
 def attn_workspace(batch: int, seq: int, hidden: int, n_heads: int, n_shards: int, device="cuda"):
     nbytes = B.tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, B.TP_BF16)

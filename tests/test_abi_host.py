@@ -58,6 +58,27 @@ def _mlp(**kw):
     return B.tp_mlp_shard_fwd(**a)
 
 
+def _swiglu(**kw):
+    a = dict(X=P, Wgate_i=P, Wup_i=P, Wdown_i=P, Z_i=P, tokens=4096, hidden=8192, ffn=28672,
+             n_shards=8, rank=0, dt=BF16, workspace=P, workspace_bytes=BIG)
+    a.update(kw)
+    return B.tp_swiglu_shard_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), 1), (dict(Wgate_i=None), 1), (dict(Wup_i=None), 1), (dict(Wdown_i=None), 1),
+    (dict(Z_i=None), 1),
+    (dict(n_shards=3), 3),                 # 28672 % 3 != 0
+    (dict(tokens=0), 2), (dict(rank=8), 4),
+    (dict(dt=F32), 5),                     # bf16 only
+    (dict(Wup_i=P + 8), 6), (dict(hidden=8196), 6),
+    (dict(workspace=None), 7), (dict(workspace_bytes=4096 * 3584 * 2 - 1), 7),
+])
+def test_swiglu_validation(kw, status):
+    assert _swiglu(**kw) == status
+    assert B.tp_last_error() != ""
+
+
 def _attn(**kw):
     a = dict(X=P, Wqkv_i=P, bqkv_i=None, Wo_i=P, Z_i=P, batch=4, seq=2048, hidden=4096,
              n_heads=32, causal=1, n_shards=8, rank=0, dt=BF16, workspace=P,
@@ -114,6 +135,9 @@ def test_workspace_sizes():
     assert B.tp_mlp_workspace_bytes(8192, 3072, 12288, 8, BF16) == 8192 * 1536 * 2
     assert B.tp_mlp_workspace_bytes(3, 8, 16, 2, BF16) == 256
     assert B.tp_mlp_workspace_bytes(32, 1024, 4096, 3, F32) == 0
+    # SwiGLU: the gated activation A_i [tokens, ffn/N] bf16
+    assert B.tp_swiglu_workspace_bytes(4096, 8192, 28672, 8, BF16) == 4096 * 3584 * 2
+    assert B.tp_swiglu_workspace_bytes(4096, 8192, 28672, 8, F32) == 0
     # attention: Q, K, V^T (seq padded to 8), O, each 256-byte aligned
     st, off = B.tp_attn_workspace_layout(4, 2048, 4096, 32, 8, BF16)
     assert st == 0
