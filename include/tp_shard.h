@@ -211,6 +211,52 @@ tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t nume
                           void* Z, tp_dtype out_dt, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Sequence-parallel block boundary (llms.blog, "Sequence Parallelism"): the all-reduce after
+ * a row-parallel layer becomes a reduce-scatter that sums the N partials but leaves rank r
+ * only its slice of every sequence, positions r*seq/N ... (r+1)*seq/N - 1; the residual
+ * addition and LayerNorm, which act on each token separately, run on that slice; an
+ * all-gather restores the full sequence before the next column-parallel layer (a
+ * reduce-scatter followed by an all-gather is the all-reduce, same page).
+ *
+ * Slice layout: slice row i = b*(seq/N) + s' holds token t = b*seq + r*(seq/N) + s'
+ * (token rows of the full tensors are t = b*seq + s). N = n_parts must divide seq.
+ *
+ * tp_reduce_scatter_partials:  H_r[i] = sum_q Z_parts[q][t(i)]
+ *   Z_parts  HOST array of n_parts DEVICE pointers, each [batch*seq, hidden] fp32
+ *   H_r      [batch*seq/N, hidden] out_dt (fp32, or bf16 rounded to nearest even)
+ * The sum runs in fp32 in the order q = 0, 1, ..., N-1 (the same bits as tp_sum_partials on
+ * those rows).
+ *
+ * tp_sp_residual_layernorm_fwd:  H_r[i] = sum_q Z_parts[q][t(i)] + residual_r[i],
+ *                                Y_r[i] = (H_r[i] - mean) / sqrt(var + eps) * gamma + beta
+ * with mean and the biased variance var taken over the hidden values of the row (fp32).
+ *   residual_r [batch*seq/N, hidden] dt, or NULL for none
+ *   gamma, beta [hidden] fp32;  eps >= 0
+ *   H_r, Y_r   [batch*seq/N, hidden] dt (H_r is the new residual stream, Y_r the normalised
+ *              input of the next block)
+ * dt: TP_F32 or TP_BF16. hidden must be a multiple of 8 and at most 16384 (the row is held
+ * in LDS).
+ *
+ * tp_all_gather_rows:  X[t] = slices[r(t)][i(t)]
+ *   slices  HOST array of n_parts DEVICE pointers, each [batch*seq/N, hidden] dt
+ *   X       [batch*seq, hidden] dt
+ * No output may alias an input. Errors as for the other calls; seq % N != 0 is
+ * TP_ERR_NOT_DIVISIBLE (the pages only use exact slices).
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_reduce_scatter_partials(const float* const* Z_parts, int n_parts, int64_t batch,
+                                     int64_t seq, int64_t hidden, int rank, void* H_r,
+                                     tp_dtype out_dt, void* stream);
+
+tp_status tp_sp_residual_layernorm_fwd(const float* const* Z_parts, int n_parts,
+                                       const void* residual_r, const float* gamma,
+                                       const float* beta, float eps, void* H_r, void* Y_r,
+                                       int64_t batch, int64_t seq, int64_t hidden, int rank,
+                                       tp_dtype dt, void* stream);
+
+tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t batch,
+                             int64_t seq, int64_t hidden, void* X, tp_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Which bf16 GEMM tile the library launches for C[M, N] = A[M, K] B[N, K]^T: block tile
  * rows x columns and waves per workgroup (honours the TPSHARD_GEMM_TILE override). A query
  * for profiling and tuning; it launches nothing. Returns TP_ERR_NULL / TP_ERR_SHAPE on bad
@@ -226,7 +272,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 4
+#define TP_SHARD_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,8 @@ STATUS_NAMES = {
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
     "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
-    "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_attn_workspace_bytes",
+    "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
+    "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
     "tp_last_error", "tp_abi_version",
 )
@@ -78,6 +79,15 @@ def lib():
     L.tp_swiglu_shard_fwd.restype = _int
     L.tp_swiglu_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
                                       _int, _vp, _sz, _vp]
+    L.tp_reduce_scatter_partials.restype = _int
+    L.tp_reduce_scatter_partials.argtypes = [ctypes.POINTER(_vp), _int, _i64, _i64, _i64, _int,
+                                             _vp, _int, _vp]
+    L.tp_sp_residual_layernorm_fwd.restype = _int
+    L.tp_sp_residual_layernorm_fwd.argtypes = [ctypes.POINTER(_vp), _int, _vp, _vp, _vp,
+                                               ctypes.c_float, _vp, _vp, _i64, _i64, _i64, _int,
+                                               _int, _vp]
+    L.tp_all_gather_rows.restype = _int
+    L.tp_all_gather_rows.argtypes = [ctypes.POINTER(_vp), _int, _i64, _i64, _i64, _vp, _int, _vp]
     L.tp_attn_workspace_bytes.restype = _sz
     L.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int]
     L.tp_attn_workspace_layout.restype = _int
@@ -154,6 +164,32 @@ def tp_swiglu_shard_fwd(X, Wgate_i, Wup_i, Wdown_i, Z_i, tokens, hidden, ffn, n_
     return lib().tp_swiglu_shard_fwd(_ptr(X), _ptr(Wgate_i), _ptr(Wup_i), _ptr(Wdown_i),
                                      _ptr(Z_i), tokens, hidden, ffn, n_shards, rank, dt,
                                      _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def _ptr_array(items):
+    arr = (_vp * max(1, len(items)))()
+    for i, t in enumerate(items):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def tp_reduce_scatter_partials(Z_parts, n_parts, batch, seq, hidden, rank, H_r, out_dt,
+                               stream=None) -> int:
+    return lib().tp_reduce_scatter_partials(_ptr_array(Z_parts), n_parts, batch, seq, hidden,
+                                            rank, _ptr(H_r), out_dt, _stream(stream))
+
+
+def tp_sp_residual_layernorm_fwd(Z_parts, n_parts, residual_r, gamma, beta, eps, H_r, Y_r,
+                                 batch, seq, hidden, rank, dt, stream=None) -> int:
+    return lib().tp_sp_residual_layernorm_fwd(_ptr_array(Z_parts), n_parts, _ptr(residual_r),
+                                              _ptr(gamma), _ptr(beta), eps, _ptr(H_r),
+                                              _ptr(Y_r), batch, seq, hidden, rank, dt,
+                                              _stream(stream))
+
+
+def tp_all_gather_rows(slices, n_parts, batch, seq, hidden, X, dt, stream=None) -> int:
+    return lib().tp_all_gather_rows(_ptr_array(slices), n_parts, batch, seq, hidden, _ptr(X),
+                                    dt, _stream(stream))
 
 
 def tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, dt) -> int:

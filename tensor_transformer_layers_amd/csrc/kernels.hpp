@@ -54,6 +54,26 @@ struct AttnProblem {
 
 hipError_t attention_fwd(const AttnProblem& p, hipStream_t stream);
 
+// Sequence-parallel block boundary of rank `rank`: rows of its s/N slice of every sequence
+// (slice row i = b * seq/N + s' is token b * seq + rank * seq/N + s').
+//   hout[i] = sum_q parts[q][token(i)] (+ resid[i]);  yout[i] = LayerNorm(hout[i]) if gamma
+struct SpProblem {
+    const float* const* parts;   // n_parts device pointers, each [batch * seq, hidden] fp32
+    int n_parts;                 // N (the slice count)
+    const void* resid;           // [batch * seq/N, hidden] or nullptr
+    const float* gamma;          // [hidden] fp32, nullptr: no LayerNorm (plain reduce-scatter)
+    const float* beta;           // [hidden] fp32
+    float eps;
+    void* hout;                  // [batch * seq/N, hidden]
+    void* yout;                  // [batch * seq/N, hidden] (with gamma)
+    int batch, seq, rank, hidden;
+    bool bf16;                   // resid, hout, yout element type: bf16 or fp32
+};
+hipError_t sp_boundary(const SpProblem& p, hipStream_t stream);
+// Full-sequence rows from the N slices: out[b * seq + r * seq/N + s'] = slices[r][b * seq/N + s'].
+hipError_t all_gather_rows(const void* const* slices, int n, int batch, int seq, int64_t row_bytes,
+                           void* out, hipStream_t stream);
+
 hipError_t sum_partials(const float* const* parts, int n_parts, int64_t numel, void* out,
                         bool out_bf16, hipStream_t stream);
 

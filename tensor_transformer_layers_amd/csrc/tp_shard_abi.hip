@@ -173,6 +173,33 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
     return TP_OK;
 }
 
+// ---- sequence-parallel boundary -------------------------------------------------------------
+tp_status validate_sp(int n_parts, int64_t batch, int64_t seq, int64_t hidden, int rank,
+                      tp_dtype dt, int64_t max_hidden)
+{
+    if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d not supported", (int)dt);
+    if (n_parts < 1 || n_parts > 64) return fail(TP_ERR_SHAPE, "n_parts=%d outside [1, 64]", n_parts);
+    if (batch < 1 || seq < 1 || hidden < 1)
+        return fail(TP_ERR_SHAPE, "batch, seq and hidden must be >= 1");
+    if (batch * seq > INT32_MAX || hidden > max_hidden)
+        return fail(TP_ERR_SHAPE, "batch*seq must be < 2^31 and hidden <= %lld", (long long)max_hidden);
+    if (seq % n_parts != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "seq=%lld not divisible into %d slices", (long long)seq, n_parts);
+    if (rank < 0 || rank >= n_parts) return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_parts);
+    if (hidden % 8 != 0) return fail(TP_ERR_ALIGN, "hidden=%lld must be a multiple of 8", (long long)hidden);
+    return TP_OK;
+}
+
+tp_status check_parts(const void* const* parts, int n_parts, const char* what)
+{
+    if (!parts) return fail(TP_ERR_NULL, "%s array is NULL", what);
+    for (int q = 0; q < n_parts; ++q) {
+        if (!parts[q]) return fail(TP_ERR_NULL, "%s %d is NULL (missing rank)", what, q);
+        if (!aligned16(parts[q])) return fail(TP_ERR_ALIGN, "%s %d is not 16-byte aligned", what, q);
+    }
+    return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -369,6 +396,72 @@ tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_
     g3.M = T; g3.N = (int)hidden; g3.K = w;
     e = tps::gemm_bf16(g3, tps::Epi::F32, s);
     return hip_status(e, "output projection launch");
+}
+
+tp_status tp_reduce_scatter_partials(const float* const* Z_parts, int n_parts, int64_t batch,
+                                     int64_t seq, int64_t hidden, int rank, void* H_r,
+                                     tp_dtype out_dt, void* stream)
+{
+    tp_status st = validate_sp(n_parts, batch, seq, hidden, rank, out_dt, INT32_MAX);
+    if (st != TP_OK) return st;
+    st = check_parts(reinterpret_cast<const void* const*>(Z_parts), n_parts, "partial");
+    if (st != TP_OK) return st;
+    if (!H_r) return fail(TP_ERR_NULL, "H_r must be non-NULL");
+    if (!aligned16(H_r)) return fail(TP_ERR_ALIGN, "H_r is not 16-byte aligned");
+    st = check_device();
+    if (st != TP_OK) return st;
+    tps::SpProblem p{};
+    p.parts = Z_parts; p.n_parts = n_parts;
+    p.hout = H_r;
+    p.batch = (int)batch; p.seq = (int)seq; p.rank = rank; p.hidden = (int)hidden;
+    p.bf16 = out_dt == TP_BF16;
+    return hip_status(tps::sp_boundary(p, reinterpret_cast<hipStream_t>(stream)),
+                      "reduce-scatter kernel launch");
+}
+
+tp_status tp_sp_residual_layernorm_fwd(const float* const* Z_parts, int n_parts,
+                                       const void* residual_r, const float* gamma,
+                                       const float* beta, float eps, void* H_r, void* Y_r,
+                                       int64_t batch, int64_t seq, int64_t hidden, int rank,
+                                       tp_dtype dt, void* stream)
+{
+    tp_status st = validate_sp(n_parts, batch, seq, hidden, rank, dt, 16384);   // row in LDS
+    if (st != TP_OK) return st;
+    st = check_parts(reinterpret_cast<const void* const*>(Z_parts), n_parts, "partial");
+    if (st != TP_OK) return st;
+    if (!gamma || !beta || !H_r || !Y_r)
+        return fail(TP_ERR_NULL, "gamma, beta, H_r and Y_r must be non-NULL");
+    if (!aligned16(gamma) || !aligned16(beta) || !aligned16(H_r) || !aligned16(Y_r) ||
+        (residual_r && !aligned16(residual_r)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(TP_ERR_SHAPE, "eps must be finite and >= 0");
+    st = check_device();
+    if (st != TP_OK) return st;
+    tps::SpProblem p{};
+    p.parts = Z_parts; p.n_parts = n_parts;
+    p.resid = residual_r; p.gamma = gamma; p.beta = beta; p.eps = eps;
+    p.hout = H_r; p.yout = Y_r;
+    p.batch = (int)batch; p.seq = (int)seq; p.rank = rank; p.hidden = (int)hidden;
+    p.bf16 = dt == TP_BF16;
+    return hip_status(tps::sp_boundary(p, reinterpret_cast<hipStream_t>(stream)),
+                      "sequence-parallel boundary kernel launch");
+}
+
+tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t batch, int64_t seq,
+                             int64_t hidden, void* X, tp_dtype dt, void* stream)
+{
+    tp_status st = validate_sp(n_parts, batch, seq, hidden, 0, dt, INT32_MAX);
+    if (st != TP_OK) return st;
+    st = check_parts(slices, n_parts, "slice");
+    if (st != TP_OK) return st;
+    if (!X) return fail(TP_ERR_NULL, "X must be non-NULL");
+    if (!aligned16(X)) return fail(TP_ERR_ALIGN, "X is not 16-byte aligned");
+    st = check_device();
+    if (st != TP_OK) return st;
+    return hip_status(tps::all_gather_rows(slices, n_parts, (int)batch, (int)seq,
+                                           hidden * (int64_t)dt_size(dt), X,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                      "all-gather kernel launch");
 }
 
 tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* tile_n, int* waves)

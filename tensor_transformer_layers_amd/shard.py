@@ -195,6 +195,57 @@ def sum_partials(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
     return out
 
 
+# ---- sequence parallelism ----------------------------------------------------------------------
+def reduce_scatter(parts: Sequence[torch.Tensor], batch: int, seq: int, rank: int,
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Rank ``rank``'s slice [batch*seq/N, hidden] of sum(parts) (N = len(parts))."""
+    _require_cuda(*parts)
+    N = len(parts)
+    hidden = parts[0].shape[-1]
+    if out is None:
+        out = torch.empty(batch * (seq // N), hidden, dtype=out_dtype, device=parts[0].device)
+    st = B.tp_reduce_scatter_partials(list(parts), N, batch, seq, hidden, rank, out,
+                                      _DT[out.dtype], _stream(stream))
+    B.check(st)
+    return out
+
+
+def sp_residual_layernorm(parts: Sequence[torch.Tensor], residual: Optional[torch.Tensor],
+                          gamma: torch.Tensor, beta: torch.Tensor, batch: int, seq: int,
+                          rank: int, eps: float = 1e-5, dtype=torch.bfloat16,
+                          H: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
+                          stream=None):
+    """(H_r, Y_r): the rank's slice of sum(parts) + residual, and its LayerNorm (fp32 gamma,
+    beta), both [batch*seq/N, hidden] of ``dtype``."""
+    _require_cuda(*parts, residual, gamma, beta)
+    N = len(parts)
+    hidden = parts[0].shape[-1]
+    rows = batch * (seq // N)
+    if H is None:
+        H = torch.empty(rows, hidden, dtype=dtype, device=parts[0].device)
+    if Y is None:
+        Y = torch.empty(rows, hidden, dtype=dtype, device=parts[0].device)
+    st = B.tp_sp_residual_layernorm_fwd(list(parts), N, residual, gamma, beta, float(eps), H, Y,
+                                        batch, seq, hidden, rank, _DT[dtype], _stream(stream))
+    B.check(st)
+    return H, Y
+
+
+def all_gather_rows(slices: Sequence[torch.Tensor], batch: int, seq: int,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The full [batch*seq, hidden] tensor from the N ranks' sequence slices."""
+    _require_cuda(*slices)
+    N = len(slices)
+    hidden = slices[0].shape[-1]
+    if out is None:
+        out = torch.empty(batch * seq, hidden, dtype=slices[0].dtype, device=slices[0].device)
+    st = B.tp_all_gather_rows(list(slices), N, batch, seq, hidden, out, _DT[out.dtype],
+                              _stream(stream))
+    B.check(st)
+    return out
+
+
 # ---- one rank's Transformer layer ------------------------------------------------------------
 class LayerShard:
     """Rank ``rank`` of an N-way tensor-parallel layer: attention block then MLP block.

@@ -79,6 +79,29 @@ def test_swiglu_validation(kw, status):
     assert B.tp_last_error() != ""
 
 
+def test_sp_validation():
+    parts = [P] * 8
+    # reduce-scatter: seq not divisible into N slices, bad rank, missing rank, dtype
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4095, 8192, 0, P, F32) == 3
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4096, 8192, 8, P, F32) == 4
+    assert B.tp_reduce_scatter_partials([P, None] + [P] * 6, 8, 1, 4096, 8192, 0, P, F32) == 1
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4096, 8192, 0, P, 3) == 5
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4096, 8196, 0, P, F32) == 6
+    assert B.tp_reduce_scatter_partials(parts, 0, 1, 4096, 8192, 0, P, F32) == 2
+    # residual + LayerNorm: hidden above the per-row LDS limit, NULL gamma, bad eps
+    lnargs = dict(Z_parts=parts, n_parts=8, residual_r=None, gamma=P, beta=P, eps=1e-5, H_r=P,
+                  Y_r=P, batch=1, seq=4096, hidden=8192, rank=0, dt=BF16)
+    assert B.tp_sp_residual_layernorm_fwd(**dict(lnargs, hidden=16392)) == 2
+    assert B.tp_sp_residual_layernorm_fwd(**dict(lnargs, gamma=None)) == 1
+    assert B.tp_sp_residual_layernorm_fwd(**dict(lnargs, eps=-1.0)) == 2
+    assert B.tp_sp_residual_layernorm_fwd(**dict(lnargs, residual_r=P + 4)) == 6
+    assert B.tp_sp_residual_layernorm_fwd(**dict(lnargs, seq=100)) == 3
+    # all-gather
+    assert B.tp_all_gather_rows(parts, 8, 1, 4095, 8192, P, BF16) == 3
+    assert B.tp_all_gather_rows(parts, 8, 1, 4096, 8192, None, BF16) == 1
+    assert B.tp_last_error() != ""
+
+
 def _attn(**kw):
     a = dict(X=P, Wqkv_i=P, bqkv_i=None, Wo_i=P, Z_i=P, batch=4, seq=2048, hidden=4096,
              n_heads=32, causal=1, n_shards=8, rank=0, dt=BF16, workspace=P,
