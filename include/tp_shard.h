@@ -196,6 +196,40 @@ tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_
                             void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Grouped-query attention shard (llms.blog, "Grouped-Query Attention (GQA) Constraints"):
+ * the attention shard above with n_kv_heads key/value heads, each read by
+ * n_heads / n_kv_heads query heads (query head j reads key/value head j / (n_heads /
+ * n_kv_heads)); n_kv_heads = n_heads is the multi-head case (tp_attn_shard_fwd is exactly
+ * that call), n_kv_heads = 1 multi-query attention.
+ * The page's constraint: n_kv_heads must be divisible by N, and then rank r holds key/value
+ * heads r*KVl ... r*KVl + KVl - 1 (KVl = n_kv_heads / N); when N exceeds n_kv_heads, N must
+ * be a multiple of it and every key/value head is duplicated on N / n_kv_heads ranks: rank r
+ * holds the single head its query heads r*Hl ... read (KVl = 1). Anything else, or n_heads
+ * not a multiple of n_kv_heads, is TP_ERR_NOT_DIVISIBLE.
+ *
+ *   Wqkv_i  [(Hl + 2*KVl)*d, hidden] bf16  rows 0..Hl*d-1 = W_Q[:, C_r]^T (the rank's query
+ *                                          heads), then W_K[:, K_r]^T and W_V[:, K_r]^T (the
+ *                                          rank's key/value heads, head-major)
+ *   bqkv_i  [(Hl + 2*KVl)*d]         bf16  matching bias slices, or NULL
+ *   Wo_i    [hidden, Hl*d]           bf16  as for tp_attn_shard_fwd
+ * Workspace: Q [batch, Hl, seq, d], K [batch, KVl, seq, d], Vt [batch, KVl, d, round8(seq)],
+ * O [batch*seq, Hl*d], at the offsets tp_gqa_attn_workspace_layout returns. Other arguments,
+ * dtype and head-width rules as for tp_attn_shard_fwd.
+ * ---------------------------------------------------------------------------------------- */
+size_t tp_gqa_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                   int n_kv_heads, int n_shards, tp_dtype dt);
+
+tp_status tp_gqa_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                       int n_kv_heads, int n_shards, tp_dtype dt, size_t* q_off,
+                                       size_t* k_off, size_t* vt_off, size_t* o_off);
+
+tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                                const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
+                                int64_t hidden, int n_heads, int n_kv_heads, int causal,
+                                int n_shards, int rank, tp_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Partial sum, the single-device stand-in for the tensor-parallel all-reduce:
  *   Z = Z_0 + Z_1 + ... + Z_{n_parts-1}       (llms.blog, Row-Parallel Linear Layer: the
  *                                              output and communication bullets)
@@ -272,7 +306,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 5
+#define TP_SHARD_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

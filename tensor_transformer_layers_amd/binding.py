@@ -30,7 +30,8 @@ STATUS_NAMES = {
 EXPORTED = (
     "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
     "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
-    "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_attn_workspace_bytes",
+    "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_gqa_attn_workspace_bytes",
+    "tp_gqa_attn_workspace_layout", "tp_gqa_attn_shard_fwd", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
     "tp_last_error", "tp_abi_version",
 )
@@ -88,6 +89,15 @@ def lib():
                                                _int, _vp]
     L.tp_all_gather_rows.restype = _int
     L.tp_all_gather_rows.argtypes = [ctypes.POINTER(_vp), _int, _i64, _i64, _i64, _vp, _int, _vp]
+    L.tp_gqa_attn_workspace_bytes.restype = _sz
+    L.tp_gqa_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int]
+    L.tp_gqa_attn_workspace_layout.restype = _int
+    L.tp_gqa_attn_workspace_layout.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int,
+                                               ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                               ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+    L.tp_gqa_attn_shard_fwd.restype = _int
+    L.tp_gqa_attn_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                        _int, _int, _int, _int, _vp, _sz, _vp]
     L.tp_attn_workspace_bytes.restype = _sz
     L.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int]
     L.tp_attn_workspace_layout.restype = _int
@@ -190,6 +200,27 @@ def tp_sp_residual_layernorm_fwd(Z_parts, n_parts, residual_r, gamma, beta, eps,
 def tp_all_gather_rows(slices, n_parts, batch, seq, hidden, X, dt, stream=None) -> int:
     return lib().tp_all_gather_rows(_ptr_array(slices), n_parts, batch, seq, hidden, _ptr(X),
                                     dt, _stream(stream))
+
+
+def tp_gqa_attn_workspace_bytes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt) -> int:
+    return lib().tp_gqa_attn_workspace_bytes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt)
+
+
+def tp_gqa_attn_workspace_layout(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt):
+    """(status, {"q": off, "k": off, "vt": off, "o": off}) byte offsets in the workspace."""
+    offs = [_sz(0) for _ in range(4)]
+    st = lib().tp_gqa_attn_workspace_layout(batch, seq, hidden, n_heads, n_kv_heads, n_shards,
+                                            dt, *[ctypes.byref(o) for o in offs])
+    return st, dict(zip(("q", "k", "vt", "o"), (o.value for o in offs)))
+
+
+def tp_gqa_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z_i, batch, seq, hidden, n_heads,
+                          n_kv_heads, causal, n_shards, rank, dt, workspace, workspace_bytes,
+                          stream=None) -> int:
+    return lib().tp_gqa_attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(bqkv_i), _ptr(Wo_i),
+                                       _ptr(Z_i), batch, seq, hidden, n_heads, n_kv_heads,
+                                       int(causal), n_shards, rank, dt, _ptr(workspace),
+                                       workspace_bytes, _stream(stream))
 
 
 def tp_attn_workspace_bytes(batch, seq, hidden, n_heads, n_shards, dt) -> int:

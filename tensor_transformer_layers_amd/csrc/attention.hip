@@ -101,12 +101,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
 
     const int64_t head_rows = (int64_t)bh * p.seq;
     const bf16* __restrict__ gQ = reinterpret_cast<const bf16*>(p.q) + head_rows * D;
+    // Key/value head of this query head (grouped-query attention shares one among
+    // Hl / KVl query heads; KVl = Hl is multi-head attention).
+    const int b_of = bh / p.heads_local;
+    const int64_t kvh = (int64_t)b_of * p.kv_heads_local +
+                        (bh - b_of * p.heads_local) / (p.heads_local / p.kv_heads_local);
     // K rows past seq and V^T columns past the buffer read as zero (range-checked loads);
     // V^T columns in [seq, ld_vt) are zeroed before this kernel runs.
-    const __amdgpu_buffer_rsrc_t rK =
-        span_rsrc(reinterpret_cast<const bf16*>(p.k) + head_rows * D, (int64_t)p.seq * D * 2);
+    const __amdgpu_buffer_rsrc_t rK = span_rsrc(
+        reinterpret_cast<const bf16*>(p.k) + kvh * p.seq * D, (int64_t)p.seq * D * 2);
     const __amdgpu_buffer_rsrc_t rV = span_rsrc(
-        reinterpret_cast<const bf16*>(p.vt) + (int64_t)bh * D * p.ld_vt, (int64_t)D * p.ld_vt * 2);
+        reinterpret_cast<const bf16*>(p.vt) + kvh * D * p.ld_vt, (int64_t)D * p.ld_vt * 2);
 
     // Q fragments stay in registers: lane holds query qw0 + 16*qb + fr, d chunk 4*ks + fg.
     bf16x8 qf[2][KS];
@@ -377,8 +382,9 @@ __global__ void zero_vt_pad_kernel(bf16* vt, int64_t rows, int seq, int64_t ld_v
 template <int D>
 hipError_t launch(const AttnProblem& p, hipStream_t s)
 {
+    if (p.kv_heads_local < 1 || p.heads_local % p.kv_heads_local != 0) return hipErrorInvalidValue;
     if (p.ld_vt > p.seq) {
-        const int64_t rows = (int64_t)p.batch * p.heads_local * D;
+        const int64_t rows = (int64_t)p.batch * p.kv_heads_local * D;
         const int64_t n = rows * (p.ld_vt - p.seq);
         hipLaunchKernelGGL(zero_vt_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            const_cast<bf16*>(reinterpret_cast<const bf16*>(p.vt)), rows, p.seq, p.ld_vt);

@@ -90,15 +90,16 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
                 float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
                 *reinterpret_cast<f32x4*>(c) = v;
             }
-        } else {  // Qkv (bf16 only)
-            const int width = p.heads_local * p.head_dim;
-            const int which = n / width;
-            const int rem = n - which * width;
+        } else {  // Qkv (bf16 only): Hl query heads, then KVl key and KVl value heads
+            const int wq = p.heads_local * p.head_dim;
+            const int wkv = p.kv_heads_local * p.head_dim;
+            const int which = n < wq ? 0 : (n < wq + wkv ? 1 : 2);
+            const int rem = n - (which == 0 ? 0 : wq + (which - 1) * wkv);
             const int head = rem / p.head_dim;
             const int j = rem - head * p.head_dim;
             const int b = m / p.seq;
             const int s = m - b * p.seq;
-            const int64_t bh = (int64_t)b * p.heads_local + head;
+            const int64_t bh = (int64_t)b * (which == 0 ? p.heads_local : p.kv_heads_local) + head;
             const bf16x4 o = to_bf16x4(v);
             if (which < 2) {
                 bf16* dst = reinterpret_cast<bf16*>(which == 0 ? p.q : p.k) +

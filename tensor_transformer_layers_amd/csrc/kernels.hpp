@@ -24,11 +24,14 @@ struct GemmProblem {
     void* C;              // [M, N] row-major, ldc (BiasGelu / F32)
     int64_t lda, ldb, ldc;
     int M, N, K;
-    // Qkv scatter: column n = which * Hl*d + head * d + j, row m = b * seq + s
+    // Qkv scatter, row m = b * seq + s: columns [0, Hl d) are the local query heads, then
+    // KVl d key columns and KVl d value columns (head-major, d per head; KVl = Hl for
+    // multi-head attention, fewer for grouped-query attention).
     void* q;              // [batch, Hl, seq, d]
-    void* k;              // [batch, Hl, seq, d]
-    void* vt;             // [batch, Hl, d, ld_vt]
+    void* k;              // [batch, KVl, seq, d]
+    void* vt;             // [batch, KVl, d, ld_vt]
     int seq, heads_local, head_dim;
+    int kv_heads_local;   // KVl
     int64_t ld_vt;
 };
 
@@ -43,10 +46,11 @@ hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t stream);
 
 struct AttnProblem {
     const void* q;        // [batch, Hl, seq, d] bf16
-    const void* k;        // [batch, Hl, seq, d] bf16
-    const void* vt;       // [batch, Hl, d, ld_vt] bf16
+    const void* k;        // [batch, KVl, seq, d] bf16
+    const void* vt;       // [batch, KVl, d, ld_vt] bf16
     void* o;              // [batch * seq, Hl * d] bf16
     int batch, heads_local, seq, head_dim;
+    int kv_heads_local;   // KVl; local query head j reads key/value head j / (Hl / KVl)
     int64_t ld_vt;
     int causal;
     float scale_log2;     // log2(e) / sqrt(d)

@@ -139,13 +139,17 @@ hipError_t launch_row(const void* X, const void* W, float* Z, int64_t rows, int6
 
 // ---- attention ---------------------------------------------------------------------------
 struct AttnLayout {
-    int hl, d;
+    int hl, kvl, d;
     int64_t ld_vt;
     size_t q, k, vt, o, total;
 };
 
-tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_heads, int n,
-                              tp_dtype dt, AttnLayout* L)
+// n_kv_heads key/value heads (= n_heads for multi-head attention). A rank holds
+// n_kv_heads / N of them when N divides n_kv_heads, else (N a multiple of n_kv_heads) one
+// head duplicated on N / n_kv_heads ranks (llms.blog, "Grouped-Query Attention (GQA)
+// Constraints").
+tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                              int n_kv_heads, int n, tp_dtype dt, AttnLayout* L)
 {
     if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports TP_BF16 only (got %d)", (int)dt);
     if (n < 1) return fail(TP_ERR_SHAPE, "n_shards %d < 1", n);
@@ -158,17 +162,25 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
                     n_heads);
     if (n_heads % n != 0)
         return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d not divisible by n_shards=%d", n_heads, n);
+    if (n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d is not a multiple of n_kv_heads=%d", n_heads,
+                    n_kv_heads);
+    if (n_kv_heads % n != 0 && n % n_kv_heads != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE,
+                    "n_kv_heads=%d neither divisible by n_shards=%d nor dividing it", n_kv_heads, n);
     const int64_t d = hidden / n_heads;
     if (d != 64 && d != 128) return fail(TP_ERR_SHAPE, "head dim %lld not supported (64 or 128)", (long long)d);
     if (hidden % 8 != 0) return fail(TP_ERR_ALIGN, "hidden=%lld must be a multiple of 8", (long long)hidden);
     L->hl = n_heads / n;
+    L->kvl = n_kv_heads % n == 0 ? n_kv_heads / n : 1;
     L->d = (int)d;
     L->ld_vt = (int64_t)round_up((size_t)seq, 8);
-    const size_t head_elems = (size_t)batch * L->hl * seq * d;
+    const size_t q_elems = (size_t)batch * L->hl * seq * d;
+    const size_t kv_elems = (size_t)batch * L->kvl * seq * d;
     L->q = 0;
-    L->k = round_up(L->q + head_elems * 2, 256);
-    L->vt = round_up(L->k + head_elems * 2, 256);
-    L->o = round_up(L->vt + (size_t)batch * L->hl * d * L->ld_vt * 2, 256);
+    L->k = round_up(L->q + q_elems * 2, 256);
+    L->vt = round_up(L->k + kv_elems * 2, 256);
+    L->o = round_up(L->vt + (size_t)batch * L->kvl * d * L->ld_vt * 2, 256);
     L->total = round_up(L->o + (size_t)batch * seq * L->hl * d * 2, 256);
     return TP_OK;
 }
@@ -326,17 +338,42 @@ tp_status tp_row_parallel_fwd(const void* X_i, const void* W_i, float* Z_i, int6
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
                                int n_shards, tp_dtype dt)
 {
-    AttnLayout L;
-    if (validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L) != TP_OK) return 0;
-    return L.total;
+    return tp_gqa_attn_workspace_bytes(batch, seq, hidden, n_heads, n_heads, n_shards, dt);
 }
 
 tp_status tp_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
                                    int n_shards, tp_dtype dt, size_t* q_off, size_t* k_off,
                                    size_t* vt_off, size_t* o_off)
 {
+    return tp_gqa_attn_workspace_layout(batch, seq, hidden, n_heads, n_heads, n_shards, dt, q_off,
+                                        k_off, vt_off, o_off);
+}
+
+tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                            const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
+                            int64_t hidden, int n_heads, int causal, int n_shards, int rank,
+                            tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return tp_gqa_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z_i, batch, seq, hidden, n_heads,
+                                 n_heads, causal, n_shards, rank, dt, workspace, workspace_bytes,
+                                 stream);
+}
+
+size_t tp_gqa_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                   int n_kv_heads, int n_shards, tp_dtype dt)
+{
     AttnLayout L;
-    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L);
+    if (validate_attn_sizes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt, &L) != TP_OK)
+        return 0;
+    return L.total;
+}
+
+tp_status tp_gqa_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                       int n_kv_heads, int n_shards, tp_dtype dt, size_t* q_off,
+                                       size_t* k_off, size_t* vt_off, size_t* o_off)
+{
+    AttnLayout L;
+    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt, &L);
     if (st != TP_OK) return st;
     if (q_off) *q_off = L.q;
     if (k_off) *k_off = L.k;
@@ -345,15 +382,16 @@ tp_status tp_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidden, i
     return ok();
 }
 
-tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
-                            const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
-                            int64_t hidden, int n_heads, int causal, int n_shards, int rank,
-                            tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                                const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
+                                int64_t hidden, int n_heads, int n_kv_heads, int causal,
+                                int n_shards, int rank, tp_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream)
 {
     if (!X || !Wqkv_i || !Wo_i || !Z_i)
         return fail(TP_ERR_NULL, "X, Wqkv_i, Wo_i and Z_i must be non-NULL");
     AttnLayout L;
-    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_shards, dt, &L);
+    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt, &L);
     if (st != TP_OK) return st;
     if (rank < 0 || rank >= n_shards)
         return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
@@ -369,22 +407,24 @@ tp_status tp_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = reinterpret_cast<char*>(workspace);
     const int T = (int)(batch * seq);
-    const int w = L.hl * L.d;   // local width h / N
+    const int w = L.hl * L.d;       // local query width
+    const int wkv = L.kvl * L.d;    // local key (and value) width
     // 1. Column-parallel QKV projection of the local heads, scattered per head (V transposed).
     tps::GemmProblem g{};
     g.A = X; g.lda = hidden;
     g.B = Wqkv_i; g.ldb = hidden;
     g.bias = bqkv_i;
-    g.M = T; g.N = 3 * w; g.K = (int)hidden;
+    g.M = T; g.N = w + 2 * wkv; g.K = (int)hidden;
     g.q = ws + L.q; g.k = ws + L.k; g.vt = ws + L.vt;
-    g.seq = (int)seq; g.heads_local = L.hl; g.head_dim = L.d; g.ld_vt = L.ld_vt;
+    g.seq = (int)seq; g.heads_local = L.hl; g.kv_heads_local = L.kvl; g.head_dim = L.d;
+    g.ld_vt = L.ld_vt;
     hipError_t e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
     if (e != hipSuccess) return hip_status(e, "QKV projection launch");
     // 2. Head-local attention; heads concatenated locally into O_i.
     tps::AttnProblem a{};
     a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;
-    a.batch = (int)batch; a.heads_local = L.hl; a.seq = (int)seq; a.head_dim = L.d;
-    a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
+    a.batch = (int)batch; a.heads_local = L.hl; a.kv_heads_local = L.kvl; a.seq = (int)seq;
+    a.head_dim = L.d; a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
     e = tps::attention_fwd(a, s);
     if (e != hipSuccess) return hip_status(e, "attention launch");

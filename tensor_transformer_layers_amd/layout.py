@@ -12,6 +12,10 @@ These helpers only slice and transpose (pure indexing, no arithmetic):
 * ``bias_shard(b, N, r)``    the column bias slice that goes with ``column_shard``.
 * ``qkv_shard(...)``         [W_Q | W_K | W_V] restricted to rank r's heads, [3 h/N, h]
                              (attention step 1: Q, K, V sliced column-wise by head).
+* ``gqa_kv_heads(...)``, ``gqa_qkv_shard(...)``, ``gqa_qkv_bias_shard(...)``
+                             grouped-query attention: rank r's query heads r H/N ... and its
+                             key/value heads (H_kv / N of them, or the one duplicated head its
+                             query heads read when N > H_kv), [(H/N + 2 KVl) d, h].
 """
 from __future__ import annotations
 
@@ -49,3 +53,34 @@ def qkv_bias_shard(bq, bk, bv, N: int, r: int):
     if bq is None:
         return None
     return np.concatenate([bias_shard(b, N, r) for b in (bq, bk, bv)])
+
+
+def gqa_kv_heads(H: int, H_kv: int, N: int, r: int) -> range:
+    """Global key/value heads held by rank r (H_kv / N contiguous heads, or one duplicated)."""
+    if H % H_kv != 0 or H % N != 0:
+        raise ValueError("heads %d / key-value heads %d / N %d do not split" % (H, H_kv, N))
+    if H_kv % N == 0:
+        n = H_kv // N
+        return range(r * n, (r + 1) * n)
+    if N % H_kv == 0:
+        g = (r * (H // N)) // (H // H_kv)
+        return range(g, g + 1)
+    raise ValueError("%d key/value heads do not split over N=%d" % (H_kv, N))
+
+
+def gqa_qkv_shard(Wq, Wk, Wv, H: int, H_kv: int, N: int, r: int) -> np.ndarray:
+    """Rows [W_Q[:, C_r]^T ; W_K[:, K_r]^T ; W_V[:, K_r]^T] of rank r (d = W_Q width / H)."""
+    d = Wq.shape[1] // H
+    kv = gqa_kv_heads(H, H_kv, N, r)
+    kc = slice(kv.start * d, kv.stop * d)
+    return np.concatenate([column_shard(Wq, N, r), np.ascontiguousarray(Wk[:, kc].T),
+                           np.ascontiguousarray(Wv[:, kc].T)], axis=0)
+
+
+def gqa_qkv_bias_shard(bq, bk, bv, H: int, H_kv: int, N: int, r: int):
+    if bq is None:
+        return None
+    d = bq.shape[0] // H
+    kv = gqa_kv_heads(H, H_kv, N, r)
+    kc = slice(kv.start * d, kv.stop * d)
+    return np.concatenate([bias_shard(bq, N, r), bk[kc], bv[kc]])

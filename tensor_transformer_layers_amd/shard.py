@@ -183,6 +183,37 @@ def attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch.Ten
     return Z, workspace
 
 
+def gqa_attn_workspace(batch: int, seq: int, hidden: int, n_heads: int, n_kv_heads: int,
+                       n_shards: int, device="cuda"):
+    nbytes = B.tp_gqa_attn_workspace_bytes(batch, seq, hidden, n_heads, n_kv_heads, n_shards,
+                                           B.TP_BF16)
+    if nbytes == 0:
+        st, _ = B.tp_gqa_attn_workspace_layout(batch, seq, hidden, n_heads, n_kv_heads, n_shards,
+                                               B.TP_BF16)
+        B.check(st)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gqa_attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch.Tensor],
+                   Wo_i: torch.Tensor, batch: int, seq: int, n_heads: int, n_kv_heads: int,
+                   n_shards: int, rank: int, causal: bool = True, Z: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Rank ``rank``'s grouped-query attention partial (see include/tp_shard.h).
+
+    Returns (Z_i fp32 [batch*seq, hidden], workspace)."""
+    _require_cuda(X, Wqkv_i, bqkv_i, Wo_i)
+    hidden = X.shape[1]
+    if Z is None:
+        Z = torch.empty(batch * seq, hidden, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = gqa_attn_workspace(batch, seq, hidden, n_heads, n_kv_heads, n_shards, X.device)
+    st = B.tp_gqa_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z, batch, seq, hidden, n_heads,
+                                 n_kv_heads, causal, n_shards, rank, _dt(X), workspace,
+                                 workspace.numel(), _stream(stream))
+    B.check(st)
+    return Z, workspace
+
+
 # ---- partial sum ------------------------------------------------------------------------------
 def sum_partials(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

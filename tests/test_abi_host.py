@@ -141,6 +141,30 @@ def test_attn_validation(kw, status):
     assert B.tp_last_error() != ""
 
 
+def test_gqa_validation_and_layout():
+    args = dict(X=P, Wqkv_i=P, bqkv_i=None, Wo_i=P, Z_i=P, batch=1, seq=4096, hidden=8192,
+                n_heads=64, n_kv_heads=8, causal=1, n_shards=8, rank=0, dt=BF16, workspace=P,
+                workspace_bytes=BIG)
+    g = lambda **kw: B.tp_gqa_attn_shard_fwd(**dict(args, **kw))
+    assert g(n_kv_heads=6) == 3        # 64 query heads are not a multiple of 6
+    assert g(n_kv_heads=12, n_heads=48, hidden=6144) == 3  # 12 % 8 != 0 and 8 % 12 != 0
+    assert g(n_kv_heads=3, n_heads=48, hidden=6144) == 3   # 3 neither divides nor is divided by 8
+    assert g(rank=8) == 4
+    assert g(dt=F32) == 5
+    assert g(workspace_bytes=1) == 7
+    # layout: Q for 8 local query heads, K and V^T for one local key/value head (64 / 8 / 8)
+    st, off = B.tp_gqa_attn_workspace_layout(1, 4096, 8192, 64, 8, 8, BF16)
+    q = 4096 * 8 * 128 * 2
+    kv = 4096 * 1 * 128 * 2
+    assert st == 0 and off == dict(q=0, k=q, vt=q + kv, o=q + 2 * kv)
+    # 4 key/value heads on 8 ranks: duplicated, still one per rank
+    st, off4 = B.tp_gqa_attn_workspace_layout(1, 4096, 8192, 64, 4, 8, BF16)
+    assert st == 0 and off4 == off
+    # H_kv = H is the multi-head layout
+    assert (B.tp_gqa_attn_workspace_bytes(4, 2048, 4096, 32, 32, 8, BF16)
+            == B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16))
+
+
 def test_sum_validation():
     assert B.tp_sum_partials([P, P], 0, 10, P, F32) == 2
     assert B.tp_sum_partials([P] * 65, 65, 10, P, F32) == 2

@@ -1,0 +1,123 @@
+"""GPU parity of tp_gqa_attn_shard_fwd (grouped-query attention shard) against the oracle.
+
+Covers key/value heads split over the ranks (N divides H_kv), duplicated on several ranks
+(N > H_kv, the page's TP = 8 with 4 key/value heads), multi-query attention (H_kv = 1) and
+the multi-head case (H_kv = H, which must give tp_attn_shard_fwd's bits). Tolerance: relative
+Frobenius error 1e-2, the oracle fed the same bf16-rounded inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import Canary, canary_tensor, dev, host, torch_cuda
+from synth import WORKLOADS, Workload, gqa_inputs, sample_rows
+from tensor_transformer_layers_amd import layout
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def run_gqa(d, batch, seq, H, H_kv, N, r, causal, bias=True):
+    """Rank r's GQA shard on the GPU; returns host fp64 (Z_i, O_i)."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import binding as B
+    from tensor_transformer_layers_amd import shard
+    h = d["X"].shape[1]
+    X = dev(d["X"], "bf16")
+    Wqkv = dev(layout.gqa_qkv_shard(d["Wq"], d["Wk"], d["Wv"], H, H_kv, N, r), "bf16")
+    bqkv = (dev(layout.gqa_qkv_bias_shard(d["bq"], d["bk"], d["bv"], H, H_kv, N, r), "bf16")
+            if bias else None)
+    Wo = dev(layout.row_shard(d["Wo"], N, r), "bf16")
+    T = batch * seq
+    Zc = canary_tensor((T, h), torch.float32)
+    nbytes = B.tp_gqa_attn_workspace_bytes(batch, seq, h, H, H_kv, N, B.TP_BF16)
+    ws = Canary(nbytes, torch.uint8, None)
+    shard.gqa_attn_shard(X, Wqkv, bqkv, Wo, batch, seq, H, H_kv, N, r, causal, Z=Zc.tensor,
+                         workspace=ws.body)
+    torch.cuda.synchronize()
+    assert Zc.intact() and ws.intact(), "write outside an output buffer"
+    st, off = B.tp_gqa_attn_workspace_layout(batch, seq, h, H, H_kv, N, B.TP_BF16)
+    assert st == 0
+    wl = (H // N) * (h // H)
+    O = ws.body[off["o"]:off["o"] + T * wl * 2].view(torch.bfloat16).view(T, wl)
+    return host(Zc.tensor), host(O)
+
+
+SMALL = [
+    # batch, seq, hidden, heads, kv heads, N, causal
+    (2, 150, 1024, 8, 2, 2, True),      # N divides H_kv: one kv head per rank, 4 q heads each
+    (1, 200, 1024, 8, 4, 2, False),
+    (2, 65, 512, 8, 4, 4, True),        # d = 64
+    (1, 130, 1024, 8, 1, 4, True),      # multi-query attention, kv head duplicated on 4 ranks
+    (1, 97, 1024, 8, 4, 8, True),       # N = 8 > 4 kv heads: each duplicated on 2 ranks
+    (2, 33, 2048, 16, 8, 4, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_gqa_small_against_oracle(case):
+    batch, seq, h, H, H_kv, N, causal = case
+    w = Workload(name="g", kind="gqa", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, kv_heads=H_kv, n_shards=N)
+    d = gqa_inputs(w, seed=seq + H_kv)
+    for r in sorted({0, N // 2, N - 1}):
+        Z, O = run_gqa(d, batch, seq, H, H_kv, N, r, causal)
+        Zo, Oo = oracle.attn_shard_gqa(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"],
+                                       d["bv"], d["Wo"], batch, seq, H, H_kv, N, r, causal,
+                                       want_heads=True)
+        eo, ez = oracle.rel_frobenius(O, Oo), oracle.rel_frobenius(Z, Zo)
+        print("%s rank %d: O err %.2e, Z err %.2e" % (case, r, eo, ez))
+        assert eo < TOL and ez < TOL
+
+
+def test_gqa_shards_sum_to_block():
+    """Duplicated key/value heads: the ranks' partials still sum to the unsharded block."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    batch, seq, h, H, H_kv = 1, 120, 1024, 8, 2
+    w = Workload(name="g", kind="gqa", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, kv_heads=H_kv, n_shards=8)
+    d = gqa_inputs(w, seed=3)
+    ref = oracle.attn_shard_gqa(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"],
+                                d["Wo"], batch, seq, H, H_kv)
+    for N in (1, 2, 8):
+        Zs = [dev(run_gqa(d, batch, seq, H, H_kv, N, r, True)[0].astype(np.float32), "f32")
+              for r in range(N)]
+        e = oracle.rel_frobenius(host(shard.sum_partials(Zs)), ref)
+        print("N=%d block err %.2e" % (N, e))
+        assert e < TOL
+
+
+def test_gqa_with_all_kv_heads_is_the_mha_call():
+    """H_kv = H through the grouped-query entry point gives tp_attn_shard_fwd's exact bits."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    batch, seq, h, H, N, r = 2, 77, 1024, 8, 2, 1
+    w = Workload(name="g", kind="gqa", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, kv_heads=H, n_shards=N)
+    d = gqa_inputs(w, seed=4)
+    Zg, _ = run_gqa(d, batch, seq, H, H, N, r, True)
+    X = dev(d["X"], "bf16")
+    Wqkv = dev(layout.qkv_shard(d["Wq"], d["Wk"], d["Wv"], N, r), "bf16")
+    bqkv = dev(layout.qkv_bias_shard(d["bq"], d["bk"], d["bv"], N, r), "bf16")
+    Wo = dev(layout.row_shard(d["Wo"], N, r), "bf16")
+    Zm, _ = shard.attn_shard(X, Wqkv, bqkv, Wo, batch, seq, H, N, r, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(Zg, host(Zm))
+
+
+@pytest.mark.parametrize("name,rank", [("gqa_shard_bf16_b1_s4096_h8192_H64_kv8_n8", 0),
+                                       ("gqa_shard_bf16_b1_s4096_h8192_H64_kv4_n8", 3)])
+def test_gqa_full_size_sampled_rows(name, rank):
+    """One rank's GQA shard at seq 4096, hidden 8192, 64 query heads, N 8, 48 sampled rows."""
+    w = WORKLOADS[name]
+    d = gqa_inputs(w)
+    Z, O = run_gqa(d, w.batch, w.seq, w.heads, w.kv_heads, w.n_shards, rank, True)
+    rows = sample_rows(w.seq, 48, seed=rank, must=[127, 128, 2048, 4095 - 64])
+    Zo, Oo = oracle.attn_shard_gqa(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"],
+                                   d["Wo"], w.batch, w.seq, w.heads, w.kv_heads, w.n_shards,
+                                   rank, True, rows=rows, want_heads=True)
+    eo, ez = oracle.rel_frobenius(O[rows], Oo), oracle.rel_frobenius(Z[rows], Zo)
+    print("%s rank %d: O err %.2e, Z err %.2e" % (name, rank, eo, ez))
+    assert eo < TOL and ez < TOL
+    assert np.isfinite(Z).all()
