@@ -133,6 +133,35 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Backward pass of the MLP shard (llms.blog, "Partitioning the MLP Block": one all-reduce in
+ * the backward pass, over the input gradients of the column-parallel layer). For the
+ * forward Z_i = GeLU(P) B_r, P = X A_r + a_r, and the upstream gradient dZ of the block
+ * output (every rank receives the same dZ, since Z is the sum of the partials):
+ *   dY = dZ B_r^T,   dP = dY * GeLU'(P),   GeLU'(x) = Phi(x) + x phi(x)
+ *   dA_r = X^T dP,   da_r = sum over tokens of dP,   dB_r = GeLU(P)^T dZ
+ *   dX_i = dP A_r^T  (rank i's input-gradient partial; the all-reduce sums them)
+ * P is recomputed from X, A_i, a_i (nothing is kept from the forward call).
+ *
+ *   X, A_i, a_i, B_i   as for tp_mlp_shard_fwd (bf16; a_i may be NULL)
+ *   dZ     [tokens, hidden]   bf16  upstream gradient
+ *   dX_i   [tokens, hidden]   fp32  input-gradient partial
+ *   dA_i   [ffn/N, hidden]    fp32  gradient of A_i in A_i's stored layout (dA_r transposed)
+ *   da_i   [ffn/N]            fp32  gradient of a_i, or NULL to skip it
+ *   dB_i   [hidden, ffn/N]    fp32  gradient of B_i in B_i's stored layout (dB_r transposed)
+ * The products run on the bf16 MFMA GEMM (fp32 accumulation); P, dP and GeLU(P) are kept
+ * in bf16 in the workspace, and the operands whose reduced dimension is not contiguous are
+ * transposed into the workspace first (tokens padded to a multiple of 8 with zeros there).
+ * dt: TP_BF16 only. hidden and ffn/N multiples of 8; tokens any value >= 1.
+ * ---------------------------------------------------------------------------------------- */
+size_t tp_mlp_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                                  tp_dtype dt);
+
+tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                           const void* dZ, float* dX_i, float* dA_i, float* da_i, float* dB_i,
+                           int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, int rank,
+                           tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Gated (SwiGLU) MLP shard:
  *   Z_i = (SiLU(X W_gate,i) * (X W_up,i)) W_down,i     (llms.blog, "Partitioning the MLP
  *                                                      Block", steps 2-3: gate and up
@@ -306,7 +335,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 6
+#define TP_SHARD_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

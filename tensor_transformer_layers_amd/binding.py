@@ -29,6 +29,7 @@ STATUS_NAMES = {
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
     "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
+    "tp_mlp_bwd_workspace_bytes", "tp_mlp_shard_bwd",
     "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
     "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_gqa_attn_workspace_bytes",
     "tp_gqa_attn_workspace_layout", "tp_gqa_attn_shard_fwd", "tp_attn_workspace_bytes",
@@ -75,6 +76,11 @@ def lib():
     L.tp_mlp_shard_fwd.restype = _int
     L.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                    _vp, _sz, _vp]
+    L.tp_mlp_bwd_workspace_bytes.restype = _sz
+    L.tp_mlp_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
+    L.tp_mlp_shard_bwd.restype = _int
+    L.tp_mlp_shard_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                   _i64, _int, _int, _int, _vp, _sz, _vp]
     L.tp_swiglu_workspace_bytes.restype = _sz
     L.tp_swiglu_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
     L.tp_swiglu_shard_fwd.restype = _int
@@ -163,6 +169,18 @@ def tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z_i, tokens, hidden, ffn, n_shards, rank,
     return lib().tp_mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(Z_i), tokens,
                                   hidden, ffn, n_shards, rank, dt, _ptr(workspace),
                                   workspace_bytes, _stream(stream))
+
+
+def tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:
+    return lib().tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards, dt)
+
+
+def tp_mlp_shard_bwd(X, A_i, a_i, B_i, dZ, dX_i, dA_i, da_i, dB_i, tokens, hidden, ffn,
+                     n_shards, rank, dt, workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_mlp_shard_bwd(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(dZ), _ptr(dX_i),
+                                  _ptr(dA_i), _ptr(da_i), _ptr(dB_i), tokens, hidden, ffn,
+                                  n_shards, rank, dt, _ptr(workspace), workspace_bytes,
+                                  _stream(stream))
 
 
 def tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:

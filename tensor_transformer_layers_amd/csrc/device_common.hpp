@@ -40,6 +40,13 @@ __device__ __forceinline__ float gelu_erf(float x)
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
+// Derivative of the exact GeLU: Phi(x) + x phi(x), phi the standard normal density.
+__device__ __forceinline__ float gelu_erf_grad(float x)
+{
+    return 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
+           x * 0.39894228040143267794f * __expf(-0.5f * x * x);
+}
+
 // D = A * B + C on a 16x16 output block with K = 32 (bf16 in, fp32 accumulate).
 // Lane l supplies A row (l & 15) and B column (l & 15), 8 consecutive K values each, and
 // receives D rows 4 * (l >> 4) + i, i = 0..3, of column (l & 15).

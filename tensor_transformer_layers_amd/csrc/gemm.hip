@@ -78,7 +78,14 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
                 v += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.bias) + n);
             }
         }
-        if constexpr (EPI == Epi::BiasGelu || EPI == Epi::Bias) {
+        if constexpr (EPI == Epi::GeluGrad) {   // dP = dY * GeLU'(P), bf16 only
+            const f32x4 pre = bf16x4_to_f32(*reinterpret_cast<const bf16x4*>(
+                reinterpret_cast<const bf16*>(p.aux) + (int64_t)m * p.ldaux + n));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= gelu_erf_grad(pre[i]);
+            bf16* c = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc + n;
+            *reinterpret_cast<bf16x4*>(c) = to_bf16x4(v);
+        } else if constexpr (EPI == Epi::BiasGelu || EPI == Epi::Bias) {
             if constexpr (EPI == Epi::BiasGelu) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
@@ -736,6 +743,7 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         case Epi::F32: TPS_LAUNCH(Epi::F32) break;
         case Epi::Qkv: TPS_LAUNCH(Epi::Qkv) break;
         case Epi::Bias: TPS_LAUNCH(Epi::Bias) break;
+        case Epi::GeluGrad: TPS_LAUNCH(Epi::GeluGrad) break;
         case Epi::SwiGlu:
             if constexpr ((BN / WN / 32) % 2 == 0) {
                 TPS_LAUNCH(Epi::SwiGlu)

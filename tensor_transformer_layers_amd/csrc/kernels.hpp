@@ -14,6 +14,7 @@ enum class Epi : int {
     Qkv = 2,        // acc + bias[n] scattered to Q / K / V^T per head, bf16
     Bias = 3,       // C = acc + bias[n]         stored in the GEMM's element type
     SwiGlu = 4,     // C = SiLU(X B^T) * (X B2^T), N output features, bf16 (gated MLP)
+    GeluGrad = 5,   // C = acc * GeLU'(aux[m, n]), bf16 (backward through the activation)
 };
 
 struct GemmProblem {
@@ -21,6 +22,8 @@ struct GemmProblem {
     const void* B;        // [N, K] row-major (weight in [out, in] layout), ldb
     const void* B2;       // SwiGlu: the up projection [N, K] (B is the gate), ldb
     const void* bias;     // [N] or nullptr
+    const void* aux;      // GeluGrad: the pre-activation P [M, N] bf16, leading dim ldaux
+    int64_t ldaux;
     void* C;              // [M, N] row-major, ldc (BiasGelu / F32)
     int64_t lda, ldb, ldc;
     int M, N, K;
@@ -77,6 +80,14 @@ hipError_t sp_boundary(const SpProblem& p, hipStream_t stream);
 // Full-sequence rows from the N slices: out[b * seq + r * seq/N + s'] = slices[r][b * seq/N + s'].
 hipError_t all_gather_rows(const void* const* slices, int n, int batch, int seq, int64_t row_bytes,
                            void* out, hipStream_t stream);
+
+// out[c][r] = f(in[r][c]) for a bf16 [rows, cols] array (f = GeLU when gelu); out has leading
+// dimension ld_out >= rows (a multiple of 8) and its columns [rows, ld_out) are zeroed.
+hipError_t transpose_bf16(const void* in, int rows, int cols, int64_t ld_in, void* out,
+                          int64_t ld_out, bool gelu, hipStream_t stream);
+// out[r] = sum_c in[r][c] (fp32) of a bf16 [rows, cols] array with leading dimension ld.
+hipError_t row_sum_bf16(const void* in, int rows, int cols, int64_t ld, float* out,
+                        hipStream_t stream);
 
 hipError_t sum_partials(const float* const* parts, int n_parts, int64_t numel, void* out,
                         bool out_bf16, hipStream_t stream);

@@ -86,6 +86,31 @@ tp_status validate_mlp_sizes(int64_t tokens, int64_t hidden, int64_t ffn, int n,
     return TP_OK;
 }
 
+// Backward workspace: P and dP [T, F/N]; B_i^T [F/N, h]; A_i^T [h, F/N]; dP^T and GeLU(P)^T
+// [F/N, T8]; X^T and dZ^T [h, T8] (T8 = tokens rounded up to 8), all bf16, 256-byte aligned.
+struct BwdLayout {
+    int64_t t8;
+    size_t p, dp, bt, at, dpt, yt, xt, dzt, total;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t h, int64_t fl)
+{
+    BwdLayout L;
+    L.t8 = (T + 7) / 8 * 8;
+    size_t o = 0;
+    auto take = [&](size_t elems) { const size_t at = o; o = round_up(o + elems * 2, 256); return at; };
+    L.p = take((size_t)T * fl);
+    L.dp = take((size_t)T * fl);
+    L.bt = take((size_t)fl * h);
+    L.at = take((size_t)h * fl);
+    L.dpt = take((size_t)fl * L.t8);
+    L.yt = take((size_t)fl * L.t8);
+    L.xt = take((size_t)h * L.t8);
+    L.dzt = take((size_t)h * L.t8);
+    L.total = o;
+    return L;
+}
+
 // ---- column / row-parallel linear layers ---------------------------------------------------
 // column: split dimension is out_features; row: split dimension is in_features.
 tp_status validate_linear(int64_t rows, int64_t in_f, int64_t out_f, int n, int rank, tp_dtype dt,
@@ -253,6 +278,73 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
     // Row-parallel: Z_i = Y_i B_i, [tokens, hidden] fp32 partial.
     e = launch_row(workspace, B_i, Z_i, tokens, ffn / n_shards, hidden, dt, s);
     return hip_status(e, "row-parallel kernel launch");
+}
+
+size_t tp_mlp_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
+                                  tp_dtype dt)
+{
+    if (dt != TP_BF16) return 0;
+    if (validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt) != TP_OK) return 0;
+    return bwd_layout(tokens, hidden, ffn / n_shards).total;
+}
+
+tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                           const void* dZ, float* dX_i, float* dA_i, float* da_i, float* dB_i,
+                           int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, int rank,
+                           tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!X || !A_i || !B_i || !dZ || !dX_i || !dA_i || !dB_i)
+        return fail(TP_ERR_NULL, "X, A_i, B_i, dZ, dX_i, dA_i and dB_i must be non-NULL");
+    if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "the MLP backward supports TP_BF16 only (got %d)", (int)dt);
+    tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(dZ) ||
+        !aligned16(dX_i) || !aligned16(dA_i) || !aligned16(dB_i) || (a_i && !aligned16(a_i)) ||
+        (da_i && !aligned16(da_i)) || (workspace && !aligned16(workspace)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const int64_t T = tokens, h = hidden, fl = ffn / n_shards;
+    const BwdLayout L = bwd_layout(T, h, fl);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    st = check_device();
+    if (st != TP_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = reinterpret_cast<char*>(workspace);
+    hipError_t e;
+#define TPS_TRY(call, what) \
+    do { e = (call); if (e != hipSuccess) return hip_status(e, what); } while (0)
+    // 1. P = X A_r + a_r, recomputed, [T, F/N] bf16
+    TPS_TRY(launch_column(X, A_i, a_i, ws + L.p, T, h, fl, TP_ACT_NONE, dt, s), "P = X A + a");
+    // 2. dP = (dZ B_r^T) * GeLU'(P): B_r = B_i^T is [F/N, h], contiguous along h
+    TPS_TRY(tps::transpose_bf16(B_i, (int)h, (int)fl, fl, ws + L.bt, h, false, s), "B transpose");
+    {
+        tps::GemmProblem g{};
+        g.A = dZ; g.lda = h;
+        g.B = ws + L.bt; g.ldb = h;
+        g.aux = ws + L.p; g.ldaux = fl;
+        g.C = ws + L.dp; g.ldc = fl;
+        g.M = (int)T; g.N = (int)fl; g.K = (int)h;
+        TPS_TRY(tps::gemm_bf16(g, tps::Epi::GeluGrad, s), "dP = dZ B^T * GeLU'(P)");
+    }
+    // 3. dX_i = dP A_r^T: A_r = A_i^T is [h, F/N], contiguous along F/N
+    TPS_TRY(tps::transpose_bf16(A_i, (int)fl, (int)h, h, ws + L.at, fl, false, s), "A transpose");
+    TPS_TRY(launch_row(ws + L.dp, ws + L.at, dX_i, T, fl, h, dt, s), "dX = dP A^T");
+    // 4. dP^T [F/N, T8]; da_r = its row sums; dA_i = dP^T X, reduced over tokens
+    TPS_TRY(tps::transpose_bf16(ws + L.dp, (int)T, (int)fl, fl, ws + L.dpt, L.t8, false, s),
+            "dP transpose");
+    if (da_i) TPS_TRY(tps::row_sum_bf16(ws + L.dpt, (int)fl, (int)T, L.t8, da_i, s), "da = sum dP");
+    TPS_TRY(tps::transpose_bf16(X, (int)T, (int)h, h, ws + L.xt, L.t8, false, s), "X transpose");
+    TPS_TRY(launch_row(ws + L.dpt, ws + L.xt, dA_i, fl, L.t8, h, dt, s), "dA = dP^T X");
+    // 5. dB_i = dZ^T GeLU(P), reduced over tokens: GeLU(P)^T [F/N, T8], dZ^T [h, T8]
+    TPS_TRY(tps::transpose_bf16(ws + L.p, (int)T, (int)fl, fl, ws + L.yt, L.t8, true, s),
+            "GeLU(P) transpose");
+    TPS_TRY(tps::transpose_bf16(dZ, (int)T, (int)h, h, ws + L.dzt, L.t8, false, s), "dZ transpose");
+    TPS_TRY(launch_row(ws + L.dzt, ws + L.yt, dB_i, h, L.t8, fl, dt, s), "dB = dZ^T Y");
+#undef TPS_TRY
+    return ok();
 }
 
 size_t tp_swiglu_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,

@@ -106,6 +106,39 @@ def mlp_shard(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor], B
     return Z, workspace
 
 
+def mlp_bwd_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, device="cuda"):
+    nbytes = B.tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards, B.TP_BF16)
+    if nbytes == 0:
+        raise B.TPError(B.TP_ERR_SHAPE, "invalid MLP backward sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mlp_shard_backward(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor],
+                       B_i: torch.Tensor, dZ: torch.Tensor, n_shards: int, rank: int,
+                       out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Gradients of rank ``rank``'s MLP partial for the upstream dZ (bf16).
+
+    Returns ({"dX": [T, h], "dA": [F/N, h], "da": [F/N], "dB": [h, F/N]} fp32, in the stored
+    layouts of X, A_i, a_i, B_i; workspace). dX is the rank's input-gradient partial."""
+    _require_cuda(X, A_i, a_i, B_i, dZ)
+    tokens, hidden = X.shape
+    fl = A_i.shape[0]
+    ffn = fl * n_shards
+    f32 = dict(dtype=torch.float32, device=X.device)
+    if out is None:
+        out = {"dX": torch.empty(tokens, hidden, **f32), "dA": torch.empty(fl, hidden, **f32),
+               "da": torch.empty(fl, **f32) if a_i is not None else None,
+               "dB": torch.empty(hidden, fl, **f32)}
+    if workspace is None:
+        workspace = mlp_bwd_workspace(tokens, hidden, ffn, n_shards, X.device)
+    st = B.tp_mlp_shard_bwd(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"), out["dB"],
+                            tokens, hidden, ffn, n_shards, rank, _dt(X), workspace,
+                            workspace.numel(), _stream(stream))
+    B.check(st)
+    return out, workspace
+
+
 # ---- gated (SwiGLU) MLP ----------------------------------------------------------------------
 def swiglu_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, device="cuda"):
     nbytes = B.tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards, B.TP_BF16)

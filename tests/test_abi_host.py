@@ -141,6 +141,25 @@ def test_attn_validation(kw, status):
     assert B.tp_last_error() != ""
 
 
+def test_mlp_bwd_validation_and_workspace():
+    args = dict(X=P, A_i=P, a_i=None, B_i=P, dZ=P, dX_i=P, dA_i=P, da_i=None, dB_i=P, tokens=4096,
+                hidden=8192, ffn=32768, n_shards=8, rank=0, dt=BF16, workspace=P, workspace_bytes=BIG)
+    g = lambda **kw: B.tp_mlp_shard_bwd(**dict(args, **kw))
+    assert g(dZ=None) == 1 and g(dB_i=None) == 1
+    assert g(dt=F32) == 5
+    assert g(n_shards=3) == 3
+    assert g(rank=9) == 4
+    assert g(da_i=P + 4) == 6
+    assert g(workspace_bytes=1024) == 7
+    # P, dP [T, F/N]; B^T [F/N, h]; A^T [h, F/N]; dP^T, GeLU(P)^T [F/N, T8]; X^T, dZ^T [h, T8]
+    T, h, fl = 4096, 8192, 4096
+    want = 2 * (2 * T * fl + 2 * fl * h + 2 * fl * T + 2 * h * T)
+    assert B.tp_mlp_bwd_workspace_bytes(T, h, 32768, 8, BF16) == want
+    # tokens are padded to a multiple of 8 in the transposed buffers
+    assert B.tp_mlp_bwd_workspace_bytes(5, 8, 16, 1, BF16) > 0
+    assert B.tp_mlp_bwd_workspace_bytes(5, 8, 16, 1, F32) == 0
+
+
 def test_gqa_validation_and_layout():
     args = dict(X=P, Wqkv_i=P, bqkv_i=None, Wo_i=P, Z_i=P, batch=1, seq=4096, hidden=8192,
                 n_heads=64, n_kv_heads=8, causal=1, n_shards=8, rank=0, dt=BF16, workspace=P,
