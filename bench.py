@@ -121,6 +121,113 @@ def cpu_baseline(w, d, rows_n: int):
     }
 
 
+def _time_events(fn, reps: int, warmup: int, stream) -> float:
+    """Average microseconds per call of fn(), HIP events on ``stream`` around ``reps`` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
+    """Throughput of the paths next to the core shard, each on its named workload.
+
+    Inputs are drawn on the device from a seeded generator with the workload's shapes and
+    distributions (activations N(0, 1), weights N(0, 0.02), bf16): only the rank's own shard
+    is drawn, the full weights are never needed for timing.
+    """
+    import torch
+    from synth import WORKLOADS
+    from tensor_transformer_layers_amd import shard
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def rnd(*shape, std=1.0, dtype=torch.bfloat16):
+        return (torch.randn(*shape, device="cuda", generator=g) * std).to(dtype)
+
+    out = {}
+    # gated MLP shard
+    w = WORKLOADS["swiglu_shard_bf16_t4096_h8192_f28672_n8"]
+    T, h, fl = w.tokens, w.hidden, w.ffn // w.n_shards
+    X, Wg, Wu, Wd = rnd(T, h), rnd(fl, h, std=0.02), rnd(fl, h, std=0.02), rnd(h, fl, std=0.02)
+    Z = torch.empty(T, h, device="cuda")
+    ws = shard.swiglu_workspace(T, h, w.ffn, w.n_shards)
+    us = _time_events(lambda: shard.swiglu_shard(X, Wg, Wu, Wd, w.n_shards, 0, Z=Z, workspace=ws),
+                      reps, warmup, stream)
+    fl_ = 2.0 * T * h * 2 * fl + 2.0 * T * fl * h
+    out["swiglu_shard"] = {"workload": w.name, "us": us, "tflops": fl_ / us / 1e6,
+                           "frac_bf16_peak": fl_ / us / 1e6 / PEAK_BF16_TFLOPS}
+    del X, Wg, Wu, Wd, Z, ws
+    # grouped-query attention shards
+    for name in ("gqa_shard_bf16_b1_s4096_h8192_H64_kv8_n8", "gqa_shard_bf16_b1_s4096_h8192_H64_kv4_n8"):
+        w = WORKLOADS[name]
+        b, sq, h, H, Hkv, N = w.batch, w.seq, w.hidden, w.heads, w.kv_heads, w.n_shards
+        d = h // H
+        hl, kvl = H // N, (Hkv // N if Hkv % N == 0 else 1)
+        T = b * sq
+        X = rnd(T, h)
+        Wqkv, bqkv = rnd((hl + 2 * kvl) * d, h, std=0.02), rnd((hl + 2 * kvl) * d, std=0.02)
+        Wo = rnd(h, hl * d, std=0.02)
+        Z = torch.empty(T, h, device="cuda")
+        ws = shard.gqa_attn_workspace(b, sq, h, H, Hkv, N)
+        us = _time_events(lambda: shard.gqa_attn_shard(X, Wqkv, bqkv, Wo, b, sq, H, Hkv, N, 0,
+                                                       True, Z=Z, workspace=ws),
+                          reps, warmup, stream)
+        fl_ = (2.0 * T * h * (hl + 2 * kvl) * d + 4.0 * d * (sq * (sq + 1) // 2) * hl * b
+               + 2.0 * T * hl * d * h)
+        out[name.split("_bf16")[0] + "_kv%d" % Hkv] = {
+            "workload": name, "us": us, "tflops": fl_ / us / 1e6,
+            "frac_bf16_peak": fl_ / us / 1e6 / PEAK_BF16_TFLOPS}
+        del X, Wqkv, bqkv, Wo, Z, ws
+    # sequence-parallel boundary (reduce-scatter + residual + LayerNorm) and all-gather
+    w = WORKLOADS["sp_boundary_bf16_b1_s4096_h8192_n8"]
+    b, sq, h, N = w.batch, w.seq, w.hidden, w.n_shards
+    T, rows = b * sq, b * sq // N
+    parts = [torch.randn(T, h, device="cuda", generator=g) for _ in range(N)]
+    resid = rnd(rows, h)
+    gamma = 1.0 + 0.1 * torch.randn(h, device="cuda", generator=g)
+    beta = 0.1 * torch.randn(h, device="cuda", generator=g)
+    H_, Y_ = torch.empty(rows, h, device="cuda", dtype=torch.bfloat16), torch.empty_like(resid)
+    us = _time_events(lambda: shard.sp_residual_layernorm(parts, resid, gamma, beta, b, sq, 0,
+                                                          H=H_, Y=Y_), reps, warmup, stream)
+    nbytes = N * rows * h * 4 + rows * h * 2 * 3 + 2 * h * 4
+    out["sp_residual_layernorm"] = {"workload": w.name, "us": us, "gbs": nbytes / us / 1e3,
+                                    "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS}
+    slices = [rnd(rows, h) for _ in range(N)]
+    full = torch.empty(T, h, device="cuda", dtype=torch.bfloat16)
+    us = _time_events(lambda: shard.all_gather_rows(slices, b, sq, out=full), reps, warmup, stream)
+    nbytes = 2 * T * h * 2
+    out["all_gather_rows"] = {"workload": w.name, "us": us, "gbs": nbytes / us / 1e3,
+                              "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS}
+    del parts, resid, H_, Y_, slices, full
+    # backward pass of the MLP shard
+    w = WORKLOADS["mlp_bwd_bf16_t4096_h8192_f32768_n8"]
+    T, h, fl, N = w.tokens, w.hidden, w.ffn // w.n_shards, w.n_shards
+    X, A_i, a_i, B_i, dZ = rnd(T, h), rnd(fl, h, std=0.02), rnd(fl, std=0.02), rnd(h, fl, std=0.02), rnd(T, h)
+    grads = {"dX": torch.empty(T, h, device="cuda"), "dA": torch.empty(fl, h, device="cuda"),
+             "da": torch.empty(fl, device="cuda"), "dB": torch.empty(h, fl, device="cuda")}
+    ws = shard.mlp_bwd_workspace(T, h, w.ffn, N)
+    us = _time_events(lambda: shard.mlp_shard_backward(X, A_i, a_i, B_i, dZ, N, 0, out=grads,
+                                                       workspace=ws), reps, warmup, stream)
+    fl_ = 4 * 2.0 * T * h * fl   # dY, dX, dA, dB (the recomputed P is not counted)
+    out["mlp_shard_backward"] = {"workload": w.name, "us": us, "tflops": fl_ / us / 1e6,
+                                 "frac_bf16_peak": fl_ / us / 1e6 / PEAK_BF16_TFLOPS,
+                                 "note": "algorithmic FLOPs of the four gradient products; the "
+                                         "call also recomputes P (one more GEMM) and transposes "
+                                         "six operands"}
+    del X, A_i, a_i, B_i, dZ, grads, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +238,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows in the CPU-oracle sample (default: the whole shard)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the timings of the gated MLP, GQA, sequence-parallel and "
+                         "backward paths")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs every tensor-parallel shard on a "
@@ -270,8 +380,12 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    del ranks, za_other, zm_other, drv
+    torch.cuda.empty_cache()
+    if not args.no_next_rows:
+        log("timing the paths next to the core shard")
+        line["next_rows"] = measure_next_rows()
     if not args.no_cpu_baseline:
-        del ranks, za_other, zm_other
         log("timing the CPU oracle on a %d-row sample" % args.cpu_rows)
         line["cpu_baseline"] = cpu_baseline(w, d, args.cpu_rows)
     print(json.dumps(line), flush=True)
