@@ -69,8 +69,10 @@ def stage_flops(w):
     }
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+def traffic_for(kernel: str, stage: str):
+    """HBM bytes per launch of ``kernel`` in ``stage`` from the committed counter summary
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration),
+    or None when the summary was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -78,10 +80,10 @@ def traffic_for(kernel: str):
         rec = json.load(f)
     if rec.get("source_sha") != kernel_source_sha():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("hbm_bytes_per_launch")
+    for name, k in rec.get("kernels", {}).items():
+        if name.split(" [")[0] == kernel and k.get("stage") == stage:
+            return k.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, d, rows_n: int):
@@ -241,7 +243,20 @@ def main() -> int:
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the timings of the gated MLP, GQA, sequence-parallel and "
                          "backward paths")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (the reference transfer "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(64 << 20, device="cuda", dtype=torch.float32)   # 256 MiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 5 x 256 MiB")
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs every tensor-parallel shard on a "
               "single device (the all-reduce is an on-device sum), so --gpus must be 1.",
@@ -360,7 +375,7 @@ def main() -> int:
     achieved = fl[dom] / (stage_us[dom] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": traffic_for(kname)}
+                "traffic": traffic_for(kname, dom)}
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
