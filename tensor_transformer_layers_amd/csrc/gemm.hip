@@ -300,25 +300,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     const uint32_t stepB = (uint32_t)(8 * NW * p.ldb) * 2u;
     typedef __attribute__((address_space(3))) void* lds_ptr;
 
+    // fetch_vw(vw, ...) issues the slab loads of wave slot vw (8-row groups vw, vw + NW, ...).
     // fetch(k0 >= K) moves no memory (every offset is out of range) and zero-fills the
     // buffer: the loop issues it unconditionally so that the loads stay in the same basic
     // block as the MFMAs they are scheduled between.
-    auto fetch = [&](int k0, int buf) {
+    auto fetch_vw = [&](int vw, int k0, int buf) {
         const bool kin = k0 + lchunk * 8 < p.K;
         const uint32_t kb = (uint32_t)k0 * 2u;
-        bf16* sA = smem + buf * (BM + BN) * BK + wave * 8 * BK;
-        bf16* sB = smem + buf * (BM + BN) * BK + BM * BK + wave * 8 * BK;
+        const uint32_t dA = (uint32_t)((vw - wave) * 8 * p.lda) * 2u;
+        const uint32_t dB = (uint32_t)((vw - wave) * 8 * p.ldb) * 2u;
+        bf16* sA = smem + buf * (BM + BN) * BK + vw * 8 * BK;
+        bf16* sB = smem + buf * (BM + BN) * BK + BM * BK + vw * 8 * BK;
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rA, (lds_ptr)(sA + i * 8 * NW * BK), 16,
-                kin ? offA + i * stepA + kb : kOutOfRange, 0, 0, 0);
+                kin ? offA + dA + i * stepA + kb : kOutOfRange, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < BCH; ++i) {
             if constexpr (GLU) {
-                // LDS row group gi = wave + i NW lies in 32-row block gi / 4: even blocks hold
+                // LDS row group gi = vw + i NW lies in 32-row block gi / 4: even blocks hold
                 // gate rows, odd ones the up rows of the same features.
-                const int gi = wave_u + i * NW;
+                const int gi = vw + i * NW;
                 const int blk = gi >> 2;
                 const uint32_t off =
                     (uint32_t)((((blk >> 1) * 32 + (gi & 3) * 8 + grp_row) * p.ldb + lchunk * 8) * 2);
@@ -328,8 +331,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             } else {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rB, (lds_ptr)(sB + i * 8 * NW * BK), 16,
-                    kin ? offB + i * stepB + kb : kOutOfRange, 0, 0, 0);
+                    kin ? offB + dB + i * stepB + kb : kOutOfRange, 0, 0, 0);
             }
+        }
+    };
+    // With 8 waves, the waves of the first half (one per SIMD) issue the slab loads of both
+    // halves and the other four issue none: a wave whose load cannot enter the full address
+    // queue stalls its own later instructions, so keeping loads out of half of the waves
+    // leaves each SIMD one wave that never waits on the queue. Wave slots w and w + NW/2 have
+    // the same parity, so they share the lane's swizzled chunk.
+    constexpr bool SPLIT_LOADS = NW == 8;
+    auto fetch = [&](int k0, int buf, auto loader) {
+        if constexpr (!SPLIT_LOADS) {
+            fetch_vw(wave_u, k0, buf);
+        } else if constexpr (decltype(loader)::value) {
+            fetch_vw(wave_u, k0, buf);
+            fetch_vw(wave_u + NW / 2, k0, buf);
         }
     };
 
@@ -376,37 +393,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     // a burst of memory instructions to issue; sched_barrier(0) fences the phases.
     constexpr int NM = FM * FN;          // MFMAs per K-step
     constexpr int NR = FM + FN;          // fragment reads per K-step
-    constexpr int NV = ACH + BCH;        // slab load instructions per wave
-    auto interleave = [&](auto loads) {
-        InterleaveGroups<0, NM, NR, decltype(loads)::value ? NV : 0>::emit();
-    };
+    constexpr int NV = ACH + BCH;        // slab load instructions per wave slot
     bf16x8 fa[2][FM], fb[2][FN];
     const int KT = (p.K + BK - 1) / BK;
-    fetch(0, 0);
-    __syncthreads();
-    read_frags(0, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        fetch((kt + 1) * BK, cur ^ 1);
-        read_frags(cur, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        interleave(std::true_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(cur, 2, fa[0], fb[0]);
-        mma(fa[1], fb[1]);
-        interleave(std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(cur, 3, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        interleave(std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
+    // The K loop, instantiated for waves that load (loader) and waves that do not.
+    auto k_loop = [&](auto loader) {
+        constexpr int NVW = !SPLIT_LOADS ? NV : (decltype(loader)::value ? 2 * NV : 0);
+        fetch(0, 0, loader);
         __syncthreads();
-        read_frags(cur ^ 1, 0, fa[0], fb[0]);   // after the last slab: reads zeros, unused
-        mma(fa[1], fb[1]);
-        interleave(std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            fetch((kt + 1) * BK, cur ^ 1, loader);
+            read_frags(cur, 1, fa[1], fb[1]);
+            mma(fa[0], fb[0]);
+            InterleaveGroups<0, NM, NR, NVW>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 2, fa[0], fb[0]);
+            mma(fa[1], fb[1]);
+            InterleaveGroups<0, NM, NR, 0>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 3, fa[1], fb[1]);
+            mma(fa[0], fb[0]);
+            InterleaveGroups<0, NM, NR, 0>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            read_frags(cur ^ 1, 0, fa[0], fb[0]);   // after the last slab: reads zeros, unused
+            mma(fa[1], fb[1]);
+            InterleaveGroups<0, NM, NR, 0>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (!SPLIT_LOADS || wave_u < NW / 2)
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
 
     if constexpr (GLU) {
         f32x16 gacc[FN / 2][FM];
