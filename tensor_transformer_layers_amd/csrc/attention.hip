@@ -29,6 +29,7 @@
 // tiles that cross a wave's diagonal or the end of the sequence; the scale is folded into the
 // exponent's FMA; the output is rescaled only when some running maximum grew. Queries are
 // dispatched longest-first (highest query tile first) to shorten the causal tail.
+#include <cstdlib>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -92,10 +93,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     auto vswz = [](int row) { return (row >> 1) & 7; };
 
     // Longest-first: block 0 takes the last query tile of every (sequence, head) first.
+    // (sequence, head) varies fastest, then the key-range half: consecutive blocks go to the
+    // 8 XCDs in turn, so with 8 | batch * heads every block of one head (both halves of its
+    // query tiles included) runs on one XCD and that head's K and V^T stay in one L2.
+    const int halves = p.kv_split;
     const int n_qt = (p.seq + BQ - 1) / BQ;
     const int n_bh = p.batch * p.heads_local;
-    const int qt = n_qt - 1 - (int)(blockIdx.x / n_bh);
-    const int bh = (int)(blockIdx.x % n_bh);
+    const int qt = n_qt - 1 - (int)(blockIdx.x / (n_bh * halves));
+    const int rem_b = (int)(blockIdx.x % (n_bh * halves));
+    const int half = rem_b / n_bh;
+    const int bh = rem_b - half * n_bh;
     const int q0 = qt * BQ;
     const int qw0 = q0 + wave * QPW;      // this wave's first query
 
@@ -127,6 +134,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
 
     const int kv_end = CAUSAL ? min(p.seq, q0 + BQ) : p.seq;
     const int n_kv = (kv_end + BKV - 1) / BKV;
+    // this workgroup's key tiles [t_lo, t_hi): all of them, or one half
+    const int n_first = (n_kv + halves - 1) / halves;
+    const int t_lo = half == 0 ? 0 : n_first;
+    const int t_hi = half == 0 ? n_first : n_kv;
 
     // Tiles go from global memory straight into LDS: a 1 KB load instruction writes lane l's
     // 16 bytes at byte 16 l of its destination, so the lane fetches the logical chunk that the
@@ -273,23 +284,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
         }
     };
     // A tile is needed by a wave unless all the wave's queries precede it (causal).
-    auto needed = [&](int t) { return t < n_kv && (!CAUSAL || t * BKV <= qw0 + QPW - 1); };
+    auto needed = [&](int t) { return t < t_hi && (!CAUSAL || t * BKV <= qw0 + QPW - 1); };
 
-    // Set s takes key tiles s, s + 2, s + 4, ...: in iteration it both sets score, weight and
-    // accumulate one tile each (2 it + s) from their own double-buffered LDS ring, loading the
-    // tile after next meanwhile; the iterations end in the shared workgroup barrier, set 1
-    // idling in the last one when n_kv is odd. (Rotating set 1's phases against set 0's so
-    // that one set's exponentials meet the other's matrix products measured slower.)
-    const int n_it = (n_kv + 1) / 2;
-    if (set < n_kv) {
-        fetchK(set * BKV, 0);
-        fetchV(set * BKV, 0);
+    // Set s takes key tiles t_lo + s, t_lo + s + 2, ...: in iteration it both sets score,
+    // weight and accumulate one tile each (t_lo + 2 it + s) from their own double-buffered LDS
+    // ring, loading the tile after next meanwhile; the iterations end in the shared workgroup
+    // barrier, set 1 idling in the last one when the range is odd. (Rotating set 1's phases
+    // against set 0's so that one set's exponentials meet the other's matrix products
+    // measured slower.)
+    const int n_it = (t_hi - t_lo + 1) / 2;
+    if (t_lo + set < t_hi) {
+        fetchK((t_lo + set) * BKV, 0);
+        fetchV((t_lo + set) * BKV, 0);
     }
     __syncthreads();
 
     auto window = [&](int it, auto masked_c) {
-        const int cur = it & 1, t = 2 * it + set, k0 = t * BKV;
-        if (t + 2 < n_kv) {
+        const int cur = it & 1, t = t_lo + 2 * it + set, k0 = t * BKV;
+        if (t + 2 < t_hi) {
             fetchK(k0 + 2 * BKV, cur ^ 1);
             fetchV(k0 + 2 * BKV, cur ^ 1);
         }
@@ -305,8 +317,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     };
     // Windows whose two tiles lie inside the sequence and wholly before the workgroup's first
     // query (causal) need no mask; the rest (the diagonal, a ragged end) do.
-    const int full_tiles = min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV);
-    const int n_full_it = min(full_tiles / 2, n_it);
+    // (Both tiles of such a window must also lie in this workgroup's range [t_lo, t_hi).)
+    const int full_tiles = min(min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV), t_hi);
+    const int n_full_it = min(max(full_tiles - t_lo, 0) / 2, n_it);
     int it = 0;
     for (; it < n_full_it; ++it) window(it, std::false_type{});
     for (; it < n_it; ++it) window(it, std::true_type{});
@@ -340,31 +353,87 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     __syncthreads();
     if (set == 1) return;
 
-    // ---- normalise and store O[token][head*D + d], 4 consecutive d per lane
+    // ---- combine; then normalise and store O[token][head*D + d] (4 consecutive d per lane),
+    // or, with the key-range split, store this half's unnormalised output, max and denominator.
+    // A side that saw no key of a query (its maximum is still -inf) carries weight 0; when
+    // the whole range is split, one half may hold no visible key for a query at all.
     const int b = bh / p.heads_local;
     const int head = bh - b * p.heads_local;
     const int64_t ldo = (int64_t)p.heads_local * D;
     bf16* __restrict__ gO = reinterpret_cast<bf16*>(p.o);
+    const int64_t item = ((int64_t)bh * n_qt + qt) * halves + half;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float m1 = xch[(NF - 4 + qb) * 64];
         const float l1 = xch[(NF - 2 + qb) * 64];
         const float m0 = m_run[qb];
         const float m = fmaxf(m0, m1);
-        // set 0 always holds key 0, which every query sees, so m0 and m are finite
-        const float a0 = __builtin_amdgcn_exp2f((m0 - m) * sl2);
+        const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * sl2);
         const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * sl2);
-        const float inv = 1.0f / (lq[qb] * a0 + l1 * a1);
+        const float l = lq[qb] * a0 + l1 * a1;
         const int q = qw0 + qb * 16 + fr;
         if (q >= p.seq) continue;
-        bf16* dst = gO + ((int64_t)b * p.seq + q) * ldo + head * D + 4 * fg;
+        if (halves == 1) {
+            const float inv = 1.0f / l;
+            bf16* dst = gO + ((int64_t)b * p.seq + q) * ldo + head * D + 4 * fg;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            f32x4 o1;
+            for (int db = 0; db < DB; ++db) {
+                f32x4 o1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
-            *reinterpret_cast<bf16x4*>(dst + db * 16) = to_bf16x4((acc[db][qb] * a0 + o1 * a1) * inv);
+                for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
+                *reinterpret_cast<bf16x4*>(dst + db * 16) = to_bf16x4((acc[db][qb] * a0 + o1 * a1) * inv);
+            }
+        } else {
+            const int r = q - q0;
+            float* po = p.part_o + (item * BQ + r) * D + 4 * fg;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                f32x4 o1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
+                *reinterpret_cast<f32x4*>(po + db * 16) = acc[db][qb] * a0 + o1 * a1;
+            }
+            if (fg == 0) {
+                float* pm = p.part_ml + (item * BQ + r) * 2;
+                pm[0] = m;
+                pm[1] = l;
+            }
         }
+    }
+}
+
+// Merge of the two key-range halves of every query tile: with m = max(m_0, m_1) and
+// a_h = exp((m_h - m) scale) (0 for a half that saw no key), O = (O_0 a_0 + O_1 a_1) /
+// (l_0 a_0 + l_1 a_1), the same rescaling as the online softmax. One workgroup per 16 rows
+// of a (sequence, head, query tile); lanes take 4-wide vectors of those rows.
+constexpr int kMergeRows = 16;
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnProblem p)
+{
+    constexpr int RB = BQ / kMergeRows;
+    const int n_qt = (p.seq + BQ - 1) / BQ;
+    const int tile = blockIdx.x / RB, rb = blockIdx.x - tile * RB;
+    const int bh = tile / n_qt, qt = tile - bh * n_qt;
+    const int q0 = qt * BQ, r0 = rb * kMergeRows;
+    const int rows = min(kMergeRows, p.seq - q0 - r0);
+    if (rows <= 0) return;
+    const int b = bh / p.heads_local, head = bh - b * p.heads_local;
+    const int64_t item0 = ((int64_t)bh * n_qt + qt) * 2;
+    const float sl2 = p.scale_log2;
+    const int64_t ldo = (int64_t)p.heads_local * D;
+    bf16* __restrict__ gO = reinterpret_cast<bf16*>(p.o);
+    for (int e = threadIdx.x; e < rows * (D / 4); e += 256) {
+        const int r = r0 + e / (D / 4), c4 = e % (D / 4);
+        const float2 ml0 = *reinterpret_cast<const float2*>(p.part_ml + (item0 * BQ + r) * 2);
+        const float2 ml1 = *reinterpret_cast<const float2*>(p.part_ml + ((item0 + 1) * BQ + r) * 2);
+        const float m = fmaxf(ml0.x, ml1.x);
+        const float a0 = ml0.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml0.x - m) * sl2);
+        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml1.x - m) * sl2);
+        const float inv = 1.0f / (ml0.y * a0 + ml1.y * a1);
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(p.part_o + (item0 * BQ + r) * D + 4 * c4);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(p.part_o + ((item0 + 1) * BQ + r) * D + 4 * c4);
+        *reinterpret_cast<bf16x4*>(gO + ((int64_t)b * p.seq + q0 + r) * ldo + head * D + 4 * c4) =
+            to_bf16x4((o0 * a0 + o1 * a1) * inv);
     }
 }
 
@@ -389,16 +458,51 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
         hipLaunchKernelGGL(zero_vt_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            const_cast<bf16*>(reinterpret_cast<const bf16*>(p.vt)), rows, p.seq, p.ld_vt);
     }
+    if (p.kv_split != 1 && (p.kv_split != 2 || !p.part_o || !p.part_ml)) return hipErrorInvalidValue;
     const int n_qt = (p.seq + BQ - 1) / BQ;
-    dim3 grid((unsigned)(n_qt * p.batch * p.heads_local)), block(kThreads);
+    const int n_tiles = n_qt * p.batch * p.heads_local;
+    dim3 grid((unsigned)(n_tiles * p.kv_split)), block(kThreads);
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, block, 0, s, p);
+    if (p.kv_split == 2)
+        hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)(n_tiles * (BQ / kMergeRows))),
+                           dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+// The key-range split pays when the query tiles alone give fewer than two workgroups per
+// compute unit (256 on MI355X) and the causal tail is long: the longest query tiles then run
+// alone for a large share of the kernel. Measured at 256 query tiles: with 32 query tiles per
+// sequence (4096 tokens) the split plus the merge takes 74 us against 88 us unsplit; with 16
+// (2048 tokens) 48 us against 45 us, the merge costing more than the shorter tail saves. The
+// default is therefore: causal, under 512 query tiles, and at least 32 query tiles per
+// sequence. The partials are reserved whenever there are under 512 query tiles (the workspace
+// size depends on the shapes only, not on the mask). TPSHARD_ATTN_SPLIT (read at launch) is a
+// test knob: 0 turns the split off, 2 forces it wherever the partials are reserved.
+size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim, bool causal,
+                               int* kv_split)
+{
+    const int n_qt = (seq + BQ - 1) / BQ;
+    const int64_t n_tiles = (int64_t)n_qt * batch * heads_local;
+    const int split = n_tiles < 2 * 256 ? 2 : 1;
+    if (kv_split) {
+        const char* e = std::getenv("TPSHARD_ATTN_SPLIT");
+        const int force = e ? std::atoi(e) : -1;
+        if (force == 0)
+            *kv_split = 1;
+        else if (force == 2)
+            *kv_split = split;
+        else
+            *kv_split = causal && n_qt >= 32 ? split : 1;
+    }
+    if (split == 1) return 0;
+    // two halves per query tile: output [128][d] and (max, denominator) [128][2], fp32
+    return (size_t)n_tiles * 2 * BQ * ((size_t)head_dim + 2) * sizeof(float);
+}
 
 hipError_t attention_fwd(const AttnProblem& p, hipStream_t s)
 {

@@ -57,7 +57,16 @@ struct AttnProblem {
     int64_t ld_vt;
     int causal;
     float scale_log2;     // log2(e) / sqrt(d)
+    // Key-range split: with kv_split = 2 each query tile's key tiles are halved between two
+    // workgroups, which write unnormalised partials (part_o [items][128][d] fp32 and the
+    // running max and denominator part_ml [items][128][2]) merged by a second kernel.
+    int kv_split;         // 1 or 2
+    float* part_o;
+    float* part_ml;
 };
+// Bytes of the key-range-split partials for a problem (0 when no split is used).
+size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim, bool causal,
+                               int* kv_split);
 
 hipError_t attention_fwd(const AttnProblem& p, hipStream_t stream);
 

@@ -166,7 +166,7 @@ hipError_t launch_row(const void* X, const void* W, float* Z, int64_t rows, int6
 struct AttnLayout {
     int hl, kvl, d;
     int64_t ld_vt;
-    size_t q, k, vt, o, total;
+    size_t q, k, vt, o, part_o, part_ml, total;   // part_*: key-range-split partials (or none)
 };
 
 // n_kv_heads key/value heads (= n_heads for multi-head attention). A rank holds
@@ -206,7 +206,13 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
     L->k = round_up(L->q + q_elems * 2, 256);
     L->vt = round_up(L->k + kv_elems * 2, 256);
     L->o = round_up(L->vt + (size_t)batch * L->kvl * d * L->ld_vt * 2, 256);
-    L->total = round_up(L->o + (size_t)batch * seq * L->hl * d * 2, 256);
+    const size_t o_end = round_up(L->o + (size_t)batch * seq * L->hl * d * 2, 256);
+    const size_t part = tps::attention_partial_bytes((int)batch, L->hl, (int)seq, (int)d, true, nullptr);
+    // split partials: outputs [items][128][d] then (max, denominator) [items][128][2]
+    const size_t part_o_bytes = part / (size_t)(d + 2) * (size_t)d;
+    L->part_o = o_end;
+    L->part_ml = round_up(L->part_o + part_o_bytes, 256);
+    L->total = part ? round_up(L->part_ml + (part - part_o_bytes), 256) : o_end;
     return TP_OK;
 }
 
@@ -518,6 +524,13 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
     a.batch = (int)batch; a.heads_local = L.hl; a.kv_heads_local = L.kvl; a.seq = (int)seq;
     a.head_dim = L.d; a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    const size_t part = tps::attention_partial_bytes((int)batch, L.hl, (int)seq, L.d, causal, &a.kv_split);
+    if (part) {
+        a.part_o = reinterpret_cast<float*>(ws + L.part_o);
+        a.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+    } else {
+        a.kv_split = 1;
+    }
     e = tps::attention_fwd(a, s);
     if (e != hipSuccess) return hip_status(e, "attention launch");
     // 3. Row-parallel output projection: Z_i = O_i W_O,i (fp32 partial).

@@ -209,7 +209,13 @@ def test_workspace_sizes():
     assert st == 0
     e = 4 * 4 * 2048 * 128 * 2
     assert off == dict(q=0, k=e, vt=2 * e, o=3 * e)
-    assert B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16) == 4 * e
+    # 16 x 16 = 256 query tiles (< 2 per compute unit): two key-range halves per tile keep
+    # fp32 partials after O: outputs [512][128][128], then (max, denominator) [512][128][2]
+    part_o, part_ml = 512 * 128 * 128 * 4, 512 * 128 * 2 * 4
+    assert B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16) == 4 * e + part_o + part_ml
+    # 8 sequences x 16 heads x 16 tiles = 2048 query tiles: no split, no partials
+    e8 = 8 * 16 * 2048 * 128 * 2
+    assert B.tp_attn_workspace_bytes(8, 2048, 8192, 64, 4, BF16) == 4 * e8
     st, off = B.tp_attn_workspace_layout(1, 5, 256, 2, 1, BF16)
     # 2 heads of d = 128, seq 5: Q and K are 2560 bytes; V^T rows are padded to 8 keys
     assert st == 0 and off == dict(q=0, k=2560, vt=5120, o=5120 + 2 * 128 * 8 * 2)

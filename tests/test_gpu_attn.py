@@ -77,6 +77,32 @@ def test_attn_small_every_step(case):
         assert max(errs) < TOL
 
 
+@pytest.mark.parametrize("case", SMALL)
+def test_attn_forced_key_range_split(case, monkeypatch):
+    """The same shards with each query tile's keys halved between two workgroups and the
+    halves merged by a second kernel (the path long causal sequences take by default; the
+    knob forces it on these small grids): ragged tails, single-tile sequences, halves that
+    hold no visible key for some queries, d = 64, and the unmasked case."""
+    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "2")
+    test_attn_small_every_step(case)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_split_and_unsplit_agree(causal, monkeypatch):
+    """Both paths compute the same softmax: agreement to bf16 rounding of O."""
+    batch, seq, h, H, N = 2, 300, 512, 4, 2
+    w = Workload(name="a", kind="attn", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, n_shards=N)
+    d = attn_inputs(w, seed=17)
+    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "2")
+    _, O_split, *_ = run_attn(d, batch, seq, H, N, 1, causal)
+    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "0")
+    _, O_one, *_ = run_attn(d, batch, seq, H, N, 1, causal)
+    e = oracle.rel_frobenius(O_split, O_one)
+    print("split vs unsplit O: %.2e" % e)
+    assert e < 5e-3
+
+
 def test_attn_causal_first_row_is_projected_value():
     """Causal row 0 of every sequence attends only to itself: O[b, 0] = V[b, 0] (to bf16)."""
     batch, seq, h, H, N = 3, 33, 256, 2, 1
@@ -88,9 +114,12 @@ def test_attn_causal_first_row_is_projected_value():
         np.testing.assert_allclose(O[b * seq], v[b * seq], rtol=1e-2, atol=1e-2)
 
 
-@pytest.mark.parametrize("rank", [0, 5])
-def test_attn_full_size_shard_sampled_rows(rank):
-    """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows."""
+@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "2")])
+def test_attn_full_size_shard_sampled_rows(rank, split, monkeypatch):
+    """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows; also
+    with the key-range split forced (at 4096 tokens per sequence it is the default)."""
+    if split:
+        monkeypatch.setenv("TPSHARD_ATTN_SPLIT", split)
     w = WORKLOADS["attn_shard_bf16_b4_s2048_h4096_H32_n8"]
     d = attn_inputs(w)
     Z, O, *_ = run_attn(d, w.batch, w.seq, w.heads, w.n_shards, rank, True)
