@@ -205,10 +205,16 @@ tp_status tp_swiglu_shard_fwd(const void* X, const void* Wgate_i, const void* Wu
  *                                       Wo_i[o][j] = W_O[r*Hl*d + j][o]
  *   Z_i     [batch*seq, hidden]   fp32  rank's partial
  * Workspace layout (byte offsets from tp_attn_workspace_layout, each 256-byte aligned):
- *   Q   [batch, Hl, seq, d]  bf16     projected queries of the local heads
+ *   Q   [batch, Hl, seq, d]  bf16     projected queries of the local heads, multiplied by
+ *                                     log2(e)/sqrt(d) (the softmax's scale, folded in before
+ *                                     the one rounding to bf16)
  *   K   [batch, Hl, seq, d]  bf16     projected keys
  *   Vt  [batch, Hl, d, seq]  bf16     projected values, transposed per head
  *   O   [batch*seq, Hl*d]    bf16     head outputs, concatenated locally
+ *   then, when the shard has under 512 query tiles of 128 tokens (batch*Hl*ceil(seq/128)),
+ *   the fp32 partial results of the two key-range halves of every query tile
+ *   ([tiles][2][128][d] outputs, then [tiles][2][128][2] maxima and denominators), used for
+ *   causal attention over sequences of 4096 tokens or more.
  * dt: TP_BF16 only. d must be 64 or 128.
  * ---------------------------------------------------------------------------------------- */
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
@@ -335,7 +341,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 7
+#define TP_SHARD_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -170,35 +170,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     };
 
     f32x4 acc[DB][2];
+    // Denominators: the P V^T products' companion with an all-ones A operand sums each
+    // query's probabilities over the tile's keys into every element of lsum[qb].
+    f32x4 lsum[2];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY};   // running max of the raw scores
-    float l_run[2] = {0.f, 0.f};               // this lane's share of the denominator
-    const float sl2 = p.scale_log2;
+    lsum[0] = lsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Running max of the scores. Q arrives multiplied by log2(e) / sqrt(d), so a score is
+    // already the exponent of base 2 and a probability is exp2(score - max).
+    float m_run[2] = {-INFINITY, -INFINITY};
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = bf16(1.0f);
 
     // The running maximum is raised only when a tile's maximum exceeds it by more than
     // 2^kLazy in probability (FlashAttention's result does not depend on which maximum is
     // subtracted, as long as numerator and denominator use the same one); in between, the
     // probabilities stay below 2^kLazy and the rescale of the output is skipped.
     constexpr float kLazy = 8.0f;
-    const float lazy_raw = kLazy / sl2;
 
-    // ---- the three phases of one key tile
-    // S^T = K Q^T : s[kb][qb][i] = score(key k0 + krow(kb, 4fg + i), query qw0 + 16qb + fr),
-    // masked (keys past the query or past the end of the sequence) when MASKED.
+    // ---- the phases of one key tile
+    // S^T = K Q^T - m: s[kb][qb][i] = score(key k0 + krow(kb, 4fg + i), query qw0 + 16qb + fr)
+    // minus that query's running max, which enters as the products' accumulator input (0
+    // while the query has none); masked (keys past the query or past the end of the sequence)
+    // when MASKED.
     auto scores = [&](const bf16* sKc, int k0, auto masked_c, f32x4 (&s)[4][2]) {
         constexpr bool MASKED = decltype(masked_c)::value;
+        f32x4 c0[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float mo = m_run[qb] == -INFINITY ? 0.f : -m_run[qb];
+            c0[qb] = f32x4{mo, mo, mo, mo};
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int row = krow(kb, fr);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int c = ks * 4 + fg;
                 const bf16x8 kf =
                     *reinterpret_cast<const bf16x8*>(&sKc[row * D + ((c ^ kswz(row)) << 3)]);
-                s[kb][0] = mfma16x16x32(kf, qf[0][ks], s[kb][0]);
-                s[kb][1] = mfma16x16x32(kf, qf[1][ks], s[kb][1]);
+                s[kb][0] = mfma16x16x32(kf, qf[0][ks], ks == 0 ? c0[0] : s[kb][0]);
+                s[kb][1] = mfma16x16x32(kf, qf[1][ks], ks == 0 ? c0[1] : s[kb][1]);
             }
         }
         if constexpr (MASKED) {
@@ -214,9 +227,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
             }
         }
     };
-    // Running max, (lazy) rescale of the output and denominator, P = exp2((s - m) scale
-    // log2 e) <= 2^kLazy packed as bf16 B-operands: pf[qb][j] = keys 32j + 8fg + 0..7.
-    auto softmax = [&](f32x4 (&s)[4][2], bf16x8 (&pf)[2][2]) {
+    // Tile maximum relative to the running one; when some query's exceeds kLazy (or the query
+    // had no maximum yet), raise that query's maximum by it, rescale its output and
+    // denominator by exp2(-shift), and shift the tile's scores to the new maximum.
+    auto update_max = [&](f32x4 (&s)[4][2]) {
         float mx[2];
         bool grew = false;
 #pragma unroll
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
             m = fmaxf(m, __shfl_xor(m, 16));
             m = fmaxf(m, __shfl_xor(m, 32));
             mx[qb] = m;
-            grew = grew || m > m_run[qb] + lazy_raw;
+            grew = grew || (m_run[qb] == -INFINITY ? m != -INFINITY : m > kLazy);
         }
         if (__any(grew)) {
             // (a scheduling fence keeps this a real branch: the rescale is rare, and
@@ -237,39 +251,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const float mn = fmaxf(m_run[qb], mx[qb]);
-                const float alpha =
-                    m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[qb] - mn) * sl2);
-                m_run[qb] = mn;
-                l_run[qb] *= alpha;
+                const bool none = m_run[qb] == -INFINITY;
+                const float shift = none ? (mx[qb] == -INFINITY ? 0.f : mx[qb]) : fmaxf(mx[qb], 0.f);
+                const float alpha = none ? 0.f : __builtin_amdgcn_exp2f(-shift);
+                m_run[qb] = none ? (mx[qb] == -INFINITY ? -INFINITY : mx[qb]) : m_run[qb] + shift;
+                lsum[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-            }
-        }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float mo = m_run[qb] == -INFINITY ? 0.f : -m_run[qb] * sl2;
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], sl2, mo));
-                    s[kb][qb][i] = e;
-                    ls += e;
-                }
-            l_run[qb] += ls;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[qb][j][i] = to_bf16(s[2 * j][qb][i]);
-                    pf[qb][j][4 + i] = to_bf16(s[2 * j + 1][qb][i]);
-                }
+                for (int kb = 0; kb < 4; ++kb) s[kb][qb] -= shift;
             }
         }
     };
-    // O^T += V^T P^T
+    // P = exp2(s) <= 2^kLazy packed as bf16 B operands: pf[qb][j] = keys 32j + 8fg + 0..7.
+    auto probs = [&](const f32x4 (&s)[4][2], bf16x8 (&pf)[2][2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[qb][j][i] = to_bf16(__builtin_amdgcn_exp2f(s[2 * j][qb][i]));
+                    pf[qb][j][4 + i] = to_bf16(__builtin_amdgcn_exp2f(s[2 * j + 1][qb][i]));
+                }
+    };
+    // O^T += V^T P^T, and the denominators
     auto pv = [&](const bf16* sVc, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -282,62 +288,89 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
                 acc[db][1] = mfma16x16x32(vf, pf[1][j], acc[db][1]);
             }
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            lsum[0] = mfma16x16x32(ones, pf[0][j], lsum[0]);
+            lsum[1] = mfma16x16x32(ones, pf[1][j], lsum[1]);
+        }
     };
     // A tile is needed by a wave unless all the wave's queries precede it (causal).
     auto needed = [&](int t) { return t < t_hi && (!CAUSAL || t * BKV <= qw0 + QPW - 1); };
 
-    // Set s takes key tiles t_lo + s, t_lo + s + 2, ...: in iteration it both sets score,
-    // weight and accumulate one tile each (t_lo + 2 it + s) from their own double-buffered LDS
-    // ring, loading the tile after next meanwhile; the iterations end in the shared workgroup
-    // barrier, set 1 idling in the last one when the range is odd. (Rotating set 1's phases
-    // against set 0's so that one set's exponentials meet the other's matrix products
-    // measured slower.)
+    // Set s takes key tiles t0 = t_lo + s, t0 + 2, ... and runs them as a two-stage pipeline:
+    // in iteration it it turns the scores of tile t = t0 + 2 it into probabilities and
+    // accumulates P V over it while the matrix cores compute the scores of tile t + 2, so one
+    // wave's exponentials overlap its own matrix products. K thus runs one tile ahead of V in
+    // the set's double-buffered LDS ring: iteration it reads K(t + 2) and V(t) and loads
+    // K(t + 4) into K(t)'s buffer and V(t + 2) into V(t - 2)'s. The iterations begin with the
+    // shared workgroup barrier; set 1 idles in the last one when the range is odd.
+    const int t0 = t_lo + set;
     const int n_it = (t_hi - t_lo + 1) / 2;
-    if (t_lo + set < t_hi) {
-        fetchK((t_lo + set) * BKV, 0);
-        fetchV((t_lo + set) * BKV, 0);
+    if (t0 < t_hi) {
+        fetchK(t0 * BKV, 0);
+        fetchV(t0 * BKV, 0);
     }
-    __syncthreads();
+    if (t0 + 2 < t_hi) fetchK((t0 + 2) * BKV, 1);
+    __syncthreads();   // (the compiler waits for the loads first)
+    f32x4 sA[4][2], sB[4][2];
+    if (needed(t0)) {
+        scores(tileK(set, 0), t0 * BKV, std::true_type{}, sA);
+        update_max(sA);
+    }
 
-    auto window = [&](int it, auto masked_c) {
-        const int cur = it & 1, t = t_lo + 2 * it + set, k0 = t * BKV;
-        if (t + 2 < t_hi) {
-            fetchK(k0 + 2 * BKV, cur ^ 1);
-            fetchV(k0 + 2 * BKV, cur ^ 1);
+    auto window = [&](int it, auto masked_c, f32x4 (&s)[4][2], f32x4 (&sn)[4][2]) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int t = t0 + 2 * it, tn = t + 2;
+        const int kb_cur = it & 1;
+        __syncthreads();   // K(t + 2) and V(t) have landed; K(t) and V(t - 2) are free
+        if (tn + 2 < t_hi) fetchK((tn + 2) * BKV, kb_cur);
+        if (tn < t_hi) fetchV(tn * BKV, kb_cur ^ 1);
+        bf16x8 pf[2][2];
+        if constexpr (!MASKED) {
+            // every query of the workgroup sees tiles t and t + 2 in full: one block, so the
+            // scheduler can interleave the two tiles' work
+            scores(tileK(set, kb_cur ^ 1), tn * BKV, std::false_type{}, sn);
+            probs(s, pf);
+            pv(tileV(set, kb_cur), pf);
+            update_max(sn);
+        } else {
+            if (needed(tn)) scores(tileK(set, kb_cur ^ 1), tn * BKV, std::true_type{}, sn);
+            if (needed(t)) {
+                probs(s, pf);
+                pv(tileV(set, kb_cur), pf);
+            }
+            if (needed(tn)) update_max(sn);
         }
-        // Unmasked windows only meet tiles that every query of the workgroup sees in full.
-        if (!decltype(masked_c)::value || needed(t)) {
-            f32x4 s[4][2];
-            bf16x8 pf[2][2];
-            scores(tileK(set, cur), k0, masked_c, s);
-            softmax(s, pf);
-            pv(tileV(set, cur), pf);
-        }
-        __syncthreads();   // the next tile has landed (the compiler waits for the loads first)
     };
-    // Windows whose two tiles lie inside the sequence and wholly before the workgroup's first
-    // query (causal) need no mask; the rest (the diagonal, a ragged end) do.
-    // (Both tiles of such a window must also lie in this workgroup's range [t_lo, t_hi).)
+    // Windows whose next tile (t + 2, for both sets) lies inside the sequence and wholly
+    // before the workgroup's first query (causal) need no mask (tile t then does not either);
+    // the rest (the diagonal, a ragged end) do. Tiles must also lie in [t_lo, t_hi).
     const int full_tiles = min(min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV), t_hi);
-    const int n_full_it = min(max(full_tiles - t_lo, 0) / 2, n_it);
+    const int n_full_it = min(max(full_tiles - t_lo - 2, 0) / 2, n_it);
     int it = 0;
-    for (; it < n_full_it; ++it) window(it, std::false_type{});
-    for (; it < n_it; ++it) window(it, std::true_type{});
+    for (; it + 2 <= n_full_it; it += 2) {
+        window(it, std::false_type{}, sA, sB);
+        window(it + 1, std::false_type{}, sB, sA);
+    }
+    if (it < n_full_it) {
+        window(it, std::false_type{}, sA, sB);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sA[kb][0] = sB[kb][0], sA[kb][1] = sB[kb][1];
+        ++it;
+    }
+    for (; it + 2 <= n_it; it += 2) {
+        window(it, std::true_type{}, sA, sB);
+        window(it + 1, std::true_type{}, sB, sA);
+    }
+    if (it < n_it) window(it, std::true_type{}, sA, sB);
 
     // ---- merge the two sets' partials: set 1 publishes (output, max, denominator) of each of
     // its lanes; the set-0 wave with the same queries (same wave index, same lane) combines
-    // them, rescaling each side by exp(m_side - m) with m the larger maximum.
-    float lq[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float l = l_run[qb];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        lq[qb] = l;
-    }
+    // them, rescaling each side by exp2(m_side - m) with m the larger maximum.
     constexpr int NF = DB * 2 * 4 + 4;   // floats per lane: output, 2 maxima, 2 denominators
     static_assert(4 * NF * 64 * 4 <= (int)sizeof(lds), "merge area");
     float* xch = reinterpret_cast<float*>(lds) + wave * NF * 64 + lane;   // [wave][field][lane]
+    __syncthreads();   // every wave is done with the tiles in the LDS
     if (set == 1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -347,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
                 for (int i = 0; i < 4; ++i) xch[((db * 2 + qb) * 4 + i) * 64] = acc[db][qb][i];
         xch[(NF - 4) * 64] = m_run[0];
         xch[(NF - 3) * 64] = m_run[1];
-        xch[(NF - 2) * 64] = lq[0];
-        xch[(NF - 1) * 64] = lq[1];
+        xch[(NF - 2) * 64] = lsum[0][0];
+        xch[(NF - 1) * 64] = lsum[1][0];
     }
     __syncthreads();
     if (set == 1) return;
@@ -368,9 +401,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
         const float l1 = xch[(NF - 2 + qb) * 64];
         const float m0 = m_run[qb];
         const float m = fmaxf(m0, m1);
-        const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * sl2);
-        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * sl2);
-        const float l = lq[qb] * a0 + l1 * a1;
+        const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+        const float l = lsum[qb][0] * a0 + l1 * a1;
         const int q = qw0 + qb * 16 + fr;
         if (q >= p.seq) continue;
         if (halves == 1) {
@@ -402,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     }
 }
 
-// Merge of the two key-range halves of every query tile: with m = max(m_0, m_1) and
-// a_h = exp((m_h - m) scale) (0 for a half that saw no key), O = (O_0 a_0 + O_1 a_1) /
+// Merge of the two key-range halves of every query tile: with m = max(m_0, m_1) (maxima of
+// the base-2 exponents) and a_h = exp2(m_h - m) (0 for a half that saw no key), O = (O_0 a_0 + O_1 a_1) /
 // (l_0 a_0 + l_1 a_1), the same rescaling as the online softmax. One workgroup per 16 rows
 // of a (sequence, head, query tile); lanes take 4-wide vectors of those rows.
 constexpr int kMergeRows = 16;
@@ -419,7 +452,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnProblem p)
     if (rows <= 0) return;
     const int b = bh / p.heads_local, head = bh - b * p.heads_local;
     const int64_t item0 = ((int64_t)bh * n_qt + qt) * 2;
-    const float sl2 = p.scale_log2;
     const int64_t ldo = (int64_t)p.heads_local * D;
     bf16* __restrict__ gO = reinterpret_cast<bf16*>(p.o);
     for (int e = threadIdx.x; e < rows * (D / 4); e += 256) {
@@ -427,8 +459,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnProblem p)
         const float2 ml0 = *reinterpret_cast<const float2*>(p.part_ml + (item0 * BQ + r) * 2);
         const float2 ml1 = *reinterpret_cast<const float2*>(p.part_ml + ((item0 + 1) * BQ + r) * 2);
         const float m = fmaxf(ml0.x, ml1.x);
-        const float a0 = ml0.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml0.x - m) * sl2);
-        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml1.x - m) * sl2);
+        const float a0 = ml0.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml0.x - m);
+        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - m);
         const float inv = 1.0f / (ml0.y * a0 + ml1.y * a1);
         const f32x4 o0 = *reinterpret_cast<const f32x4*>(p.part_o + (item0 * BQ + r) * D + 4 * c4);
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(p.part_o + ((item0 + 1) * BQ + r) * D + 4 * c4);

@@ -8,7 +8,8 @@
 //   F32       Z_i = Y_i B_i  (fp32 partial)             row-parallel layers (MLP, W_O)
 //   Bias      Y = X W_i + b_i                           column-parallel, no activation
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
-//             per head, V written transposed for the attention kernel's P V product.
+//             per head, V written transposed for the attention kernel's P V product, Q
+//             multiplied by q_scale (the softmax's scale) before it is rounded.
 //   SwiGlu    A_i = SiLU(X W_gate,i) * (X W_up,i)       gated column-parallel MLP layer: the
 //             block's B slab interleaves gate and up rows in 32-row blocks (loaded from the
 //             two weights), so each wave's pairs of 32-column MFMA blocks hold the gate and
@@ -107,7 +108,7 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
             const int b = m / p.seq;
             const int s = m - b * p.seq;
             const int64_t bh = (int64_t)b * (which == 0 ? p.heads_local : p.kv_heads_local) + head;
-            const bf16x4 o = to_bf16x4(v);
+            const bf16x4 o = to_bf16x4(which == 0 ? v * p.q_scale : v);
             if (which < 2) {
                 bf16* dst = reinterpret_cast<bf16*>(which == 0 ? p.q : p.k) +
                             (bh * p.seq + s) * p.head_dim + j;

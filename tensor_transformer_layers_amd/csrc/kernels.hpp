@@ -36,6 +36,7 @@ struct GemmProblem {
     int seq, heads_local, head_dim;
     int kv_heads_local;   // KVl
     int64_t ld_vt;
+    float q_scale;        // factor on the query columns before rounding (the softmax's scale)
 };
 
 // Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).
@@ -48,7 +49,7 @@ hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t stream);
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t stream);
 
 struct AttnProblem {
-    const void* q;        // [batch, Hl, seq, d] bf16
+    const void* q;        // [batch, Hl, seq, d] bf16, Q times log2(e) / sqrt(d)
     const void* k;        // [batch, KVl, seq, d] bf16
     const void* vt;       // [batch, KVl, d, ld_vt] bf16
     void* o;              // [batch * seq, Hl * d] bf16
@@ -56,7 +57,6 @@ struct AttnProblem {
     int kv_heads_local;   // KVl; local query head j reads key/value head j / (Hl / KVl)
     int64_t ld_vt;
     int causal;
-    float scale_log2;     // log2(e) / sqrt(d)
     // Key-range split: with kv_split = 2 each query tile's key tiles are halved between two
     // workgroups, which write unnormalised partials (part_o [items][128][d] fp32 and the
     // running max and denominator part_ml [items][128][2]) merged by a second kernel.

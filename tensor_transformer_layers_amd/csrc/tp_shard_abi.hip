@@ -516,6 +516,9 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
     g.q = ws + L.q; g.k = ws + L.k; g.vt = ws + L.vt;
     g.seq = (int)seq; g.heads_local = L.hl; g.kv_heads_local = L.kvl; g.head_dim = L.d;
     g.ld_vt = L.ld_vt;
+    // The softmax's scale 1/sqrt(d), with log2(e) for its base-2 exponentials, is folded into
+    // the stored queries (one rounding of the fp32 result either way).
+    g.q_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
     hipError_t e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
     if (e != hipSuccess) return hip_status(e, "QKV projection launch");
     // 2. Head-local attention; heads concatenated locally into O_i.
@@ -523,7 +526,6 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
     a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;
     a.batch = (int)batch; a.heads_local = L.hl; a.kv_heads_local = L.kvl; a.seq = (int)seq;
     a.head_dim = L.d; a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
-    a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
     const size_t part = tps::attention_partial_bytes((int)batch, L.hl, (int)seq, L.d, causal, &a.kv_split);
     if (part) {
         a.part_o = reinterpret_cast<float*>(ws + L.part_o);

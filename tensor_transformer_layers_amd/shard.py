@@ -181,7 +181,8 @@ def attn_workspace(batch: int, seq: int, hidden: int, n_heads: int, n_shards: in
 
 def attn_views(workspace: torch.Tensor, batch: int, seq: int, hidden: int, n_heads: int,
                n_shards: int) -> Dict[str, torch.Tensor]:
-    """Views of the attention workspace: q, k [b, Hl, s, d], vt [b, Hl, d, ld_vt], o [b*s, Hl*d]."""
+    """Views of the attention workspace: q, k [b, Hl, s, d], vt [b, Hl, d, ld_vt], o [b*s, Hl*d].
+    q holds the projected queries times log2(e) / sqrt(d) (the softmax's scale, folded in)."""
     st, off = B.tp_attn_workspace_layout(batch, seq, hidden, n_heads, n_shards, B.TP_BF16)
     B.check(st)
     hl = n_heads // n_shards

@@ -37,7 +37,8 @@ def run_attn(d, batch, seq, H, N, r, causal, bias=True):
     v = shard.attn_views(ws.body, batch, seq, h, H, N)
     hl, dd = H // N, h // H
     # [b, Hl, s, d] -> [b*s, Hl*d]
-    q = host(v["q"].permute(0, 2, 1, 3).reshape(T, hl * dd))
+    # the workspace holds Q times the softmax's log2(e) / sqrt(d)
+    q = host(v["q"].permute(0, 2, 1, 3).reshape(T, hl * dd)) / (np.log2(np.e) / np.sqrt(dd))
     k = host(v["k"].permute(0, 2, 1, 3).reshape(T, hl * dd))
     vv = host(v["vt"][..., :seq].permute(0, 3, 1, 2).reshape(T, hl * dd))
     return host(Zc.tensor), host(v["o"]), q, k, vv
