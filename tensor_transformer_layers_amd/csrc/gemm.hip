@@ -98,26 +98,6 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
                 float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
                 *reinterpret_cast<f32x4*>(c) = v;
             }
-        } else {  // Qkv (bf16 only): Hl query heads, then KVl key and KVl value heads
-            const int wq = p.heads_local * p.head_dim;
-            const int wkv = p.kv_heads_local * p.head_dim;
-            const int which = n < wq ? 0 : (n < wq + wkv ? 1 : 2);
-            const int rem = n - (which == 0 ? 0 : wq + (which - 1) * wkv);
-            const int head = rem / p.head_dim;
-            const int j = rem - head * p.head_dim;
-            const int b = m / p.seq;
-            const int s = m - b * p.seq;
-            const int64_t bh = (int64_t)b * (which == 0 ? p.heads_local : p.kv_heads_local) + head;
-            const bf16x4 o = to_bf16x4(which == 0 ? v * p.q_scale : v);
-            if (which < 2) {
-                bf16* dst = reinterpret_cast<bf16*>(which == 0 ? p.q : p.k) +
-                            (bh * p.seq + s) * p.head_dim + j;
-                *reinterpret_cast<bf16x4*>(dst) = o;
-            } else {
-                bf16* dst = reinterpret_cast<bf16*>(p.vt) + (bh * p.head_dim + j) * p.ld_vt + s;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * p.ld_vt] = o[i];
-            }
         }
     }
 }
@@ -178,8 +158,8 @@ struct InterleaveGroups {
 // the (now idle) operand LDS, FM / R block-rows at a time, and reads it back row-contiguously:
 // consecutive lanes take consecutive 4-column vectors of one row, so every store instruction
 // writes whole row segments. The staging rows are padded by 16 bytes, which puts the 16 rows
-// written by one 16-lane pass on 16 distinct bank groups. The Qkv scatter keeps the direct
-// path (its destination is three per-head arrays, one of them transposed).
+// written by one 16-lane pass on 16 distinct bank groups. The Qkv scatter reads the staged
+// tile back in 8-element chunks along rows (queries, keys) or columns (values, transposed).
 // Fewest rounds R (a divisor of the FM block-rows) whose FM / R block-rows of every wave fit
 // in the LDS at once; bytes_per_block_row covers all the waves.
 constexpr int staging_rounds(int fm, int bytes_per_block_row, int lds_bytes)
@@ -189,55 +169,127 @@ constexpr int staging_rounds(int fm, int bytes_per_block_row, int lds_bytes)
     return fm + 1;   // does not fit even one block-row at a time: caught by the static_assert
 }
 
+// The Qkv scatter of one staged round: RR rows x WTN columns of fp32 at byte pitch PITCH, the
+// round's origin at output row m0 and column c0. Query and key columns leave as 8-column row
+// chunks (one 16-byte store into a head's [seq, d] row: consecutive lanes write consecutive
+// chunks of a row); value columns as 8-token column chunks (one 16-byte store into the V^T row
+// of that feature) when the sequence length is a multiple of 8, else token by token. The query
+// columns are multiplied by q_scale after the bias. A chunk never straddles two heads (head
+// widths are multiples of 8 and so are the chunks' first columns).
+template <int WTN, int RR, int PITCH>
+__device__ __forceinline__ void qkv_write(const GemmProblem& p, const char* region, int m0,
+                                          int c0, int lane)
+{
+    const int d = p.head_dim;
+    const int wq = p.heads_local * d;
+    const int vlo = wq + p.kv_heads_local * d;   // first value column
+    const bf16* bias = reinterpret_cast<const bf16*>(p.bias);
+    if (c0 < vlo) {
+        constexpr int C8 = WTN / 8, ITEMS = RR * C8;
+#pragma unroll
+        for (int t0 = 0; t0 < ITEMS; t0 += 64) {
+            const int t = t0 + lane;
+            const int row = t / C8, c8 = t - row * C8;
+            const int m = m0 + row, n = c0 + 8 * c8;
+            if (t >= ITEMS || m >= p.M || n >= vlo) continue;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(region + row * PITCH + c8 * 32);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(region + row * PITCH + c8 * 32 + 16);
+            float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            if (bias) {
+                const bf16x8 bb = *reinterpret_cast<const bf16x8*>(bias + n);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += static_cast<float>(bb[e]);
+            }
+            const bool isq = n < wq;
+            const float sc = isq ? p.q_scale : 1.0f;
+            const int rem = isq ? n : n - wq;
+            const int head = rem / d, jj = rem - head * d;
+            const int bb_ = m / p.seq, sq = m - bb_ * p.seq;
+            const int64_t bh = (int64_t)bb_ * (isq ? p.heads_local : p.kv_heads_local) + head;
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e] * sc);
+            bf16* dst = reinterpret_cast<bf16*>(isq ? p.q : p.k) + (bh * p.seq + sq) * d + jj;
+            *reinterpret_cast<bf16x8*>(dst) = o;
+        }
+    }
+    if (c0 + WTN > vlo) {
+        constexpr int R8 = RR / 8, ITEMS = R8 * WTN;
+        const bool vec = p.seq % 8 == 0;
+#pragma unroll
+        for (int t0 = 0; t0 < ITEMS; t0 += 64) {
+            const int t = t0 + lane;
+            const int rc = t / WTN, col = t - rc * WTN;
+            const int n = c0 + col, mb = m0 + 8 * rc;
+            if (t >= ITEMS || n < vlo || n >= p.N || mb >= p.M) continue;
+            const float bv = bias ? static_cast<float>(bias[n]) : 0.0f;
+            const int rem = n - vlo;
+            const int head = rem / d, jj = rem - head * d;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = *reinterpret_cast<const float*>(region + (8 * rc + e) * PITCH + col * 4) + bv;
+            bf16* vt = reinterpret_cast<bf16*>(p.vt);
+            if (vec) {
+                // seq % 8 == 0: the 8 tokens lie in one sequence, starting at a multiple of 8
+                const int bb_ = mb / p.seq, sq = mb - bb_ * p.seq;
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = to_bf16(v[e]);
+                *reinterpret_cast<bf16x8*>(
+                    vt + (((int64_t)bb_ * p.kv_heads_local + head) * d + jj) * p.ld_vt + sq) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int m = mb + e;
+                    if (m >= p.M) break;
+                    const int bb_ = m / p.seq, sq = m - bb_ * p.seq;
+                    vt[(((int64_t)bb_ * p.kv_heads_local + head) * d + jj) * p.ld_vt + sq] =
+                        to_bf16(v[e]);
+                }
+            }
+        }
+    }
+}
+
+// ---- epilogue: every output type goes through LDS ---------------------------------------
+// Each wave stages its accumulators (fp32) in its own region of the idle operand LDS, FM / R
+// block-rows per round, then reads them back row-contiguously (the Qkv scatter: see qkv_write).
 template <Epi EPI, int WTM, int WTN, int NW, int LDS_BYTES>
 __device__ __forceinline__ void store_tile(const GemmProblem& p, f32x16 (&acc)[WTN / 32][WTM / 32],
                                            char* lds, int r0, int c0, int wave, int lane)
 {
     constexpr int FM = WTM / 32, FN = WTN / 32;
     const int fr = lane & 31, fg = lane >> 5;
-    if constexpr (EPI == Epi::Qkv) {
+    constexpr int PITCH = WTN * 4 + 16;                 // bytes per staged row
+    constexpr int R = staging_rounds(FM, NW * 32 * PITCH, LDS_BYTES);   // rounds
+    constexpr int FMR = FM / R, RR = FMR * 32;          // block-rows and rows per round
+    static_assert(NW * RR * PITCH <= LDS_BYTES, "staging does not fit");
+    constexpr int V4 = WTN / 4;                         // 4-column vectors per row
+    constexpr int PER_LANE = RR * V4 / 64;
+    char* region = lds + wave * RR * PITCH;
+    // Every wave is past its last operand read, and this wave's slab loads (including the
+    // unused one past the end of K) have landed, before the operand LDS is overwritten.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = r0 + j * 32 + fr;
-            if (m >= p.M) continue;
+    for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+        for (int jj = 0; jj < FMR; ++jj)
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = c0 + i * 32 + 8 * q + 4 * fg;
-                    if (n < p.N)
-                        store_out<EPI, bf16>(p, m, n,
-                                             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                   acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+                    const int j = rr * FMR + jj;
+                    *reinterpret_cast<f32x4*>(region + (jj * 32 + fr) * PITCH +
+                                              (i * 32 + 8 * q + 4 * fg) * 4) =
+                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
                 }
-        }
-    } else {
-        constexpr int PITCH = WTN * 4 + 16;                 // bytes per staged row
-        constexpr int R = staging_rounds(FM, NW * 32 * PITCH, LDS_BYTES);   // rounds
-        constexpr int FMR = FM / R, RR = FMR * 32;          // block-rows and rows per round
-        static_assert(NW * RR * PITCH <= LDS_BYTES, "staging does not fit");
-        constexpr int V4 = WTN / 4;                         // 4-column vectors per row
-        constexpr int PER_LANE = RR * V4 / 64;
-        char* region = lds + wave * RR * PITCH;
-        // Every wave is past its last operand read, and this wave's slab loads (including the
-        // unused one past the end of K) have landed, before the operand LDS is overwritten.
-        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-#pragma unroll
-            for (int jj = 0; jj < FMR; ++jj)
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int j = rr * FMR + jj;
-                        *reinterpret_cast<f32x4*>(region + (jj * 32 + fr) * PITCH +
-                                                  (i * 32 + 8 * q + 4 * fg) * 4) =
-                            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                  acc[i][j][4 * q + 3]};
-                    }
-            __syncthreads();
+        if constexpr (EPI == Epi::Qkv) {
+            qkv_write<WTN, RR, PITCH>(p, region, r0 + rr * RR, c0, lane);
+        } else {
 #pragma unroll
             for (int t = 0; t < PER_LANE; ++t) {
                 const int idx = lane + 64 * t;
@@ -246,8 +298,8 @@ __device__ __forceinline__ void store_tile(const GemmProblem& p, f32x16 (&acc)[W
                 const int m = r0 + rr * RR + row, n = c0 + v4 * 4;
                 if (m < p.M && n < p.N) store_out<EPI, bf16>(p, m, n, v);
             }
-            if (rr + 1 < R) __syncthreads();
         }
+        if (rr + 1 < R) __syncthreads();
     }
 }
 
@@ -263,7 +315,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "tile");
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && NW % 2 == 0, "slab split");
 
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * BK];
+    // two slab buffers, then a 256-byte sink for the weight prefetch below
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * BK + 128];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -398,18 +451,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     bf16x8 fa[2][FM], fb[2][FN];
     const int KT = (p.K + BK - 1) / BK;
     // The K loop, instantiated for waves that load (loader) and waves that do not.
+    // Weight prefetch into the L2. The weight operand B is read once per layer step, so its
+    // slabs arrive from HBM; the two-buffer LDS ring hides one slab of that latency. The
+    // loading waves therefore also touch every 128-byte row segment of the B slab two slabs
+    // ahead with a 4-byte LDS-DMA load into a 256-byte sink (no register destination, so
+    // nothing ever waits on it early). Vector-memory loads complete in order, so the wait
+    // before each barrier allows exactly these PFI loads to stay in flight. The activations
+    // (A) usually come from the kernel just before and are not prefetched.
+    constexpr int PFI = (BN + 255) / 256;   // prefetch instructions per loading wave
+    constexpr int kPrefetchAhead = 2;       // slabs
+    auto prefetch = [&](int k0) {
+        bf16* sink = smem + 2 * (BM + BN) * BK;
+#pragma unroll
+        for (int t = 0; t < PFI; ++t) {
+            const int r0 = (t * 4 + (wave_u & 3)) * 64;   // a 64-row group of the B slab (scalar)
+            const int r = r0 + lane;
+            // SwiGlu: B rows [0, BN/2) of the gate, then the same features of the up weight
+            const bool up = GLU && r0 >= BN / 2;
+            const int rr = up ? r - BN / 2 : r;
+            const uint32_t off = k0 < p.K && r < BN ? (uint32_t)(rr * p.ldb + k0) * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rB2 : rB, (lds_ptr)sink, 4, off, 0, 0, 0);
+        }
+    };
     auto k_loop = [&](auto loader) {
+        constexpr bool LD = !SPLIT_LOADS || decltype(loader)::value;   // this wave loads
         constexpr int NVW = !SPLIT_LOADS ? NV : (decltype(loader)::value ? 2 * NV : 0);
+        constexpr int NPF = LD ? PFI : 0;
         fetch(0, 0, loader);
+#pragma unroll
+        for (int d = 1; d < kPrefetchAhead; ++d)
+            if constexpr (LD) prefetch(d * BK);
         __syncthreads();
         read_frags(0, 0, fa[0], fb[0]);
         for (int kt = 0; kt < KT; ++kt) {
             const int cur = kt & 1;
             __builtin_amdgcn_sched_barrier(0);
             fetch((kt + 1) * BK, cur ^ 1, loader);
+            if constexpr (LD) prefetch((kt + kPrefetchAhead) * BK);
             read_frags(cur, 1, fa[1], fb[1]);
             mma(fa[0], fb[0]);
-            InterleaveGroups<0, NM, NR, NVW>::emit();
+            InterleaveGroups<0, NM, NR, NVW + NPF>::emit();
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur, 2, fa[0], fb[0]);
             mma(fa[1], fb[1]);
@@ -419,7 +500,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             mma(fa[0], fb[0]);
             InterleaveGroups<0, NM, NR, 0>::emit();
             __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
+            // this wave's slab loads have landed (only its NPF newer prefetches may still be
+            // in flight) and its fragment reads are done; then the workgroup barrier
+            __builtin_amdgcn_s_waitcnt(0x0070 | NPF);   // vmcnt(NPF) expcnt(7) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
             read_frags(cur ^ 1, 0, fa[0], fb[0]);   // after the last slab: reads zeros, unused
             mma(fa[1], fb[1]);
             InterleaveGroups<0, NM, NR, 0>::emit();
