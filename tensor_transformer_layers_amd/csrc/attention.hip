@@ -11,24 +11,32 @@
 // output; a new key tile with maximum m' rescales both by exp(m - m'). This gives exactly
 // the softmax result (up to rounding) without materialising the seq x seq score matrix.
 //
-// Work decomposition: one workgroup = BQ = 128 queries of one (sequence, head), run by two
-// sets of 4 waves; in each set a wave owns 32 queries (two 16-query MFMA columns). The key
-// tiles (64 keys: K tile [64][d], V^T tile [d][64]) are dealt to the sets alternately (set 0
-// the even tiles, set 1 the odd ones), each set streaming its own tiles through its own
+// Work decomposition: one workgroup = BQ = 128 queries of one (sequence, head), run by one
+// or two sets of 4 waves; in a set a wave owns 32 queries (two 16-query MFMA columns). Key
+// tiles are 64 keys (K tile [64][d], V^T tile [d][64]), streamed through each set's own
 // double-buffered LDS ring (loaded from global memory directly into LDS during the previous
-// tile's work). Every SIMD thus runs two independent waves, one of each set, so one wave's
-// softmax arithmetic overlaps the other's matrix products. At the end the two partial
-// results of each query (running max, denominator, unnormalised output) are merged through
-// LDS with the same max-rescaling, which keeps the result exact. Per tile, a wave computes
-//   S^T = K Q^T      (MFMA "M" = keys, "N" = queries, K = d)
-//   O^T += V^T P^T   (MFMA "M" = d,    "N" = queries, K = keys)
+// tile's work).
+//  * Two sets (unsplit launches): the sets take alternate key tiles (set 0 the even ones), so
+//    every SIMD runs two independent waves, and their partial results (running max,
+//    denominator, unnormalised output) are merged through LDS with the same rescaling.
+//  * One set (with the key-range split, below): 64 KB of LDS, two workgroups per compute unit.
+//  * Key-range split (long causal sequences with few query tiles): each query tile's keys are
+//    halved between two workgroups, which write fp32 partials; attn_merge_kernel combines
+//    them.
+// Per tile, a wave computes
+//   S^T = K Q^T - m  (MFMA "M" = keys, "N" = queries, K = d; the running max m enters as the
+//                     accumulator input, and Q arrives pre-multiplied by log2(e)/sqrt(d))
+//   O^T += V^T P^T   (MFMA "M" = d,    "N" = queries, K = keys), and the denominators with an
+//                     all-ones operand in place of V^T
+// as a two-stage pipeline: the scores of the next tile are computed while the current tile's
+// probabilities (exp2) are formed, so a wave's exponentials overlap its own matrix products.
 // With keys on the MFMA's row side, each lane's accumulator values of S^T all belong to ONE
-// query (lane & 15), so the row max/sum need only a 4-lane exchange, the probabilities P are
+// query (lane & 15), so the row max needs only a 4-lane exchange, the probabilities P are
 // already in the lane layout the second MFMA takes as its B operand, and the O^T rows a lane
 // accumulates belong to the same query whose statistics it holds. Masks are applied only on
-// tiles that cross a wave's diagonal or the end of the sequence; the scale is folded into the
-// exponent's FMA; the output is rescaled only when some running maximum grew. Queries are
-// dispatched longest-first (highest query tile first) to shorten the causal tail.
+// tiles that cross a wave's diagonal or the end of the sequence; the output is rescaled only
+// when some running maximum grew by more than 2^8. Queries are dispatched longest-first
+// (highest query tile first) to shorten the causal tail.
 #include <cstdlib>
 #include <type_traits>
 
@@ -38,7 +46,6 @@
 namespace tps {
 namespace {
 
-constexpr int kThreads = 512;   // two sets of 4 waves
 constexpr int BQ = 128;     // queries per workgroup (per set)
 constexpr int BKV = 64;     // keys per tile
 constexpr int QPW = 32;     // queries per wave
@@ -53,8 +60,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, in
                                              0x00020000);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
+template <int D, bool CAUSAL, int NSETS>
+__global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kernel(AttnProblem p)
 {
     constexpr int KS = D / 32;            // MFMA K-steps of the S product
     constexpr int DB = D / 16;            // 16-row blocks of O^T
@@ -64,13 +71,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     constexpr int VI = D / 8 / 4;         // V^T load instructions per wave per tile (8 rows each)
 
     // [set][buffer][K tile | V^T tile]; reused for the merge of the two sets' partials.
-    __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * 2 * BKV * D];
+    __shared__ __attribute__((aligned(16))) bf16 lds[NSETS * 2 * 2 * BKV * D];
     auto tileK = [&](int set, int buf) { return lds + ((set * 2 + buf) * 2) * BKV * D; };
     auto tileV = [&](int set, int buf) { return lds + ((set * 2 + buf) * 2 + 1) * BKV * D; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int set = __builtin_amdgcn_readfirstlane(tid >> 8);   // which half of the key tiles
+    const int set = NSETS == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;   // key-tile parity
     // query group within the set; scalar, so that the per-tile causal tests below (whole tile
     // visible, tile crossing this wave's diagonal) are wave-uniform branches
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
@@ -99,8 +106,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     const int halves = p.kv_split;
     const int n_qt = (p.seq + BQ - 1) / BQ;
     const int n_bh = p.batch * p.heads_local;
-    const int qt = n_qt - 1 - (int)(blockIdx.x / (n_bh * halves));
-    const int rem_b = (int)(blockIdx.x % (n_bh * halves));
+    // With one set (two workgroups per compute unit), blocks past the first 256 take the
+    // query tiles in the reverse order, so that a unit pairs a long causal tile with a short one.
+    int bidx = (int)blockIdx.x;
+    if (NSETS == 1 && (int)gridDim.x > 256) {
+        const int r = bidx - 256, per = n_bh * halves, groups = ((int)gridDim.x - 256) / per;
+        if (r >= 0 && 256 % per == 0 && (int)gridDim.x % per == 0)
+            bidx = 256 + (groups - 1 - r / per) * per + r % per;
+    }
+    const int qt = n_qt - 1 - bidx / (n_bh * halves);
+    const int rem_b = bidx % (n_bh * halves);
     const int half = rem_b / n_bh;
     const int bh = rem_b - half * n_bh;
     const int q0 = qt * BQ;
@@ -305,12 +320,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     // K(t + 4) into K(t)'s buffer and V(t + 2) into V(t - 2)'s. The iterations begin with the
     // shared workgroup barrier; set 1 idles in the last one when the range is odd.
     const int t0 = t_lo + set;
-    const int n_it = (t_hi - t_lo + 1) / 2;
+    const int n_it = (t_hi - t_lo + NSETS - 1) / NSETS;
     if (t0 < t_hi) {
         fetchK(t0 * BKV, 0);
         fetchV(t0 * BKV, 0);
     }
-    if (t0 + 2 < t_hi) fetchK((t0 + 2) * BKV, 1);
+    if (t0 + NSETS < t_hi) fetchK((t0 + NSETS) * BKV, 1);
     __syncthreads();   // (the compiler waits for the loads first)
     f32x4 sA[4][2], sB[4][2];
     if (needed(t0)) {
@@ -320,10 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
 
     auto window = [&](int it, auto masked_c, f32x4 (&s)[4][2], f32x4 (&sn)[4][2]) {
         constexpr bool MASKED = decltype(masked_c)::value;
-        const int t = t0 + 2 * it, tn = t + 2;
+        const int t = t0 + NSETS * it, tn = t + NSETS;
         const int kb_cur = it & 1;
-        __syncthreads();   // K(t + 2) and V(t) have landed; K(t) and V(t - 2) are free
-        if (tn + 2 < t_hi) fetchK((tn + 2) * BKV, kb_cur);
+        __syncthreads();   // K(tn) and V(t) have landed; K(t) and V(t - NSETS) are free
+        if (tn + NSETS < t_hi) fetchK((tn + NSETS) * BKV, kb_cur);
         if (tn < t_hi) fetchV(tn * BKV, kb_cur ^ 1);
         bf16x8 pf[2][2];
         if constexpr (!MASKED) {
@@ -346,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     // before the workgroup's first query (causal) need no mask (tile t then does not either);
     // the rest (the diagonal, a ragged end) do. Tiles must also lie in [t_lo, t_hi).
     const int full_tiles = min(min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV), t_hi);
-    const int n_full_it = min(max(full_tiles - t_lo - 2, 0) / 2, n_it);
+    const int n_full_it = min(max(full_tiles - t_lo - NSETS, 0) / NSETS, n_it);
     int it = 0;
     for (; it + 2 <= n_full_it; it += 2) {
         window(it, std::false_type{}, sA, sB);
@@ -368,10 +383,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     // its lanes; the set-0 wave with the same queries (same wave index, same lane) combines
     // them, rescaling each side by exp2(m_side - m) with m the larger maximum.
     constexpr int NF = DB * 2 * 4 + 4;   // floats per lane: output, 2 maxima, 2 denominators
-    static_assert(4 * NF * 64 * 4 <= (int)sizeof(lds), "merge area");
+    static_assert(NSETS == 1 || 4 * NF * 64 * 4 <= (int)sizeof(lds), "merge area");
     float* xch = reinterpret_cast<float*>(lds) + wave * NF * 64 + lane;   // [wave][field][lane]
-    __syncthreads();   // every wave is done with the tiles in the LDS
-    if (set == 1) {
+    if constexpr (NSETS == 2) __syncthreads();   // every wave is done with the tiles in the LDS
+    if (NSETS == 2 && set == 1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -383,8 +398,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
         xch[(NF - 2) * 64] = lsum[0][0];
         xch[(NF - 1) * 64] = lsum[1][0];
     }
-    __syncthreads();
-    if (set == 1) return;
+    if constexpr (NSETS == 2) {
+        __syncthreads();
+        if (set == 1) return;
+    }
 
     // ---- combine; then normalise and store O[token][head*D + d] (4 consecutive d per lane),
     // or, with the key-range split, store this half's unnormalised output, max and denominator.
@@ -397,8 +414,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
     const int64_t item = ((int64_t)bh * n_qt + qt) * halves + half;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const float m1 = xch[(NF - 4 + qb) * 64];
-        const float l1 = xch[(NF - 2 + qb) * 64];
+        // (one set: there is no second partial)
+        const float m1 = NSETS == 2 ? xch[(NF - 4 + qb) * 64] : -INFINITY;
+        const float l1 = NSETS == 2 ? xch[(NF - 2 + qb) * 64] : 0.f;
         const float m0 = m_run[qb];
         const float m = fmaxf(m0, m1);
         const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
@@ -413,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
             for (int db = 0; db < DB; ++db) {
                 f32x4 o1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
+                for (int i = 0; i < 4; ++i) o1[i] = NSETS == 2 ? xch[((db * 2 + qb) * 4 + i) * 64] : 0.f;
                 *reinterpret_cast<bf16x4*>(dst + db * 16) = to_bf16x4((acc[db][qb] * a0 + o1 * a1) * inv);
             }
         } else {
@@ -423,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnProblem p)
             for (int db = 0; db < DB; ++db) {
                 f32x4 o1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o1[i] = xch[((db * 2 + qb) * 4 + i) * 64];
+                for (int i = 0; i < 4; ++i) o1[i] = NSETS == 2 ? xch[((db * 2 + qb) * 4 + i) * 64] : 0.f;
                 *reinterpret_cast<f32x4*>(po + db * 16) = acc[db][qb] * a0 + o1 * a1;
             }
             if (fg == 0) {
@@ -493,11 +511,28 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
     if (p.kv_split != 1 && (p.kv_split != 2 || !p.part_o || !p.part_ml)) return hipErrorInvalidValue;
     const int n_qt = (p.seq + BQ - 1) / BQ;
     const int n_tiles = n_qt * p.batch * p.heads_local;
-    dim3 grid((unsigned)(n_tiles * p.kv_split)), block(kThreads);
-    if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, block, 0, s, p);
+    dim3 grid((unsigned)(n_tiles * p.kv_split));
+    // Sets per workgroup: with the key-range split every query tile already has two
+    // workgroups, and one-set workgroups (64 KB of LDS, two per compute unit) overlap one
+    // workgroup's prologue and epilogue with the other's key loop: measured 2.5 us faster on
+    // the 4096-token layer step. Unsplit, two sets keep eight waves on every unit.
+    // TPSHARD_ATTN_SETS=1/2 overrides the choice (a test knob).
+    int nsets = p.kv_split == 2 ? 1 : 2;
+    if (const char* e = std::getenv("TPSHARD_ATTN_SETS")) {
+        const int v = std::atoi(e);
+        if (v == 1 || v == 2) nsets = v;
+    }
+    if (nsets == 1) {
+        if (p.causal)
+            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 1>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 1>), grid, dim3(256), 0, s, p);
+    } else {
+        if (p.causal)
+            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 2>), grid, dim3(512), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 2>), grid, dim3(512), 0, s, p);
+    }
     if (p.kv_split == 2)
         hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)(n_tiles * (BQ / kMergeRows))),
                            dim3(256), 0, s, p);

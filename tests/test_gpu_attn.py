@@ -88,6 +88,17 @@ def test_attn_forced_key_range_split(case, monkeypatch):
     test_attn_small_every_step(case)
 
 
+@pytest.mark.parametrize("split,sets", [("2", "2"), ("0", "1")])
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[3], SMALL[5]])
+def test_attn_other_set_counts(case, split, sets, monkeypatch):
+    """The combinations the default does not take: the key-range split with two sets of
+    waves per workgroup (merged through LDS, then across the halves), and one set without
+    the split (no merge at all)."""
+    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", split)
+    monkeypatch.setenv("TPSHARD_ATTN_SETS", sets)
+    test_attn_small_every_step(case)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_attn_split_and_unsplit_agree(causal, monkeypatch):
     """Both paths compute the same softmax: agreement to bf16 rounding of O."""
