@@ -214,7 +214,7 @@ tp_status tp_swiglu_shard_fwd(const void* X, const void* Wgate_i, const void* Wu
  *   then, when the shard has under 512 query tiles of 128 tokens (batch*Hl*ceil(seq/128)),
  *   the fp32 partial results of the two key-range halves of every query tile
  *   ([tiles][2][128][d] outputs, then [tiles][2][128][2] maxima and denominators), used for
- *   causal attention over sequences of 4096 tokens or more.
+ *   causal attention over sequences of 2048 tokens or more.
  * dt: TP_BF16 only. d must be 64 or 128.
  * ---------------------------------------------------------------------------------------- */
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,

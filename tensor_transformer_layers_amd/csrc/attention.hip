@@ -512,12 +512,13 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
     const int n_qt = (p.seq + BQ - 1) / BQ;
     const int n_tiles = n_qt * p.batch * p.heads_local;
     dim3 grid((unsigned)(n_tiles * p.kv_split));
-    // Sets per workgroup: with the key-range split every query tile already has two
-    // workgroups, and one-set workgroups (64 KB of LDS, two per compute unit) overlap one
-    // workgroup's prologue and epilogue with the other's key loop: measured 2.5 us faster on
-    // the 4096-token layer step. Unsplit, two sets keep eight waves on every unit.
-    // TPSHARD_ATTN_SETS=1/2 overrides the choice (a test knob).
-    int nsets = p.kv_split == 2 ? 1 : 2;
+    // Sets per workgroup: with at least 512 workgroups (two per compute unit), one-set
+    // workgroups (64 KB of LDS) overlap one workgroup's prologue and epilogue with the other's
+    // key loop: 2.5 us faster on the 4096-token layer step (split), 57.7 against 61.0 us on
+    // 8 sequences of 2048 tokens with 4 local heads (unsplit, 512 query tiles). With fewer
+    // workgroups, two sets keep eight waves on every unit. TPSHARD_ATTN_SETS=1/2 overrides the
+    // choice (a test knob).
+    int nsets = grid.x >= 2 * 256 ? 1 : 2;
     if (const char* e = std::getenv("TPSHARD_ATTN_SETS")) {
         const int v = std::atoi(e);
         if (v == 1 || v == 2) nsets = v;
@@ -543,10 +544,10 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
 
 // The key-range split pays when the query tiles alone give fewer than two workgroups per
 // compute unit (256 on MI355X) and the causal tail is long: the longest query tiles then run
-// alone for a large share of the kernel. Measured at 256 query tiles: with 32 query tiles per
-// sequence (4096 tokens) the split plus the merge takes 74 us against 88 us unsplit; with 16
-// (2048 tokens) 48 us against 45 us, the merge costing more than the shorter tail saves. The
-// default is therefore: causal, under 512 query tiles, and at least 32 query tiles per
+// alone for a large share of the kernel. Measured at 256 query tiles, attention plus merge:
+// with 32 query tiles per sequence (4096 tokens) 74 us split against 88 us unsplit; with 16
+// (2048 tokens) 42.9 against 44.0 us once split workgroups run two per compute unit. The
+// default is therefore: causal, under 512 query tiles, and at least 16 query tiles per
 // sequence. The partials are reserved whenever there are under 512 query tiles (the workspace
 // size depends on the shapes only, not on the mask). TPSHARD_ATTN_SPLIT (read at launch) is a
 // test knob: 0 turns the split off, 2 forces it wherever the partials are reserved.
@@ -564,7 +565,7 @@ size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim
         else if (force == 2)
             *kv_split = split;
         else
-            *kv_split = causal && n_qt >= 32 ? split : 1;
+            *kv_split = causal && n_qt >= 16 ? split : 1;
     }
     if (split == 1) return 0;
     // two halves per query tile: output [128][d] and (max, denominator) [128][2], fp32

@@ -126,10 +126,11 @@ def test_attn_causal_first_row_is_projected_value():
         np.testing.assert_allclose(O[b * seq], v[b * seq], rtol=1e-2, atol=1e-2)
 
 
-@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "2")])
+@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "0")])
 def test_attn_full_size_shard_sampled_rows(rank, split, monkeypatch):
-    """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows; also
-    with the key-range split forced (at 4096 tokens per sequence it is the default)."""
+    """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows: the
+    default takes the key-range split (256 query tiles of 16 per sequence); also with the
+    split turned off (one two-set workgroup per query tile)."""
     if split:
         monkeypatch.setenv("TPSHARD_ATTN_SPLIT", split)
     w = WORKLOADS["attn_shard_bf16_b4_s2048_h4096_H32_n8"]
