@@ -34,6 +34,10 @@ tp_status ok()
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A GEMM tile addresses its 256 operand rows through one buffer descriptor (32-bit byte
+// offsets, range below 2 GiB), so a reduced (K) dimension is limited to 2^22 elements.
+constexpr int64_t kMaxReduced = int64_t(1) << 22;
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t dt_size(tp_dtype dt) { return dt == TP_F32 ? 4 : 2; }
@@ -83,6 +87,9 @@ tp_status validate_mlp_sizes(int64_t tokens, int64_t hidden, int64_t ffn, int n,
     if (hidden % 8 != 0 || (ffn / n) % 8 != 0)
         return fail(TP_ERR_ALIGN, "hidden=%lld and ffn/N=%lld must be multiples of 8",
                     (long long)hidden, (long long)(ffn / n));
+    if (hidden > kMaxReduced || ffn / n > kMaxReduced)
+        return fail(TP_ERR_SHAPE, "hidden=%lld and ffn/N=%lld must not exceed 2^22", (long long)hidden,
+                    (long long)(ffn / n));
     return TP_OK;
 }
 
@@ -133,6 +140,8 @@ tp_status validate_linear(int64_t rows, int64_t in_f, int64_t out_f, int n, int 
     if (k % 8 != 0 || w % 8 != 0)
         return fail(TP_ERR_ALIGN, "reduced dimension %lld and output width %lld must be multiples of 8",
                     (long long)k, (long long)w);
+    if (k > kMaxReduced)
+        return fail(TP_ERR_SHAPE, "reduced dimension %lld must not exceed 2^22", (long long)k);
     return TP_OK;
 }
 
@@ -182,6 +191,8 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
         return fail(TP_ERR_SHAPE, "batch, seq, hidden and n_heads must be >= 1");
     if (batch * seq > INT32_MAX || hidden > INT32_MAX)
         return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
+    if (hidden > kMaxReduced)
+        return fail(TP_ERR_SHAPE, "hidden=%lld must not exceed 2^22", (long long)hidden);
     if (hidden % n_heads != 0)
         return fail(TP_ERR_NOT_DIVISIBLE, "hidden=%lld not divisible by n_heads=%d", (long long)hidden,
                     n_heads);
@@ -289,7 +300,7 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
 size_t tp_mlp_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,
                                   tp_dtype dt)
 {
-    if (dt != TP_BF16) return 0;
+    if (dt != TP_BF16 || tokens > kMaxReduced) return 0;
     if (validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt) != TP_OK) return 0;
     return bwd_layout(tokens, hidden, ffn / n_shards).total;
 }
@@ -304,6 +315,8 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
     if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "the MLP backward supports TP_BF16 only (got %d)", (int)dt);
     tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
     if (st != TP_OK) return st;
+    if (tokens > kMaxReduced)   // dA and dB reduce over the tokens
+        return fail(TP_ERR_SHAPE, "tokens=%lld must not exceed 2^22 in the backward", (long long)tokens);
     if (rank < 0 || rank >= n_shards)
         return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
     if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(dZ) ||

@@ -73,6 +73,7 @@ def _swiglu(**kw):
     (dict(dt=F32), 5),                     # bf16 only
     (dict(Wup_i=P + 8), 6), (dict(hidden=8196), 6),
     (dict(workspace=None), 7), (dict(workspace_bytes=4096 * 3584 * 2 - 1), 7),
+    (dict(hidden=(1 << 22) + 8), 2),
 ])
 def test_swiglu_validation(kw, status):
     assert _swiglu(**kw) == status
@@ -119,6 +120,7 @@ def _attn(**kw):
     (dict(X=P + 8), 6), (dict(a_i=P + 4), 6), (dict(hidden=1020), 6),
     (dict(ffn=4096 + 2 * 4), 6),           # ffn/N = 2052 is not a multiple of 8
     (dict(workspace=None), 7), (dict(workspace_bytes=100), 7),
+    (dict(hidden=(1 << 22) + 8), 2),       # reduced dimension above 2^22 (32-bit tile offsets)
 ])
 def test_mlp_validation(kw, status):
     assert _mlp(**kw) == status
@@ -135,6 +137,7 @@ def test_mlp_validation(kw, status):
     (dict(bqkv_i=P + 2), 6),
     (dict(workspace_bytes=1), 7),
     (dict(seq=0), 2),
+    (dict(hidden=(1 << 22) + 4096), 2),   # reduced dimension of the QKV projection above 2^22
 ])
 def test_attn_validation(kw, status):
     assert _attn(**kw) == status
@@ -151,6 +154,8 @@ def test_mlp_bwd_validation_and_workspace():
     assert g(rank=9) == 4
     assert g(da_i=P + 4) == 6
     assert g(workspace_bytes=1024) == 7
+    assert g(tokens=(1 << 22) + 1) == 2        # dA and dB reduce over the tokens
+    assert B.tp_mlp_bwd_workspace_bytes((1 << 22) + 1, 8192, 32768, 8, BF16) == 0
     # P, dP [T, F/N]; B^T [F/N, h]; A^T [h, F/N]; dP^T, GeLU(P)^T [F/N, T8]; X^T, dZ^T [h, T8]
     T, h, fl = 4096, 8192, 4096
     want = 2 * (2 * T * fl + 2 * fl * h + 2 * fl * T + 2 * h * T)
