@@ -38,8 +38,8 @@
  *     non-OK status on the calling thread. Pointers must be 16-byte aligned; hidden,
  *     ffn / N and the head width must be multiples of 8 (16-byte rows); tokens and seq may
  *     be any value >= 1. A GEMM's reduced dimension (hidden, ffn / N; the tokens in the MLP
- *     backward) must not exceed 2^22 (TP_ERR_SHAPE): a tile's operand rows are addressed with
- *     32-bit byte offsets.
+ *     backward) and the attention's sequence length must not exceed 2^22 (TP_ERR_SHAPE): a
+ *     tile's operand rows, and a head's keys and values, are addressed with 32-bit offsets.
  *   - Precision: TP_BF16 inputs, weights and intermediates (Y_i, Q/K/V, head outputs) are
  *     bfloat16 rounded to nearest even, with fp32 accumulation; TP_F32 is fp32 throughout.
  *     Partials Z_i are always fp32.

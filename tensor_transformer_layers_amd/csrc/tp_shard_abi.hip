@@ -191,8 +191,9 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
         return fail(TP_ERR_SHAPE, "batch, seq, hidden and n_heads must be >= 1");
     if (batch * seq > INT32_MAX || hidden > INT32_MAX)
         return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
-    if (hidden > kMaxReduced)
-        return fail(TP_ERR_SHAPE, "hidden=%lld must not exceed 2^22", (long long)hidden);
+    if (hidden > kMaxReduced || seq > kMaxReduced)   // (each head's K and V^T: one descriptor too)
+        return fail(TP_ERR_SHAPE, "hidden=%lld and seq=%lld must not exceed 2^22", (long long)hidden,
+                    (long long)seq);
     if (hidden % n_heads != 0)
         return fail(TP_ERR_NOT_DIVISIBLE, "hidden=%lld not divisible by n_heads=%d", (long long)hidden,
                     n_heads);

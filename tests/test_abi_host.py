@@ -138,6 +138,7 @@ def test_mlp_validation(kw, status):
     (dict(workspace_bytes=1), 7),
     (dict(seq=0), 2),
     (dict(hidden=(1 << 22) + 4096), 2),   # reduced dimension of the QKV projection above 2^22
+    (dict(batch=1, seq=(1 << 22) + 1), 2),  # a head's keys past 32-bit offsets
 ])
 def test_attn_validation(kw, status):
     assert _attn(**kw) == status
