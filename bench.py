@@ -147,7 +147,7 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
     """
     import torch
     from synth import WORKLOADS
-    from tensor_transformer_layers_amd import shard
+    from tensor_transformer_layers_amd import binding, shard
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
     stream = torch.cuda.current_stream()
@@ -226,6 +226,45 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
                                          "call also recomputes P (one more GEMM) and transposes "
                                          "six operands"}
     del X, A_i, a_i, B_i, dZ, grads, ws
+    # all N shards of one MLP block, N in {1, 2, 4, 8}: how the shard's GEMM shape moves the
+    # MFMA utilisation (column GEMM T x F/N x h, row GEMM T x h x F/N), the whole block (every
+    # shard in turn, then the on-device sum) and the sum alone
+    w = WORKLOADS["mlp_block_bf16_t2048_h12288_f49152"]
+    T, h, F = w.tokens, w.hidden, w.ffn
+    X = rnd(T, h)
+    sweep = {}
+    for N in (1, 2, 4, 8):
+        fl = F // N
+        A_s = [rnd(fl, h, std=0.02) for _ in range(N)]
+        a_s = [rnd(fl, std=0.02) for _ in range(N)]
+        B_s = [rnd(h, fl, std=0.02) for _ in range(N)]
+        Zs = [torch.empty(T, h, device="cuda") for _ in range(N)]
+        Zsum = torch.empty(T, h, device="cuda")
+        ws = shard.mlp_workspace(T, h, F, N, torch.bfloat16)
+        shard_us = _time_events(lambda: shard.mlp_shard(X, A_s[0], a_s[0], B_s[0], N, 0, Z=Zs[0],
+                                                        workspace=ws), reps, warmup, stream)
+
+        def block():
+            for r in range(N):
+                shard.mlp_shard(X, A_s[r], a_s[r], B_s[r], N, r, Z=Zs[r], workspace=ws)
+            shard.sum_partials(Zs, out=Zsum)
+
+        block_us = _time_events(block, max(4, reps // N), 2, stream)
+        sum_us = _time_events(lambda: shard.sum_partials(Zs, out=Zsum), reps, warmup, stream)
+        fl_shard = 4.0 * T * h * fl
+        sum_bytes = (N + 1) * T * h * 4
+        _, cbm, cbn, _ = binding.tp_gemm_tile_info(T, fl, h)
+        _, rbm, rbn, _ = binding.tp_gemm_tile_info(T, h, fl)
+        sweep["N=%d" % N] = {
+            "shard_us": shard_us, "shard_tflops": fl_shard / shard_us / 1e6,
+            "shard_frac_bf16_peak": fl_shard / shard_us / 1e6 / PEAK_BF16_TFLOPS,
+            "column_gemm": "%dx%dx%d, tile %dx%d" % (T, fl, h, cbm, cbn),
+            "row_gemm": "%dx%dx%d, tile %dx%d" % (T, h, fl, rbm, rbn),
+            "block_us": block_us, "block_tflops": N * fl_shard / block_us / 1e6,
+            "sum_us": sum_us, "sum_gbs": sum_bytes / sum_us / 1e3}
+        del A_s, a_s, B_s, Zs, Zsum, ws
+    out["mlp_block_sweep"] = {"workload": w.name, "per_n": sweep}
+    del X
     torch.cuda.synchronize()
     return out
 
