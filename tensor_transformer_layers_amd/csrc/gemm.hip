@@ -133,15 +133,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Scheduling groups of one pipeline phase: after MFMA I come NR (I+1)/NM - NR I/NM fragment
-// reads and NV (I+1)/NM - NV I/NM slab loads, spreading both evenly between the phase's NM
-// MFMAs. Masks: 0x8 MFMA, 0x100 LDS read, 0x20 global read.
+// Scheduling groups of one pipeline phase: after MFMA I come up to three fragment reads
+// (front-loaded, so that the last read of the phase still has most of the phase's MFMAs to
+// land before the next phase waits on it) and NV (I+1)/NM - NV I/NM slab loads (spread evenly
+// between the phase's NM MFMAs). Masks: 0x8 MFMA, 0x100 LDS read, 0x20 global read.
 template <int I, int NM, int NR, int NV>
 struct InterleaveGroups {
     __device__ __forceinline__ static void emit()
     {
         if constexpr (I < NM) {
-            constexpr int nr = NR * (I + 1) / NM - NR * I / NM;
+            constexpr int nr = NR - 3 * I < 0 ? 0 : (NR - 3 * I > 3 ? 3 : NR - 3 * I);
             constexpr int nv = NV * (I + 1) / NM - NV * I / NM;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
@@ -358,18 +359,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     // fetch(k0 >= K) moves no memory (every offset is out of range) and zero-fills the
     // buffer: the loop issues it unconditionally so that the loads stay in the same basic
     // block as the MFMAs they are scheduled between.
-    auto fetch_vw = [&](int vw, int k0, int buf) {
+    auto fetch_vw_a = [&](int vw, int k0, int buf) {
         const bool kin = k0 + lchunk * 8 < p.K;
         const uint32_t kb = (uint32_t)k0 * 2u;
         const uint32_t dA = (uint32_t)((vw - wave) * 8 * p.lda) * 2u;
-        const uint32_t dB = (uint32_t)((vw - wave) * 8 * p.ldb) * 2u;
         bf16* sA = smem + buf * (BM + BN) * BK + vw * 8 * BK;
-        bf16* sB = smem + buf * (BM + BN) * BK + BM * BK + vw * 8 * BK;
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rA, (lds_ptr)(sA + i * 8 * NW * BK), 16,
                 kin ? offA + dA + i * stepA + kb : kOutOfRange, 0, 0, 0);
+    };
+    auto fetch_vw_b = [&](int vw, int k0, int buf) {
+        const bool kin = k0 + lchunk * 8 < p.K;
+        const uint32_t kb = (uint32_t)k0 * 2u;
+        const uint32_t dB = (uint32_t)((vw - wave) * 8 * p.ldb) * 2u;
+        bf16* sB = smem + buf * (BM + BN) * BK + BM * BK + vw * 8 * BK;
 #pragma unroll
         for (int i = 0; i < BCH; ++i) {
             if constexpr (GLU) {
@@ -388,6 +393,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
                     kin ? offB + dB + i * stepB + kb : kOutOfRange, 0, 0, 0);
             }
         }
+    };
+    auto fetch_vw = [&](int vw, int k0, int buf) {
+        fetch_vw_a(vw, k0, buf);
+        fetch_vw_b(vw, k0, buf);
     };
     // With 8 waves, the waves of the first half (one per SIMD) issue the slab loads of both
     // halves and the other four issue none: a wave whose load cannot enter the full address
@@ -511,7 +520,59 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if (!SPLIT_LOADS || wave_u < NW / 2)
+    // Four waves (one per SIMD, each a 128 x 128 block of the tile): a third fewer fragment
+    // reads per MFMA than the eight-wave layout, but no second wave on the SIMD to cover a
+    // read that has not landed. The fragments therefore go through four register sets, read
+    // well before their MFMAs. Iteration kt (slab kt in buffer kt & 1, its K-steps 0 and 1 in
+    // sets 0 and 1, slab kt+1's loads in flight):
+    //   read steps 2, 3 into sets 2, 3, MFMAs set 0 | MFMAs set 1 |
+    //   wait for slab kt+1, barrier (every wave is done with slab kt) |
+    //   read slab kt+1 steps 0, 1 into sets 0, 1, load slab kt+2's A part into buffer kt & 1,
+    //   MFMAs set 2 | load slab kt+2's B part, prefetch, MFMAs set 3.
+    // Every read has at least a full phase of MFMAs before it is waited on (reading one set
+    // per phase instead measured 2-3 % slower); the loads have a whole iteration to land.
+    auto k_loop_deep = [&]() {
+        bf16x8 ga[4][FM], gb[4][FN];
+        fetch_vw(wave_u, 0, 0);
+        __syncthreads();
+        read_frags(0, 0, ga[0], gb[0]);
+        read_frags(0, 1, ga[1], gb[1]);
+        fetch_vw(wave_u, BK, 1);
+        // issued after slab 1's loads, so that the first barrier's wait, which lets the PFI
+        // newest loads stay in flight, covers all of slab 1
+#pragma unroll
+        for (int d = 1; d < kPrefetchAhead; ++d) prefetch(d * BK);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur, 2, ga[2], gb[2]);
+            read_frags(cur, 3, ga[3], gb[3]);
+            mma(ga[0], gb[0]);
+            InterleaveGroups<0, NM, 2 * NR, 0>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+            mma(ga[1], gb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's loads of slab kt+1 have landed (its PFI newer prefetches may still be
+            // in flight) and its reads of slab kt are done; then the workgroup barrier
+            __builtin_amdgcn_s_waitcnt(0x0070 | PFI);   // vmcnt(PFI) expcnt(7) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cur ^ 1, 0, ga[0], gb[0]);   // after the last slab: zeros, unused
+            read_frags(cur ^ 1, 1, ga[1], gb[1]);
+            fetch_vw_a(wave_u, (kt + 2) * BK, cur);
+            mma(ga[2], gb[2]);
+            InterleaveGroups<0, NM, 2 * NR, ACH>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_vw_b(wave_u, (kt + 2) * BK, cur);
+            prefetch((kt + kPrefetchAhead) * BK);
+            mma(ga[3], gb[3]);
+            InterleaveGroups<0, NM, 0, BCH + PFI>::emit();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (NW == 4)
+        k_loop_deep();
+    else if (!SPLIT_LOADS || wave_u < NW / 2)
         k_loop(std::true_type{});
     else
         k_loop(std::false_type{});
