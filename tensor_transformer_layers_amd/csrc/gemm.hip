@@ -152,6 +152,23 @@ struct InterleaveGroups {
     }
 };
 
+// Scheduling groups of a phase whose fragment reads and slab loads are already interleaved
+// in program order (the compiler keeps LDS reads and LDS-DMA loads in that order, since it
+// cannot prove them disjoint): after MFMA I come NO (I+1)/NM - NO I/NM of the phase's NO
+// memory operations, of either kind. Mask 0x120: LDS read or global read.
+template <int I, int NM, int NO>
+struct MixedOps {
+    __device__ __forceinline__ static void emit()
+    {
+        if constexpr (I < NM) {
+            constexpr int no = NO * (I + 1) / NM - NO * I / NM;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (no > 0) __builtin_amdgcn_sched_group_barrier(0x120, no, 0);
+            MixedOps<I + 1, NM, NO>::emit();
+        }
+    }
+};
+
 // ---- bf16 kernels' output stage -----------------------------------------------------------
 // acc[i][j][4 q + v] of a wave holds C[r0 + 32 j + fr][c0 + 32 i + 8 q + 4 fg + v] (fr = lane & 31,
 // fg = lane >> 5). Stored as it lies, one 16-byte vector per lane would put the 32 lanes of an
@@ -522,51 +539,108 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     };
     // Four waves (one per SIMD, each a 128 x 128 block of the tile): a third fewer fragment
     // reads per MFMA than the eight-wave layout, but no second wave on the SIMD to cover a
-    // read that has not landed. The fragments therefore go through four register sets, read
-    // well before their MFMAs. Iteration kt (slab kt in buffer kt & 1, its K-steps 0 and 1 in
-    // sets 0 and 1, slab kt+1's loads in flight):
-    //   read steps 2, 3 into sets 2, 3, MFMAs set 0 | MFMAs set 1 |
+    // stall. Per-phase cycle counts show that fragment reads and slab loads cost almost
+    // nothing when each MFMA is followed by one or two of them, and stall the wave when they
+    // come in bursts (the LDS or the address queue fills). So the fragments go through four
+    // register sets, each read at least a phase before its MFMAs, and the phase's reads and
+    // loads are issued alternately, in program order, one or two after each MFMA; the slab
+    // loads are spread over three of the four phases, most of them in the two after the
+    // barrier (7/16 each), which leaves the loads issued before it the longest time to land.
+    // Iteration kt (slab kt in buffer
+    // kt & 1, its K-steps 0 and 1 in sets 0 and 1):
+    //   phase 0: MFMAs set 0 | read step 2 into set 2 and half of step 3 into set 3 + load
+    //            part 2 of slab kt+1 (into buffer kt+1 & 1), then the prefetch |
+    //   phase 1: MFMAs set 1 | early in the phase, the rest of step 3 |
     //   wait for slab kt+1, barrier (every wave is done with slab kt) |
-    //   read slab kt+1 steps 0, 1 into sets 0, 1, load slab kt+2's A part into buffer kt & 1,
-    //   MFMAs set 2 | load slab kt+2's B part, prefetch, MFMAs set 3.
-    // Every read has at least a full phase of MFMAs before it is waited on (reading one set
-    // per phase instead measured 2-3 % slower); the loads have a whole iteration to land.
+    //   phase 2: MFMAs set 2 | read slab kt+1 step 0 into set 0 + load part 0 of slab kt+2
+    //            into buffer kt & 1 |
+    //   phase 3: MFMAs set 3 | read slab kt+1 step 1 into set 1 + load part 1 of slab kt+2.
+    // The wait before the barrier lets only the prefetch, issued after part 2, stay in flight.
+    constexpr int LW4 = ACH + BCH;                       // slab loads per wave
+    constexpr int LP0 = (7 * LW4 + 8) / 16, LP1 = (7 * LW4 + 8) / 16, LP2 = LW4 - LP0 - LP1;
+    auto load_one = [&](int j, int k0, int buf) {   // j is a constant once unrolled
+        const uint32_t oob = (uint32_t)(k0 + lchunk * 8 >= p.K) << 31;
+        const uint32_t kb = (uint32_t)k0 * 2u;
+        bf16* sbuf = smem + buf * (BM + BN) * BK;
+        if (j < ACH) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rA, (lds_ptr)(sbuf + wave_u * 8 * BK + j * 8 * NW * BK), 16,
+                (offA + j * stepA + kb) | oob, 0, 0, 0);
+        } else {
+            const int i = j - ACH;
+            bf16* sB = sbuf + BM * BK + wave_u * 8 * BK + i * 8 * NW * BK;
+            if constexpr (GLU) {
+                const int gi = wave_u + i * NW;
+                const int blk = gi >> 2;
+                const uint32_t off = (uint32_t)(
+                    (((blk >> 1) * 32 + (gi & 3) * 8 + grp_row) * p.ldb + lchunk * 8) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds((blk & 1) ? rB2 : rB, (lds_ptr)sB, 16,
+                                                         (off + kb) | oob, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (lds_ptr)sB, 16, (offB + i * stepB + kb) | oob, 0, 0, 0);
+            }
+        }
+    };
+    // fragment idx of K-step ks: A fragments 0 .. FM-1, then B fragments
+    auto read_one = [&](int buf, int ks, int idx, bf16x8* fa, bf16x8* fb) {
+        const bf16* sA = smem + buf * (BM + BN) * BK;
+        const bf16* sB = sA + BM * BK;
+        const int ch = ks * 2 + fg;
+        if (idx < FM) {
+            const int r = wm * WTM + idx * 32 + fr;
+            fa[idx] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ ((r >> 1) & 7)) << 3));
+        } else {
+            const int r = wn * WTN + (idx - FM) * 32 + fr;
+            fb[idx - FM] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ ((r >> 1) & 7)) << 3));
+        }
+    };
     auto k_loop_deep = [&]() {
         bf16x8 ga[4][FM], gb[4][FN];
         fetch_vw(wave_u, 0, 0);
         __syncthreads();
         read_frags(0, 0, ga[0], gb[0]);
         read_frags(0, 1, ga[1], gb[1]);
-        fetch_vw(wave_u, BK, 1);
-        // issued after slab 1's loads, so that the first barrier's wait, which lets the PFI
-        // newest loads stay in flight, covers all of slab 1
 #pragma unroll
-        for (int d = 1; d < kPrefetchAhead; ++d) prefetch(d * BK);
+        for (int j = 0; j < LP0 + LP1; ++j) load_one(j, BK, 1);
         for (int kt = 0; kt < KT; ++kt) {
             const int cur = kt & 1;
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(cur, 2, ga[2], gb[2]);
-            read_frags(cur, 3, ga[3], gb[3]);
             mma(ga[0], gb[0]);
-            InterleaveGroups<0, NM, 2 * NR, 0>::emit();
+#pragma unroll
+            for (int t = 0; t < NR + NR / 2; ++t) {
+                const int set = 2 + t / NR;
+                read_one(cur, set, t % NR, ga[set], gb[set]);
+                if (t < LP2) load_one(LP0 + LP1 + t, (kt + 1) * BK, cur ^ 1);
+            }
+            prefetch((kt + kPrefetchAhead) * BK);
+            MixedOps<0, NM, NR + NR / 2 + LP2 + PFI>::emit();
             __builtin_amdgcn_sched_barrier(0);
             mma(ga[1], gb[1]);
+#pragma unroll
+            for (int t = NR / 2; t < NR; ++t) read_one(cur, 3, t, ga[3], gb[3]);
+            MixedOps<0, NM / 2, NR - NR / 2>::emit();
             __builtin_amdgcn_sched_barrier(0);
             // this wave's loads of slab kt+1 have landed (its PFI newer prefetches may still be
             // in flight) and its reads of slab kt are done; then the workgroup barrier
             __builtin_amdgcn_s_waitcnt(0x0070 | PFI);   // vmcnt(PFI) expcnt(7) lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(cur ^ 1, 0, ga[0], gb[0]);   // after the last slab: zeros, unused
-            read_frags(cur ^ 1, 1, ga[1], gb[1]);
-            fetch_vw_a(wave_u, (kt + 2) * BK, cur);
             mma(ga[2], gb[2]);
-            InterleaveGroups<0, NM, 2 * NR, ACH>::emit();
+#pragma unroll
+            for (int t = 0; t < NR || t < LP0; ++t) {
+                if (t < NR) read_one(cur ^ 1, 0, t, ga[0], gb[0]);   // after the last slab: zeros
+                if (t < LP0) load_one(t, (kt + 2) * BK, cur);
+            }
+            MixedOps<0, NM, NR + LP0>::emit();
             __builtin_amdgcn_sched_barrier(0);
-            fetch_vw_b(wave_u, (kt + 2) * BK, cur);
-            prefetch((kt + kPrefetchAhead) * BK);
             mma(ga[3], gb[3]);
-            InterleaveGroups<0, NM, 0, BCH + PFI>::emit();
+#pragma unroll
+            for (int t = 0; t < NR || t < LP1; ++t) {
+                if (t < NR) read_one(cur ^ 1, 1, t, ga[1], gb[1]);
+                if (t < LP1) load_one(LP0 + t, (kt + 2) * BK, cur);
+            }
+            MixedOps<0, NM, NR + LP1>::emit();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
