@@ -329,7 +329,9 @@ tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t bat
 
 /* ------------------------------------------------------------------------------------------
  * Which bf16 GEMM tile the library launches for C[M, N] = A[M, K] B[N, K]^T: block tile
- * rows x columns and waves per workgroup (honours the TPSHARD_GEMM_TILE override). A query
+ * rows x columns and waves per workgroup (honours the TPSHARD_GEMM_TILE override). The
+ * answer holds for every epilogue except the per-head Q/K/V scatter, which always runs eight
+ * waves per workgroup, and the gated (SwiGLU) product, which picks its own tile. A query
  * for profiling and tuning; it launches nothing. Returns TP_ERR_NULL / TP_ERR_SHAPE on bad
  * arguments.
  * ---------------------------------------------------------------------------------------- */

@@ -64,6 +64,15 @@ def test_mlp_backward_small(T, h, F, N):
         _compare(got, ref, "T=%d h=%d F=%d N=%d r=%d:" % (T, h, F, N, r))
 
 
+@pytest.mark.parametrize("tile", ["256x256w4", "128x128w4", "256x192"])
+@pytest.mark.parametrize("T,h,F,N", [(37, 200, 480, 2), (300, 264, 1040, 2)])
+def test_mlp_backward_small_forced_tiles(T, h, F, N, tile, monkeypatch):
+    """The same gradients with every GEMM of the call forced onto one tile layout (the
+    GeLU' epilogue and the fp32 products in the 4-wave layouts, on ragged shapes)."""
+    monkeypatch.setenv("TPSHARD_GEMM_TILE", tile)
+    test_mlp_backward_small(T, h, F, N)
+
+
 def test_mlp_backward_input_gradient_all_reduce():
     """The ranks' dX partials summed on the device = the unsharded block's dX."""
     torch = torch_cuda()
