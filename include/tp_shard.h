@@ -217,6 +217,10 @@ tp_status tp_swiglu_shard_fwd(const void* X, const void* Wgate_i, const void* Wu
  *   the fp32 partial results of the two key-range halves of every query tile
  *   ([tiles][2][128][d] outputs, then [tiles][2][128][2] maxima and denominators), used for
  *   causal attention over sequences of 2048 tokens or more.
+ *   When the projection's 256 x 256 output tiles (batch*seq by the local Q/K/V width) would
+ *   occupy at most 128 compute units and hidden >= 4096, it runs split along hidden into S
+ *   parts (S = min(4, 256 / tiles)); their fp32 partials [S][batch*seq][Q/K/V width] start
+ *   at O's offset (the size covers whichever of the two regions reaches further).
  * dt: TP_BF16 only. d must be 64 or 128.
  * ---------------------------------------------------------------------------------------- */
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
@@ -345,7 +349,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 8
+#define TP_SHARD_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

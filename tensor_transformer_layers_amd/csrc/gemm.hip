@@ -30,6 +30,7 @@
 // The MFMA is issued as D = B_frag * A_frag (weight rows as the "M" side), so each lane's
 // four accumulator values are four consecutive output COLUMNS of one row: epilogue stores
 // are 16-byte (fp32) or 8-byte (bf16) vectors, and the bias is one vector load.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -47,11 +48,11 @@ constexpr int kThreads = 256;
 // (block b runs on XCD b % 8); the remap gives each XCD a contiguous run of logical tiles,
 // and logical tiles are ordered in bands of kGroupM tile-rows so that blocks running at the
 // same time on one XCD share A rows and B columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn)
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn,
+                                            int bid = (int)blockIdx.x)
 {
     constexpr int kXcd = 8, kGroupM = 4;
     const int nb = tiles_m * tiles_n;
-    int bid = blockIdx.x;
     if (nb % kXcd == 0) bid = (bid % kXcd) * (nb / kXcd) + bid / kXcd;
     const int per_group = kGroupM * tiles_n;
     const int group = bid / per_group;
@@ -347,7 +348,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = ((GLU ? 2 * p.N : p.N) + BN - 1) / BN;
     int tm, tn;
-    tile_coords(tiles_m, tiles_n, tm, tn);
+    if (EPI == Epi::F32 && p.k_splits > 1) {
+        // group of blocks -> part of K: A, B and C move to the part, K to its length (a part
+        // past the end has length <= 0 and writes zeros)
+        const int tiles = tiles_m * tiles_n;
+        const int split = (int)blockIdx.x / tiles;
+        const int kc = ((p.K + p.k_splits - 1) / p.k_splits + BK - 1) / BK * BK;
+        const int kb = split * kc;
+        p.A = reinterpret_cast<const bf16*>(p.A) + kb;
+        p.B = reinterpret_cast<const bf16*>(p.B) + kb;
+        p.C = reinterpret_cast<float*>(p.C) + split * p.split_stride;
+        p.K = max(min(p.K - kb, kc), 0);
+        tile_coords(tiles_m, tiles_n, tm, tn, (int)blockIdx.x - split * tiles);
+    } else {
+        tile_coords(tiles_m, tiles_n, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int f0 = GLU ? n0 / 2 : n0;       // first B row (output feature) of the tile
 
@@ -988,7 +1003,8 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     const int ncols = epi == Epi::SwiGlu ? 2 * p.N : p.N;   // gate and up columns
     const int tiles = ((p.M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
-    dim3 grid(tiles), block(64 * WM * WN);
+    const int splits = epi == Epi::F32 && p.k_splits > 1 ? p.k_splits : 1;
+    dim3 grid(tiles * splits), block(64 * WM * WN);
 #define TPS_LAUNCH(E)                                                                        \
     if constexpr (S4)                                                                        \
         hipLaunchKernelGGL((gemm_bf16_s4_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);  \
@@ -1134,12 +1150,132 @@ hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         GemmTile o = t;
         bool ow4 = false, os4 = false;
         if (tile_override(o, ow4, os4) && glu_ok(o, ow4)) { t = o; w4 = ow4; s4 = os4; }
+    } else if (epi == Epi::F32 && p.k_splits > 1) {
+        // a K-split launch exists to fill the compute units with the largest tile; the
+        // 4-stage pipeline does not implement the split
+        t = GemmTile{256, 256};
+        tile_override(t, w4, s4);
+        s4 = false;
     } else {
         t = gemm_bf16_pick_tile(p.M, p.N, p.K);
         w4 = prefer_four_waves(p.M, p.N, p.K, t, epi);
         tile_override(t, w4, s4);
     }
     return s4 ? gemm_bf16_tile<true>(p, epi, s, t, w4) : gemm_bf16_tile<false>(p, epi, s, t, w4);
+}
+
+// A Q/K/V projection with few output columns (grouped-query attention: 4096 x 1280 x 8192
+// on a rank with 8 query and one key/value head) gives 80 tiles of 256 x 256 for 256 CUs,
+// and smaller tiles run at a much lower rate. Cutting K into S parts gives S times the
+// blocks; the parts' fp32 sums go through qkv_reduce_scatter. S = min(4, 256 / tiles) when
+// the tiles fill at most half of the CUs and K is at least 4096. TPSHARD_QKV_SPLIT (1 to 8)
+// overrides the count: a test knob (the workspace size follows it).
+int qkv_k_splits(int M, int N, int K)
+{
+    const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+    int s = 1;
+    if (2 * tiles <= 256 && K >= 4096) s = (int)std::min<long>(4, 256 / std::max<long>(tiles, 1));
+    if (const char* e = std::getenv("TPSHARD_QKV_SPLIT")) {
+        const int v = std::atoi(e);
+        if (v >= 1 && v <= 8) s = v;
+    }
+    return s;
+}
+
+namespace {
+
+// One block per 32 x 64 tile of the [M, N] projection. Each thread first sums 8 consecutive
+// columns of one row over the parts (in the fixed order 0, 1, ..., so the result does not
+// depend on timing), adds the bias, scales the query columns and stages them in LDS; then
+// query and key tiles leave as 8-column row chunks (one 16-byte store into a head's [seq, d]
+// row) and value tiles as 8-token column chunks of V^T when the sequence length is a
+// multiple of 8, else token by token. The query, key and value widths are multiples of 64,
+// so a tile never straddles two of them or two heads.
+constexpr int kRsRows = 32, kRsCols = 64;
+__global__ __launch_bounds__(256) void qkv_reduce_scatter_kernel(GemmProblem p, const float* parts)
+{
+    __shared__ float tile[kRsRows][kRsCols + 4];
+    const int tiles_n = p.N / kRsCols;
+    const int tr = (int)blockIdx.x / tiles_n, tc = (int)blockIdx.x - tr * tiles_n;
+    const int m0 = tr * kRsRows, n0 = tc * kRsCols;
+    const int t = threadIdx.x;
+    const int d = p.head_dim;
+    const int wq = p.heads_local * d, wkv = p.kv_heads_local * d;
+    {
+        const int r = t >> 3, c8 = (t & 7) * 8;
+        const int m = m0 + r, n = n0 + c8;
+        if (m < p.M) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < p.k_splits; ++sp) {
+                const float* src = parts + sp * p.split_stride + (int64_t)m * p.N + n;
+                a += *reinterpret_cast<const f32x4*>(src);
+                b += *reinterpret_cast<const f32x4*>(src + 4);
+            }
+            if (p.bias) {
+                const bf16* bias = reinterpret_cast<const bf16*>(p.bias) + n;
+                a += bf16x4_to_f32(*reinterpret_cast<const bf16x4*>(bias));
+                b += bf16x4_to_f32(*reinterpret_cast<const bf16x4*>(bias + 4));
+            }
+            if (n < wq) {
+                a *= p.q_scale;
+                b *= p.q_scale;
+            }
+            *reinterpret_cast<f32x4*>(&tile[r][c8]) = a;
+            *reinterpret_cast<f32x4*>(&tile[r][c8 + 4]) = b;
+        }
+    }
+    __syncthreads();
+    if (n0 < wq + wkv) {   // query or key columns
+        const int r = t >> 3, c8 = (t & 7) * 8;
+        const int m = m0 + r;
+        if (m >= p.M) return;
+        const int n = n0 + c8;
+        const int b = m / p.seq, sq = m - b * p.seq;
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf16(tile[r][c8 + e]);
+        bf16* dst;
+        if (n < wq) {
+            const int head = n / d, dd = n - head * d;
+            dst = reinterpret_cast<bf16*>(p.q) +
+                  (((int64_t)b * p.heads_local + head) * p.seq + sq) * d + dd;
+        } else {
+            const int nk = n - wq, head = nk / d, dd = nk - head * d;
+            dst = reinterpret_cast<bf16*>(p.k) +
+                  (((int64_t)b * p.kv_heads_local + head) * p.seq + sq) * d + dd;
+        }
+        *reinterpret_cast<bf16x8*>(dst) = v;
+    } else {               // value columns, transposed
+        const int c = t & 63, rc = (t >> 6) * 8;   // column, first of the chunk's 8 rows
+        const int nv = n0 + c - wq - wkv, head = nv / d, dd = nv - head * d;
+        bf16* vt = reinterpret_cast<bf16*>(p.vt);
+        const int m = m0 + rc;
+        if (p.seq % 8 == 0) {
+            if (m >= p.M) return;   // M is a multiple of seq, so the whole chunk is valid
+            const int b = m / p.seq, sq = m - b * p.seq;
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = bf16(tile[rc + e][c]);
+            *reinterpret_cast<bf16x8*>(
+                vt + (((int64_t)b * p.kv_heads_local + head) * d + dd) * p.ld_vt + sq) = v;
+        } else {
+            for (int e = 0; e < 8 && m + e < p.M; ++e) {
+                const int b = (m + e) / p.seq, sq = m + e - b * p.seq;
+                vt[(((int64_t)b * p.kv_heads_local + head) * d + dd) * p.ld_vt + sq] =
+                    bf16(tile[rc + e][c]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t qkv_reduce_scatter(const GemmProblem& p, const float* parts, hipStream_t s)
+{
+    if (p.N % kRsCols != 0 || p.k_splits < 1) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)((p.M + kRsRows - 1) / kRsRows) * (p.N / kRsCols);
+    hipLaunchKernelGGL(qkv_reduce_scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, parts);
+    return hipGetLastError();
 }
 
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)

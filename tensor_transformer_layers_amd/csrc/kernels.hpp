@@ -37,6 +37,11 @@ struct GemmProblem {
     int kv_heads_local;   // KVl
     int64_t ld_vt;
     float q_scale;        // factor on the query columns before rounding (the softmax's scale)
+    // F32 only: with k_splits > 1 the K range is cut into k_splits slab-aligned parts and the
+    // grid into as many groups of blocks; group s writes the partial product over its part to
+    // C + s * split_stride (elements). Zero or one: no split.
+    int k_splits;
+    int64_t split_stride;
 };
 
 // Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).
@@ -46,6 +51,13 @@ GemmTile gemm_bf16_pick_tile(int M, int N, int K);
 // Tile and wave count gemm_bf16 launches for this shape (after the environment override).
 GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves);
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t stream);
+// K-split count for the Q/K/V projection of an M x N x K shape (1: no split): > 1 when 256 x
+// 256 tiles would occupy at most half of the compute units.
+int qkv_k_splits(int M, int N, int K);
+// The split Q/K/V projection's second half: the sum of the k_splits fp32 partials at
+// parts + s * split_stride ([M, N], leading dimension N), plus the bias, the query columns
+// times q_scale, scattered per head like the Qkv epilogue (p supplies the layout).
+hipError_t qkv_reduce_scatter(const GemmProblem& p, const float* parts, hipStream_t stream);
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t stream);
 
 struct AttnProblem {

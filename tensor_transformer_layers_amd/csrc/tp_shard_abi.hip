@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -176,6 +177,8 @@ struct AttnLayout {
     int hl, kvl, d;
     int64_t ld_vt;
     size_t q, k, vt, o, part_o, part_ml, total;   // part_*: key-range-split partials (or none)
+    int qkv_splits;                               // K-split count of the Q/K/V projection
+    size_t qkv_part;                              // its fp32 partials (when qkv_splits > 1)
 };
 
 // n_kv_heads key/value heads (= n_heads for multi-head attention). A rank holds
@@ -225,6 +228,13 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
     L->part_o = o_end;
     L->part_ml = round_up(L->part_o + part_o_bytes, 256);
     L->total = part ? round_up(L->part_ml + (part - part_o_bytes), 256) : o_end;
+    // The split Q/K/V projection's partials [splits][T][N] fp32 share the space from O on:
+    // they are consumed by the scatter before the attention writes O or its own partials.
+    const int64_t T = batch * seq, ncol = (int64_t)(L->hl + 2 * L->kvl) * d;
+    L->qkv_splits = tps::qkv_k_splits((int)T, (int)ncol, (int)hidden);
+    L->qkv_part = L->o;
+    if (L->qkv_splits > 1)
+        L->total = std::max(L->total, round_up(L->o + (size_t)L->qkv_splits * T * ncol * 4, 256));
     return TP_OK;
 }
 
@@ -533,8 +543,24 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
     // The softmax's scale 1/sqrt(d), with log2(e) for its base-2 exponentials, is folded into
     // the stored queries (one rounding of the fp32 result either way).
     g.q_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
-    hipError_t e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
-    if (e != hipSuccess) return hip_status(e, "QKV projection launch");
+    hipError_t e;
+    if (L.qkv_splits > 1) {
+        // few output columns: the projection runs as K-split fp32 partials, then one pass
+        // sums them and applies the bias, the scale and the scatter
+        float* parts = reinterpret_cast<float*>(ws + L.qkv_part);
+        g.k_splits = L.qkv_splits;
+        g.split_stride = (int64_t)g.M * g.N;
+        tps::GemmProblem gp = g;
+        gp.bias = nullptr;
+        gp.C = parts; gp.ldc = g.N;
+        e = tps::gemm_bf16(gp, tps::Epi::F32, s);
+        if (e != hipSuccess) return hip_status(e, "QKV projection launch");
+        e = tps::qkv_reduce_scatter(g, parts, s);
+        if (e != hipSuccess) return hip_status(e, "QKV scatter launch");
+    } else {
+        e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
+        if (e != hipSuccess) return hip_status(e, "QKV projection launch");
+    }
     // 2. Head-local attention; heads concatenated locally into O_i.
     tps::AttnProblem a{};
     a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;

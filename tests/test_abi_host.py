@@ -190,6 +190,25 @@ def test_gqa_validation_and_layout():
             == B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16))
 
 
+def test_gqa_workspace_holds_the_split_projection(monkeypatch):
+    """4096 x 1280 x 8192 (8 query heads and one key/value head per rank) gives 80 tiles of
+    256 x 256: the projection is split three ways along K, and its fp32 partials
+    [3][4096][1280] take the space from O on (past the attention's own partials)."""
+    q, kv = 4096 * 8 * 128 * 2, 4096 * 1 * 128 * 2
+    o = q + 2 * kv
+    assert B.tp_gqa_attn_workspace_bytes(1, 4096, 8192, 64, 8, 8, BF16) == o + 3 * 4096 * 1280 * 4
+    # without the split: O, then the key-range halves' outputs and (max, denominator)
+    monkeypatch.setenv("TPSHARD_QKV_SPLIT", "1")
+    unsplit = o + 4096 * 1024 * 2 + 256 * 2 * 128 * 128 * 4 + 256 * 2 * 128 * 2 * 4
+    assert B.tp_gqa_attn_workspace_bytes(1, 4096, 8192, 64, 8, 8, BF16) == unsplit
+    # the multi-head layer shape (4096 x 3072 x 8192: 192 tiles) is not split
+    monkeypatch.delenv("TPSHARD_QKV_SPLIT")
+    st, off = B.tp_attn_workspace_layout(1, 4096, 8192, 64, 8, BF16)
+    assert st == 0
+    assert B.tp_attn_workspace_bytes(1, 4096, 8192, 64, 8, BF16) == (
+        off["o"] + 4096 * 1024 * 2 + 256 * 2 * 128 * 130 * 4)
+
+
 def test_sum_validation():
     assert B.tp_sum_partials([P, P], 0, 10, P, F32) == 2
     assert B.tp_sum_partials([P] * 65, 65, 10, P, F32) == 2

@@ -88,6 +88,13 @@ def test_attn_forced_key_range_split(case, monkeypatch):
     test_attn_small_every_step(case)
 
 
+@pytest.mark.parametrize("case", SMALL)
+def test_attn_qkv_k_split(case, monkeypatch):
+    """The multi-head shards with the Q/K/V projection forced through the K-split path."""
+    monkeypatch.setenv("TPSHARD_QKV_SPLIT", "3")
+    test_attn_small_every_step(case)
+
+
 @pytest.mark.parametrize("split,sets", [("2", "2"), ("0", "1")])
 @pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[3], SMALL[5]])
 def test_attn_other_set_counts(case, split, sets, monkeypatch):

@@ -70,6 +70,16 @@ def test_gqa_small_against_oracle(case):
         assert eo < TOL and ez < TOL
 
 
+@pytest.mark.parametrize("splits", ["2", "3"])
+@pytest.mark.parametrize("case", SMALL)
+def test_gqa_small_qkv_k_split(case, splits, monkeypatch):
+    """The same shards with the Q/K/V projection forced through the K-split path (fp32
+    partials, then the summing scatter): ragged sequences (value columns token by token),
+    d = 64, and parts that lie past the end of K (zeros)."""
+    monkeypatch.setenv("TPSHARD_QKV_SPLIT", splits)
+    test_gqa_small_against_oracle(case)
+
+
 def test_gqa_shards_sum_to_block():
     """Duplicated key/value heads: the ranks' partials still sum to the unsharded block."""
     torch = torch_cuda()
