@@ -1124,7 +1124,7 @@ static bool glu_ok(GemmTile t, bool w4)
     return (t.bm == 256 && t.bn == 256) || (t.bm == 256 && t.bn == 128);
 }
 
-static GemmTile glu_pick_tile(int M, int N, bool* w4)
+static GemmTile glu_pick_tile(int M, int N, int K, bool* w4)
 {
     // same cost model as gemm_bf16_pick_tile over the 2 N gate and up columns
     struct Cand { int bm, bn; bool w4; double cost; };
@@ -1137,6 +1137,11 @@ static GemmTile glu_pick_tile(int M, int N, bool* w4)
         const double t = (double)((tiles + 255) / 256) * c.bm * c.bn * c.cost;
         if (t < best_t - 1e-9) { best_t = t; best = GemmTile{c.bm, c.bn}; bw4 = c.w4; }
     }
+    // 256 x 256 with more than one tile per CU and a long K loop: four waves (the gated MLP
+    // shard 4096 x 8192 x 28672, 448 gate/up tiles: 656 against 671 us for the whole shard)
+    if (best.bm == 256 && best.bn == 256 && K >= 2048 &&
+        (long)((M + 255) / 256) * ((2L * N + 255) / 256) > 256)
+        bw4 = true;
     *w4 = bw4;
     return best;
 }
@@ -1146,7 +1151,7 @@ hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
     bool w4 = false, s4 = false;
     GemmTile t;
     if (epi == Epi::SwiGlu) {
-        t = glu_pick_tile(p.M, p.N, &w4);
+        t = glu_pick_tile(p.M, p.N, p.K, &w4);
         GemmTile o = t;
         bool ow4 = false, os4 = false;
         if (tile_override(o, ow4, os4) && glu_ok(o, ow4)) { t = o; w4 = ow4; s4 = os4; }
