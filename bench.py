@@ -297,8 +297,8 @@ def main() -> int:
         log("copied 5 x 256 MiB")
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs every tensor-parallel shard on a "
-              "single device (the all-reduce is an on-device sum), so --gpus must be 1.",
+        print("bench.py measures one GPU: every tensor-parallel shard runs on a single device "
+              "(the all-reduce is an on-device sum), so --gpus must be 1.",
               file=sys.stderr)
         return 2
 
