@@ -253,13 +253,13 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
         sum_us = _time_events(lambda: shard.sum_partials(Zs, out=Zsum), reps, warmup, stream)
         fl_shard = 4.0 * T * h * fl
         sum_bytes = (N + 1) * T * h * 4
-        _, cbm, cbn, _ = binding.tp_gemm_tile_info(T, fl, h)
-        _, rbm, rbn, _ = binding.tp_gemm_tile_info(T, h, fl)
+        _, cbm, cbn, cw = binding.tp_gemm_tile_info(T, fl, h)
+        _, rbm, rbn, rw = binding.tp_gemm_tile_info(T, h, fl)
         sweep["N=%d" % N] = {
             "shard_us": shard_us, "shard_tflops": fl_shard / shard_us / 1e6,
             "shard_frac_bf16_peak": fl_shard / shard_us / 1e6 / PEAK_BF16_TFLOPS,
-            "column_gemm": "%dx%dx%d, tile %dx%d" % (T, fl, h, cbm, cbn),
-            "row_gemm": "%dx%dx%d, tile %dx%d" % (T, h, fl, rbm, rbn),
+            "column_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, fl, h, cbm, cbn, cw),
+            "row_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, h, fl, rbm, rbn, rw),
             "block_us": block_us, "block_tflops": N * fl_shard / block_us / 1e6,
             "sum_us": sum_us, "sum_gbs": sum_bytes / sum_us / 1e3}
         del A_s, a_s, B_s, Zs, Zsum, ws

@@ -247,9 +247,19 @@ def test_workspace_sizes():
     assert B.tp_attn_workspace_bytes(1, 5, 256, 2, 1, F32) == 0
 
 
-def test_gemm_tile_info():
+def test_gemm_tile_info(monkeypatch):
+    monkeypatch.delenv("TPSHARD_GEMM_TILE", raising=False)
     st, bm, bn, w = B.tp_gemm_tile_info(4096, 4096, 8192)
-    assert st == 0 and (bm, bn, w) == (256, 256, 8)
+    assert st == 0 and (bm, bn, w) == (256, 256, 8)      # one tile per CU: eight waves
     st, bm, bn, w = B.tp_gemm_tile_info(4096, 3072, 8192)
     assert st == 0 and (bm, bn) == (256, 192)
+    # 256 x 256 with two or more tiles per CU and K >= 2048: four waves
+    assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 4)
+    assert B.tp_gemm_tile_info(8192, 8192, 8192)[1:] == (256, 256, 4)
+    assert B.tp_gemm_tile_info(4096, 8192, 1024)[1:] == (256, 256, 8)   # short K
+    # the override names the layout
+    monkeypatch.setenv("TPSHARD_GEMM_TILE", "256x256")
+    assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 8)
+    monkeypatch.setenv("TPSHARD_GEMM_TILE", "128x128w4")
+    assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (128, 128, 4)
     assert B.tp_gemm_tile_info(0, 1, 1)[0] == 2
