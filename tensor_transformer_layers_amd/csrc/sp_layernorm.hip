@@ -22,7 +22,9 @@
 namespace tps {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // all-gather workgroup
+constexpr int kRowThreads = 1024;  // boundary workgroup: one slice row, two vectors per lane at
+                                   // hidden 8192 (256 lanes left 8 dependent rounds per lane)
 constexpr int kMaxParts = 64;
 
 struct Parts {
@@ -47,7 +49,8 @@ __device__ __forceinline__ void store4(void* base, int64_t i4, f32x4 v)
         reinterpret_cast<f32x4*>(base)[i4] = v;
 }
 
-// Sum of v over the workgroup (256 lanes = 4 waves); every lane receives the result.
+// Sum of v over the boundary workgroup (kRowThreads lanes); every lane receives the result,
+// the waves' partial sums added in a fixed order.
 __device__ __forceinline__ float block_sum(float v, float* red)
 {
 #pragma unroll
@@ -56,12 +59,15 @@ __device__ __forceinline__ float block_sum(float v, float* red)
     __syncthreads();   // red may still be read by the previous call
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / 64; ++w) s += red[w];
+    return s;
 }
 
 // NP > 0: compile-time partial count; NP == 0: runtime n.
 template <int NP, bool BF16, bool LN>
-__global__ __launch_bounds__(kThreads) void sp_boundary_kernel(Parts parts, int n,
+__global__ __launch_bounds__(kRowThreads) void sp_boundary_kernel(Parts parts, int n,
                                                                const void* resid,
                                                                const float* gamma,
                                                                const float* beta, float eps,
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void sp_boundary_kernel(Parts parts, int 
                                                                int seq_r, int rank, int hidden)
 {
     extern __shared__ __attribute__((aligned(16))) float row[];   // [hidden] when LN
-    __shared__ float red[4];
+    __shared__ float red[kRowThreads / 64];
     const int np = NP > 0 ? NP : n;
     const int i = blockIdx.x;                  // slice row
     const int b = i / seq_r, sp = i - b * seq_r;
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void sp_boundary_kernel(Parts parts, int 
     const int h4 = hidden / 4;
     const int64_t src4 = t * h4, dst4 = (int64_t)i * h4;
     float sum = 0.f;
-    for (int v = threadIdx.x; v < h4; v += kThreads) {
+    for (int v = threadIdx.x; v < h4; v += kRowThreads) {
         f32x4 acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + src4 + v);
         if constexpr (NP > 0) {
 #pragma unroll
@@ -97,13 +103,13 @@ __global__ __launch_bounds__(kThreads) void sp_boundary_kernel(Parts parts, int 
     if constexpr (LN) {
         const float mean = block_sum(sum, red) / (float)hidden;   // block_sum syncs the row too
         float sq = 0.f;
-        for (int v = threadIdx.x; v < h4; v += kThreads) {
+        for (int v = threadIdx.x; v < h4; v += kRowThreads) {
             const f32x4 d = *reinterpret_cast<const f32x4*>(row + 4 * v) - mean;
             sq += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
         }
         const float var = block_sum(sq, red) / (float)hidden;
         const float inv = 1.0f / __builtin_sqrtf(var + eps);
-        for (int v = threadIdx.x; v < h4; v += kThreads) {
+        for (int v = threadIdx.x; v < h4; v += kRowThreads) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(row + 4 * v);
             const f32x4 g = reinterpret_cast<const f32x4*>(gamma)[v];
             const f32x4 be = reinterpret_cast<const f32x4*>(beta)[v];
@@ -122,14 +128,22 @@ __global__ __launch_bounds__(kThreads) void all_gather_rows_kernel(Parts slices,
     const int r = s / seq_r, sp = s - r * seq_r;
     const u32x4* src = reinterpret_cast<const u32x4*>(slices.p[r]) + ((int64_t)b * seq_r + sp) * row16;
     u32x4* dst = reinterpret_cast<u32x4*>(out) + (int64_t)t * row16;
-    for (int64_t v = threadIdx.x; v < row16; v += kThreads)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+    // four vectors per round, all loads before the stores (so they are in flight together)
+    for (int64_t v0 = threadIdx.x; v0 < row16; v0 += 4 * kThreads) {
+        u32x4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (v0 + u * kThreads < row16) x[u] = __builtin_nontemporal_load(src + v0 + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (v0 + u * kThreads < row16) __builtin_nontemporal_store(x[u], dst + v0 + u * kThreads);
+    }
 }
 
 template <int NP, bool BF16>
 void launch_np(const Parts& pp, int n, const SpProblem& p, hipStream_t s)
 {
-    const dim3 grid((unsigned)((int64_t)p.batch * (p.seq / n))), block(kThreads);
+    const dim3 grid((unsigned)((int64_t)p.batch * (p.seq / n))), block(kRowThreads);
     const int seq_r = p.seq / n;
     if (p.gamma) {
         const size_t lds = (size_t)p.hidden * sizeof(float);
