@@ -472,18 +472,36 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnProblem p)
     const int64_t item0 = ((int64_t)bh * n_qt + qt) * 2;
     const int64_t ldo = (int64_t)p.heads_local * D;
     bf16* __restrict__ gO = reinterpret_cast<bf16*>(p.o);
-    for (int e = threadIdx.x; e < rows * (D / 4); e += 256) {
-        const int r = r0 + e / (D / 4), c4 = e % (D / 4);
-        const float2 ml0 = *reinterpret_cast<const float2*>(p.part_ml + (item0 * BQ + r) * 2);
-        const float2 ml1 = *reinterpret_cast<const float2*>(p.part_ml + ((item0 + 1) * BQ + r) * 2);
-        const float m = fmaxf(ml0.x, ml1.x);
-        const float a0 = ml0.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml0.x - m);
-        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - m);
-        const float inv = 1.0f / (ml0.y * a0 + ml1.y * a1);
-        const f32x4 o0 = *reinterpret_cast<const f32x4*>(p.part_o + (item0 * BQ + r) * D + 4 * c4);
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(p.part_o + ((item0 + 1) * BQ + r) * D + 4 * c4);
-        *reinterpret_cast<bf16x4*>(gO + ((int64_t)b * p.seq + q0 + r) * ldo + head * D + 4 * c4) =
-            to_bf16x4((o0 * a0 + o1 * a1) * inv);
+    // two vectors per lane and round, all loads before the stores
+    constexpr int U = 2;
+    const int n_e = rows * (D / 4);
+    for (int e0 = threadIdx.x; e0 < n_e; e0 += U * 256) {
+        float2 ml0[U], ml1[U];
+        f32x4 o0[U], o1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * 256;
+            if (e < n_e) {
+                const int r = r0 + e / (D / 4), c4 = e % (D / 4);
+                ml0[u] = *reinterpret_cast<const float2*>(p.part_ml + (item0 * BQ + r) * 2);
+                ml1[u] = *reinterpret_cast<const float2*>(p.part_ml + ((item0 + 1) * BQ + r) * 2);
+                o0[u] = *reinterpret_cast<const f32x4*>(p.part_o + (item0 * BQ + r) * D + 4 * c4);
+                o1[u] = *reinterpret_cast<const f32x4*>(p.part_o + ((item0 + 1) * BQ + r) * D + 4 * c4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * 256;
+            if (e < n_e) {
+                const int r = r0 + e / (D / 4), c4 = e % (D / 4);
+                const float m = fmaxf(ml0[u].x, ml1[u].x);
+                const float a0 = ml0[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml0[u].x - m);
+                const float a1 = ml1[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1[u].x - m);
+                const float inv = 1.0f / (ml0[u].y * a0 + ml1[u].y * a1);
+                *reinterpret_cast<bf16x4*>(gO + ((int64_t)b * p.seq + q0 + r) * ldo + head * D +
+                                           4 * c4) = to_bf16x4((o0[u] * a0 + o1[u] * a1) * inv);
+            }
+        }
     }
 }
 

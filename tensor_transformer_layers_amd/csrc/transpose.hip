@@ -79,7 +79,18 @@ __global__ __launch_bounds__(kThreads) void row_sum_kernel(const bf16* __restric
     const int r = blockIdx.x;
     const bf16* row = in + (int64_t)r * ld;
     float s = 0.f;
-    for (int c = threadIdx.x; c < cols; c += kThreads) s += static_cast<float>(row[c]);
+    if (ld % 8 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0) {
+        // 16-byte rows: 8 values per load (2-byte loads left the kernel at 2.4 TB/s)
+        const int c8 = cols / 8 * 8;
+        for (int c = threadIdx.x * 8; c < c8; c += kThreads * 8) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += static_cast<float>(v[e]);
+        }
+        for (int c = c8 + threadIdx.x; c < cols; c += kThreads) s += static_cast<float>(row[c]);
+    } else {
+        for (int c = threadIdx.x; c < cols; c += kThreads) s += static_cast<float>(row[c]);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
