@@ -1,0 +1,61 @@
+"""Host-side checks of the benchmark's bookkeeping (no GPU): the algorithmic FLOP count of the
+layer step, the counter-summary lookup and its source-hash guard, and the single-GPU refusal."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synth import WORKLOADS  # noqa: E402
+
+LAYER = "layer_shard_bf16_b1_s4096_h8192_H64_f32768_n8"
+
+
+def test_layer_step_flops():
+    # rank 0 of N = 8 at hidden 8192, 64 heads of 128, ffn 32768, one causal sequence of 4096:
+    # 8 local heads (1024 columns), ffn shard 4096; attention counts the s(s+1)/2 triangle.
+    fl = bench.stage_flops(WORKLOADS[LAYER])
+    assert fl["qkv_projection"] == 206_158_430_208        # 2 x 4096 x 8192 x 3072
+    assert fl["out_projection"] == 68_719_476_736         # 2 x 4096 x 1024 x 8192
+    assert fl["mlp_column"] == 274_877_906_944            # 2 x 4096 x 8192 x 4096
+    assert fl["mlp_row"] == 274_877_906_944
+    assert fl["attention"] == 34_368_126_976              # 4 x 128 x 8390656 x 8
+    assert sum(fl.values()) == 859_001_847_808
+
+
+def test_traffic_lookup_and_hash_guard(monkeypatch):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        pytest.skip("no committed counter summary")
+    rec = json.load(open(path))
+    name, k = next((n, k) for n, k in rec["kernels"].items() if k["stage"] == "mlp_column")
+    kernel = name.split(" [")[0]
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: rec["source_sha"])
+    assert bench.traffic_for(kernel, "mlp_column") == k["hbm_bytes_per_launch"]
+    assert bench.traffic_for(kernel, "mlp_row") is None       # the column kernel, other stage
+    assert bench.traffic_for("no_such_kernel<1>", "mlp_column") is None
+    # other kernel sources: the figures no longer describe the library, so none is reported
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
+    assert bench.traffic_for(kernel, "mlp_column") is None
+
+
+def test_source_hash_covers_the_kernel_sources():
+    h = bench.kernel_source_sha()
+    assert len(h) == 16 and int(h, 16) >= 0
+    assert h == bench.kernel_source_sha()
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv, env=e,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus must be 1" in r.stderr
+    assert r.stdout == ""
