@@ -1084,7 +1084,8 @@ static bool tile_override(GemmTile& t, bool& w4, bool& s4)
 // 4096 x 8192 x 4096 (512 tiles) 1300 against 1267 TFLOP/s, 8192^3 1343 against 1314; one
 // tile per CU (4096 x 4096 x 8192) 1226 against 1260. In the layer step: the MLP row GEMM
 // 233 against 239 us, but the output projection (K = 1024) 3 us slower. The Qkv scatter
-// keeps eight waves (its 4-wave build spills).
+// keeps eight waves: its 4-wave build measured slower at 768 tiles (16384 x 3072 x 8192: 799
+// against 691 us) as at one tile per CU (4096 x 3072 x 8192, 256 x 192: 219 against 195 us).
 static bool prefer_four_waves(int M, int N, int K, GemmTile t, Epi epi)
 {
     if (t.bm != 256 || t.bn != 256 || epi == Epi::Qkv || K < 2048) return false;
