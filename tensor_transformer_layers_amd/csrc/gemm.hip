@@ -1086,10 +1086,12 @@ static bool tile_override(GemmTile& t, bool& w4, bool& s4)
 // 233 against 239 us, but the output projection (K = 1024) 3 us slower. The Qkv scatter
 // keeps eight waves: its 4-wave build measured slower at 768 tiles (16384 x 3072 x 8192: 799
 // against 691 us) as at one tile per CU (4096 x 3072 x 8192, 256 x 192: 219 against 195 us).
+// 256 x 192 tiles follow the same rule: on the MLP block's row GEMMs (512 tiles) 2381 against
+// 2500 us at 2048 x 12288 x 49152 and 1068 against 1175 us at K = 24576.
 static bool prefer_four_waves(int M, int N, int K, GemmTile t, Epi epi)
 {
-    if (t.bm != 256 || t.bn != 256 || epi == Epi::Qkv || K < 2048) return false;
-    const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+    if (t.bm != 256 || (t.bn != 256 && t.bn != 192) || epi == Epi::Qkv || K < 2048) return false;
+    const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     return tiles >= 512;
 }
 

@@ -257,6 +257,10 @@ def test_gemm_tile_info(monkeypatch):
     assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 4)
     assert B.tp_gemm_tile_info(8192, 8192, 8192)[1:] == (256, 256, 4)
     assert B.tp_gemm_tile_info(4096, 8192, 1024)[1:] == (256, 256, 8)   # short K
+    # 256 x 192 tiles likewise: the MLP block's row GEMM at N = 1 and 2 (512 tiles)
+    assert B.tp_gemm_tile_info(2048, 12288, 49152)[1:] == (256, 192, 4)
+    assert B.tp_gemm_tile_info(2048, 12288, 24576)[1:] == (256, 192, 4)
+    assert B.tp_gemm_tile_info(4096, 3072, 8192)[1:] == (256, 192, 8)    # 256 tiles
     # the override names the layout
     monkeypatch.setenv("TPSHARD_GEMM_TILE", "256x256")
     assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 8)

@@ -64,7 +64,7 @@ def test_mlp_backward_small(T, h, F, N):
         _compare(got, ref, "T=%d h=%d F=%d N=%d r=%d:" % (T, h, F, N, r))
 
 
-@pytest.mark.parametrize("tile", ["256x256w4", "128x128w4", "256x192"])
+@pytest.mark.parametrize("tile", ["256x256w4", "128x128w4", "256x192", "256x192w4"])
 @pytest.mark.parametrize("T,h,F,N", [(37, 200, 480, 2), (300, 264, 1040, 2)])
 def test_mlp_backward_small_forced_tiles(T, h, F, N, tile, monkeypatch):
     """The same gradients with every GEMM of the call forced onto one tile layout (the
