@@ -438,3 +438,44 @@ def test_bf16_workload_inputs_are_bf16_exact():
     # RNE: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
     x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -1 - 2.0 ** -8], dtype=np.float32)
     assert list(bf16_round(x)) == [1.0, 1 + 2.0 ** -6, -1.0]
+
+
+# --------------------------------------------------------------------------------------
+# The parity metric: relative Frobenius error ||got - ref||_F / ||ref||_F over the whole
+# tensor (the acceptance test every GPU parity assertion goes through)
+# --------------------------------------------------------------------------------------
+def test_rel_frobenius_hand_computed_values():
+    # ref (3, 4) has norm 5; got differs by (0, 1/2): 0.5 / 5 = 0.1 exactly. The squared
+    # ratio would give 0.01, and ||got|| in the denominator 0.5 / sqrt(29.25) = 0.0925.
+    assert oracle.rel_frobenius([3.0, 4.5], [3.0, 4.0]) == pytest.approx(0.1, rel=1e-15, abs=0)
+    assert abs(oracle.rel_frobenius([3.0, 4.5], [3.0, 4.0]) - 0.1) < 1e-16
+    # The denominator is the reference's norm, not the result's: the error of an all-zero
+    # result is exactly 1, and swapping the arguments changes the value.
+    assert oracle.rel_frobenius([0.0, 0.0], [3.0, 4.0]) == 1.0
+    assert oracle.rel_frobenius([6.0, 8.0], [3.0, 4.0]) == 1.0
+    assert oracle.rel_frobenius([3.0, 4.0], [6.0, 8.0]) == 0.5
+    # Negated result: ||2 ref|| / ||ref|| = 2 (a sum instead of a difference gives 0).
+    assert oracle.rel_frobenius([-3.0, -4.0], [3.0, 4.0]) == 2.0
+
+
+def test_rel_frobenius_is_over_the_whole_tensor():
+    # ref [[1, 2], [2, 4]] has Frobenius norm 5; got differs in one element by 3: 3 / 5.
+    # Row-wise variants differ: the worst row gives 3 / sqrt(20) = 0.671, the mean of the
+    # rows' errors 0.335, the largest element error over the largest element 0.75.
+    ref = np.array([[1.0, 2.0], [2.0, 4.0]])
+    got = np.array([[1.0, 2.0], [2.0, 1.0]])
+    assert abs(oracle.rel_frobenius(got, ref) - 0.6) < 1e-15
+    # shape-agnostic: the same 4 numbers flattened or transposed give the same value
+    assert oracle.rel_frobenius(got.ravel(), ref.ravel()) == oracle.rel_frobenius(got, ref)
+    assert oracle.rel_frobenius(got.T, ref.T) == oracle.rel_frobenius(got, ref)
+
+
+def test_rel_frobenius_is_computed_in_fp64():
+    # A 1e-9 relative difference on 2^20 fp32-exact elements: in fp64 the metric returns it
+    # to 1e-6 relative; an fp32 computation of the difference would round it away (each
+    # element's difference is below half an fp32 ulp of the values).
+    n = 1 << 20
+    ref = np.full(n, 1.0, dtype=np.float64)
+    got = ref + 1e-9
+    assert abs(oracle.rel_frobenius(got, ref) - 1e-9) < 1e-15
+    assert oracle.rel_frobenius(got.astype(np.float32), ref.astype(np.float32)) == 0.0
