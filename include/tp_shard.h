@@ -38,8 +38,9 @@
  *     non-OK status on the calling thread. Pointers must be 16-byte aligned; hidden,
  *     ffn / N and the head width must be multiples of 8 (16-byte rows); tokens and seq may
  *     be any value >= 1. A GEMM's reduced dimension (hidden, ffn / N; the tokens in the MLP
- *     backward) and the attention's sequence length must not exceed 2^22 (TP_ERR_SHAPE): a
- *     tile's operand rows, and a head's keys and values, are addressed with 32-bit offsets.
+ *     backward) must be below 2^22 and the attention's sequence length at most 2^22
+ *     (TP_ERR_SHAPE): a tile's operand rows, and a head's keys and values, are addressed with
+ *     32-bit offsets below 2^31.
  *   - Precision: TP_BF16 inputs, weights and intermediates (Y_i, Q/K/V, head outputs) are
  *     bfloat16 rounded to nearest even, with fp32 accumulation; TP_F32 is fp32 throughout.
  *     Partials Z_i are always fp32.
@@ -69,7 +70,8 @@ typedef enum {
     TP_ERR_ALIGN = 6,          /* pointer not 16-byte aligned or row width not 8-multiple */
     TP_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than *_workspace_bytes()       */
     TP_ERR_HIP = 8,            /* a HIP runtime call or kernel launch failed               */
-    TP_ERR_DEVICE = 9          /* the current device is not gfx950                         */
+    TP_ERR_DEVICE = 9,         /* the current device is not gfx950                         */
+    TP_ERR_ALIAS = 10          /* an output shares memory with an input it may not alias  */
 } tp_status;
 
 typedef enum {
@@ -280,7 +282,9 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
  *   Z_parts  HOST array of n_parts DEVICE pointers, each [numel] fp32, 16-byte aligned;
  *            a NULL entry is a missing rank (TP_ERR_NULL).
  *   n_parts  1 ... 64
- *   Z        [numel] out_dt; may alias Z_parts[0], no other aliasing.
+ *   Z        [numel] out_dt. An fp32 Z may be one of the partials itself (the same
+ *            pointer: each element is read from every partial before it is written); any
+ *            other overlap with a partial, and every overlap of a bf16 Z, is TP_ERR_ALIAS.
  * ---------------------------------------------------------------------------------------- */
 tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel,
                           void* Z, tp_dtype out_dt, void* stream);
@@ -315,7 +319,8 @@ tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t nume
  * tp_all_gather_rows:  X[t] = slices[r(t)][i(t)]
  *   slices  HOST array of n_parts DEVICE pointers, each [batch*seq/N, hidden] dt
  *   X       [batch*seq, hidden] dt
- * No output may alias an input. Errors as for the other calls; seq % N != 0 is
+ * No output may share memory with an input or with the other output (TP_ERR_ALIAS; H_r
+ * may be residual_r itself). Errors as for the other calls; seq % N != 0 is
  * TP_ERR_NOT_DIVISIBLE (the pages only use exact slices).
  * ---------------------------------------------------------------------------------------- */
 tp_status tp_reduce_scatter_partials(const float* const* Z_parts, int n_parts, int64_t batch,
@@ -333,7 +338,7 @@ tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t bat
 
 /* ------------------------------------------------------------------------------------------
  * Which bf16 GEMM tile the library launches for C[M, N] = A[M, K] B[N, K]^T: block tile
- * rows x columns and waves per workgroup (honours the TPSHARD_GEMM_TILE override). The
+ * rows x columns and waves per workgroup (honours the gemm_tile test override). The
  * answer holds for every epilogue except the per-head Q/K/V scatter, which always runs eight
  * waves per workgroup, and the gated (SwiGLU) product, which picks its own tile. A query
  * for profiling and tuning; it launches nothing. Returns TP_ERR_NULL / TP_ERR_SHAPE on bad
@@ -342,6 +347,25 @@ tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t bat
 tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* tile_n,
                             int* waves);
 
+/* ------------------------------------------------------------------------------------------
+ * Test and tuning hook, for callers that need every launch variant exercised (the library's
+ * tests): forces launch choices that are otherwise made per shape. Not part of any passage of
+ * the method; results stay within the documented precision whatever is forced.
+ *   spec  NULL or "" restores the library's own choices; otherwise a comma-separated list of
+ *         key=value items, each replacing one choice (the list replaces every earlier one):
+ *           gemm_tile=<bm>x<bn>[w4]   bf16 GEMM tile 256x256, 256x192, 256x128 or 128x128,
+ *                                     "w4": four waves per workgroup instead of eight
+ *           qkv_split=1..8            K-split count of the Q/K/V projection
+ *           attn_sets=1|2             attention wave sets per workgroup
+ *           attn_split=1|2            key-range split of the attention off (1) or forced (2)
+ *           sum_grid=<n>              partial-sum workgroups (0: one lane per vector)
+ *           sum_unroll=1|2|4          partial-sum vectors per lane
+ * The setting is process-wide and applies to launches (and workspace sizes) from then on;
+ * set it while no other thread is calling the library. TP_ERR_SHAPE (nothing changed) on an
+ * unknown key or a bad value. The library reads no environment variable.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_set_test_overrides(const char* spec);
+
 /* Description of the last non-OK status returned on the calling thread ("" if none).
    The string is owned by the library and valid until the next call on that thread. */
 const char* tp_last_error(void);
@@ -349,7 +373,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 9
+#define TP_SHARD_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@ it raises ``TPShardNotBuilt``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -23,7 +24,7 @@ TP_ACT_GELU = 1
 STATUS_NAMES = {
     0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_NOT_DIVISIBLE", 4: "TP_ERR_RANK",
     5: "TP_ERR_DTYPE", 6: "TP_ERR_ALIGN", 7: "TP_ERR_WORKSPACE", 8: "TP_ERR_HIP",
-    9: "TP_ERR_DEVICE",
+    9: "TP_ERR_DEVICE", 10: "TP_ERR_ALIAS",
 }
 
 # Every symbol include/tp_shard.h declares.
@@ -34,7 +35,7 @@ EXPORTED = (
     "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_gqa_attn_workspace_bytes",
     "tp_gqa_attn_workspace_layout", "tp_gqa_attn_shard_fwd", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
-    "tp_last_error", "tp_abi_version",
+    "tp_set_test_overrides", "tp_last_error", "tp_abi_version",
 )
 
 
@@ -118,6 +119,8 @@ def lib():
                                     ctypes.POINTER(_int)]
     L.tp_sum_partials.restype = _int
     L.tp_sum_partials.argtypes = [ctypes.POINTER(_vp), _int, _i64, _vp, _int, _vp]
+    L.tp_set_test_overrides.restype = _int
+    L.tp_set_test_overrides.argtypes = [ctypes.c_char_p]
     _lib = L
     return L
 
@@ -270,6 +273,21 @@ def tp_gemm_tile_info(M, N, K):
     a, b, c = _int(0), _int(0), _int(0)
     st = lib().tp_gemm_tile_info(M, N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
     return st, a.value, b.value, c.value
+
+
+def tp_set_test_overrides(spec: Optional[str]) -> int:
+    return lib().tp_set_test_overrides(None if spec is None else spec.encode())
+
+
+@contextlib.contextmanager
+def forced_launch(spec: Optional[str]):
+    """Launch choices forced by ``tp_set_test_overrides(spec)`` inside the block, the library's
+    own choices again after it."""
+    check(tp_set_test_overrides(spec))
+    try:
+        yield
+    finally:
+        tp_set_test_overrides(None)
 
 
 def check(status: int) -> None:

@@ -37,7 +37,6 @@
 // tiles that cross a wave's diagonal or the end of the sequence; the output is rescaled only
 // when some running maximum grew by more than 2^8. Queries are dispatched longest-first
 // (highest query tile first) to shorten the causal tail.
-#include <cstdlib>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -534,13 +533,10 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
     // workgroups (64 KB of LDS) overlap one workgroup's prologue and epilogue with the other's
     // key loop: 2.5 us faster on the 4096-token layer step (split), 57.7 against 61.0 us on
     // 8 sequences of 2048 tokens with 4 local heads (unsplit, 512 query tiles). With fewer
-    // workgroups, two sets keep eight waves on every unit. TPSHARD_ATTN_SETS=1/2 overrides the
-    // choice (a test knob).
+    // workgroups, two sets keep eight waves on every unit. The test override "attn_sets=1|2"
+    // replaces the choice.
     int nsets = grid.x >= 2 * 256 ? 1 : 2;
-    if (const char* e = std::getenv("TPSHARD_ATTN_SETS")) {
-        const int v = std::atoi(e);
-        if (v == 1 || v == 2) nsets = v;
-    }
+    if (const int v = tuning().attn_sets) nsets = v;
     if (nsets == 1) {
         if (p.causal)
             hipLaunchKernelGGL((attn_fwd_kernel<D, true, 1>), grid, dim3(256), 0, s, p);
@@ -567,8 +563,8 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
 // (2048 tokens) 42.9 against 44.0 us once split workgroups run two per compute unit. The
 // default is therefore: causal, under 512 query tiles, and at least 16 query tiles per
 // sequence. The partials are reserved whenever there are under 512 query tiles (the workspace
-// size depends on the shapes only, not on the mask). TPSHARD_ATTN_SPLIT (read at launch) is a
-// test knob: 0 turns the split off, 2 forces it wherever the partials are reserved.
+// size depends on the shapes only, not on the mask). The test override "attn_split=1" turns
+// the split off, "attn_split=2" forces it wherever the partials are reserved.
 size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim, bool causal,
                                int* kv_split)
 {
@@ -576,9 +572,8 @@ size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim
     const int64_t n_tiles = (int64_t)n_qt * batch * heads_local;
     const int split = n_tiles < 2 * 256 ? 2 : 1;
     if (kv_split) {
-        const char* e = std::getenv("TPSHARD_ATTN_SPLIT");
-        const int force = e ? std::atoi(e) : -1;
-        if (force == 0)
+        const int force = tuning().attn_split;
+        if (force == 1)
             *kv_split = 1;
         else if (force == 2)
             *kv_split = split;

@@ -31,9 +31,6 @@
 // four accumulator values are four consecutive output COLUMNS of one row: epilogue stores
 // are 16-byte (fp32) or 8-byte (bf16) vectors, and the bias is one vector load.
 #include <algorithm>
-#include <cstdio>
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -690,200 +687,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     }
 }
 
-// ---- bf16 GEMM, 32-wide slabs in a 4-stage LDS ring -------------------------------------
-// Same tile, waves and epilogue as gemm_bf16_kernel; the K loop instead streams 32-wide slabs
-// (64-byte rows, two MFMA K-steps each) through FOUR LDS buffers and loads each slab three
-// slabs ahead, so a slab's global loads have five K-steps of MFMAs to land. Each wave waits
-// only for the slab about to be read (s_waitcnt vmcnt(2 slabs of its own loads)) before the
-// barrier; the two newer slabs stay in flight across it.
-// Swizzle for 64-byte rows: chunk c of row r is stored at c ^ ((r >> 2) & 3), so the 16 rows
-// of one MFMA operand read (same logical chunk) hit 16 distinct 16-byte groups of the banks.
-template <int BM, int BN, int WM, int WN, Epi EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_s4_kernel(GemmProblem p)
-{
-    constexpr int NW = WM * WN;
-    constexpr int BK = 32;
-    constexpr int ST = 4;                   // LDS stages
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int GA = BM / 16, GB = BN / 16;   // 16-row load groups of the A and B slabs
-    constexpr int G = GA + GB;
-    constexpr int LMAX = (G + NW - 1) / NW;     // load instructions per wave per slab (max)
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "tile");
-    static_assert(BM % 16 == 0 && BN % 16 == 0 && 2 * LMAX < 64, "slab split");
-
-    __shared__ __attribute__((aligned(16))) bf16 smem[ST * (BM + BN) * BK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    const int wm = wave / WN, wn = wave % WN;
-    constexpr bool GLU = EPI == Epi::SwiGlu;
-    static_assert(!GLU || FN % 2 == 0, "SwiGlu pairs the wave's 32-column blocks");
-    const int tiles_m = (p.M + BM - 1) / BM;
-    const int tiles_n = ((GLU ? 2 * p.N : p.N) + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int f0 = GLU ? n0 / 2 : n0;       // first B row (output feature) of the tile
-    const __amdgpu_buffer_rsrc_t rA = tile_rsrc(p.A, m0, min(BM, p.M - m0), p.lda, 2);
-    const __amdgpu_buffer_rsrc_t rB =
-        tile_rsrc(p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
-    const __amdgpu_buffer_rsrc_t rB2 =
-        tile_rsrc(GLU ? p.B2 : p.B, f0, min(GLU ? BN / 2 : BN, p.N - f0), p.ldb, 2);
-
-    // One load instruction moves 16 rows x 64 bytes: lane l writes row (l >> 2), physical
-    // chunk (l & 3) of its destination, so it fetches logical chunk (l & 3) ^ ((row >> 2) & 3)
-    // = (l & 3) ^ (l >> 4). The G = GA + GB row groups of the two operands are dealt to the
-    // waves round-robin: wave w moves groups w, w + NW, ... (L_w of them).
-    const int grp_row = lane >> 2;
-    const int lchunk = (lane & 3) ^ (lane >> 4);
-    const int L_w = (G - wave + NW - 1) / NW;
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    // fetch_part(k0, buf, LO, HI) issues this wave's loads LO .. HI-1 of a slab; fetch(k0 >= K)
-    // moves no memory (out-of-range offsets) but still issues L_w loads, which keeps the vmcnt
-    // arithmetic uniform.
-    auto fetch_part = [&](int k0, int buf, auto lo_c, auto hi_c) {
-        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
-        const bool kin = k0 + lchunk * 8 < p.K;
-        const uint32_t kb = (uint32_t)k0 * 2u;
-        bf16* slab = smem + buf * (BM + BN) * BK;
-#pragma unroll
-        for (int i = LO; i < HI; ++i) {
-            const int g = wave + i * NW;
-            // With GA and GB multiples of NW, group i of every wave is in A iff i < GA / NW: a
-            // compile-time choice (no branch splits the loop body).
-            constexpr bool even = GA % NW == 0 && GB % NW == 0;
-            if (even ? i < GA / NW : g < GA) {
-                const uint32_t off = (uint32_t)((16 * g + grp_row) * p.lda + lchunk * 8) * 2u + kb;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(slab + 16 * g * BK), 16,
-                                                         kin ? off : kOutOfRange, 0, 0, 0);
-            } else if (even || g < G) {
-                const int gb = g - GA;
-                if constexpr (GLU) {
-                    // 16-row group gb lies in 32-row block gb / 2: gate rows in even blocks,
-                    // the up rows of the same features in odd ones
-                    const int blk = gb >> 1;
-                    const uint32_t off = (uint32_t)((((blk >> 1) * 32 + (gb & 1) * 16 + grp_row) *
-                                                         p.ldb + lchunk * 8) * 2) + kb;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        (blk & 1) ? rB2 : rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16,
-                        kin ? off : kOutOfRange, 0, 0, 0);
-                } else {
-                    const uint32_t off =
-                        (uint32_t)((16 * gb + grp_row) * p.ldb + lchunk * 8) * 2u + kb;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rB, (lds_ptr)(slab + BM * BK + 16 * gb * BK), 16, kin ? off : kOutOfRange,
-                        0, 0, 0);
-                }
-            }
-        }
-    };
-    auto fetch = [&](int k0, int buf) {
-        fetch_part(k0, buf, std::integral_constant<int, 0>{}, std::integral_constant<int, LMAX>{});
-    };
-    const int fr = lane & 31;
-    const int fg = lane >> 5;
-    auto read_frags = [&](int buf, int ks, bf16x8* fa, bf16x8* fb) {
-        const bf16* sA = smem + buf * (BM + BN) * BK;
-        const bf16* sB = sA + BM * BK;
-        const int ch = ks * 2 + fg;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = wm * WTM + i * 32 + fr;
-            fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((ch ^ ((r >> 2) & 3)) << 3));
-        }
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int r = wn * WTN + i * 32 + fr;
-            fb[i] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((ch ^ ((r >> 2) & 3)) << 3));
-        }
-    };
-    f32x16 acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16(fb[i], fa[j], acc[i][j]);
-    };
-    constexpr int NM = FM * FN;
-    constexpr int NR = FM + FN;
-    // A slab's loads are split between the two MFMA phases of an iteration (SPLIT before the
-    // barrier, the rest after it), so that the waves' global loads reach the address unit
-    // spread over the whole iteration rather than in one burst.
-    constexpr int SPLIT = (LMAX + 1) / 2;
-    auto interleave = [&](auto nv) {
-        InterleaveGroups<0, NM, NR, decltype(nv)::value>::emit();
-    };
-    // s_waitcnt immediate with vmcnt = n, expcnt and lgkmcnt left at their maxima (gfx9 encoding).
-#define TPS_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
-    // Prologue: slab 0 has landed once at most the two newer slabs' loads are outstanding.
-    auto wait_prologue = [&]() {
-        if (G % NW == 0 || L_w == LMAX)
-            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(2 * LMAX));
-        else
-            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(2 * (LMAX - 1)));
-    };
-    // In iteration kt, slab kt+1 has landed once at most slab kt+2's loads and the first part
-    // of slab kt+3's are outstanding.
-    auto wait_next_slab = [&]() {
-        if (G % NW == 0 || L_w == LMAX)
-            __builtin_amdgcn_s_waitcnt(TPS_VMCNT(LMAX + SPLIT));
-        else
-            __builtin_amdgcn_s_waitcnt(TPS_VMCNT((LMAX - 1) + (SPLIT < LMAX - 1 ? SPLIT : LMAX - 1)));
-    };
-#undef TPS_VMCNT
-
-    bf16x8 fa[2][FM], fb[2][FN];
-    const int KT = (p.K + BK - 1) / BK;
-    fetch(0, 0);
-    fetch(BK, 1);
-    fetch(2 * BK, 2);
-    wait_prologue();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, fa[0], fb[0]);
-    // Iteration kt: slab kt in buffer kt % 4, its K-step 0 fragments in set 0.
-    //   first part of slab kt+3's loads into buffer (kt+3) % 4 (last read before the previous
-    //   barrier) | read step 1 | MFMAs step 0 | wait for slab kt+1, barrier | rest of slab
-    //   kt+3's loads | read slab kt+1 step 0 | MFMAs step 1.
-    using Split = std::integral_constant<int, SPLIT>;
-    using Rest = std::integral_constant<int, LMAX - SPLIT>;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 3;
-        const int k3 = (kt + 3) * BK, b3 = (kt + 3) & 3;
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_part(k3, b3, std::integral_constant<int, 0>{}, Split{});
-        read_frags(cur, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        interleave(Split{});
-        __builtin_amdgcn_sched_barrier(0);
-        wait_next_slab();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_part(k3, b3, Split{}, std::integral_constant<int, LMAX>{});
-        read_frags((kt + 1) & 3, 0, fa[0], fb[0]);   // past the last slab: zeros, unused
-        mma(fa[1], fb[1]);
-        interleave(Rest{});
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (GLU) {
-        f32x16 gacc[FN / 2][FM];
-        swiglu_combine<FN, FM>(acc, gacc);
-        store_tile<Epi::Bias, WTM, WTN / 2, NW, (int)sizeof(smem)>(
-            p, gacc, reinterpret_cast<char*>(smem), m0 + wm * WTM, f0 + wn * (WTN / 2), wave, lane);
-    } else {
-        store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
-                                                       m0 + wm * WTM, n0 + wn * WTN, wave, lane);
-    }
-}
-
 // ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
 // Same structure; a 16-byte chunk holds 4 fp32 K values, BK = 32 (128-byte rows again). Lane
 // l reads chunk 4*ks + (l >> 4) and feeds its 4 values to 4 consecutive MFMAs, so MFMA t of
@@ -998,18 +801,15 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool S4>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     const int ncols = epi == Epi::SwiGlu ? 2 * p.N : p.N;   // gate and up columns
     const int tiles = ((p.M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
     const int splits = epi == Epi::F32 && p.k_splits > 1 ? p.k_splits : 1;
     dim3 grid(tiles * splits), block(64 * WM * WN);
-#define TPS_LAUNCH(E)                                                                        \
-    if constexpr (S4)                                                                        \
-        hipLaunchKernelGGL((gemm_bf16_s4_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);  \
-    else                                                                                     \
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);
+#define TPS_LAUNCH(E) \
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);
     switch (epi) {
         case Epi::BiasGelu: TPS_LAUNCH(Epi::BiasGelu) break;
         case Epi::F32: TPS_LAUNCH(Epi::F32) break;
@@ -1058,22 +858,15 @@ GemmTile gemm_bf16_pick_tile(int M, int N, int K)
     return best;
 }
 
-// TPSHARD_GEMM_TILE=<bm>x<bn>[w4][s4] (one of the compiled shapes; "w4" selects the 4-wave
-// layout instead of the default 8-wave one, "s4" the 4-stage 32-wide-slab pipeline instead of
-// the default 2-stage 64-wide one) overrides the choice: a tuning and test knob for sweeping
-// tile shapes; unknown values are ignored.
-static bool tile_override(GemmTile& t, bool& w4, bool& s4)
+// The test override (tp_set_test_overrides "gemm_tile=<bm>x<bn>[w4]") replaces the choice
+// with one of the compiled shapes; "w4" selects the 4-wave layout instead of the default
+// 8-wave one. Tests use it to run every tile layout.
+static bool tile_override(GemmTile& t, bool& w4)
 {
-    const char* e = std::getenv("TPSHARD_GEMM_TILE");
-    if (!e) return false;
-    int bm = 0, bn = 0;
-    if (std::sscanf(e, "%dx%d", &bm, &bn) != 2) return false;
-    const bool known = (bm == 256 && (bn == 256 || bn == 192 || bn == 128)) ||
-                       (bm == 128 && bn == 128);
-    if (!known) return false;
-    t = GemmTile{bm, bn};
-    w4 = std::strstr(e, "w4") != nullptr;
-    s4 = std::strstr(e, "s4") != nullptr;
+    const Tuning tu = tuning();
+    if (tu.gemm_bm == 0) return false;
+    t = GemmTile{tu.gemm_bm, tu.gemm_bn};
+    w4 = tu.gemm_w4 != 0;
     return true;
 }
 
@@ -1098,22 +891,21 @@ static bool prefer_four_waves(int M, int N, int K, GemmTile t, Epi epi)
 GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves)
 {
     GemmTile t = gemm_bf16_pick_tile(M, N, K);
-    bool w4 = prefer_four_waves(M, N, K, t, Epi::F32), s4 = false;
-    tile_override(t, w4, s4);
+    bool w4 = prefer_four_waves(M, N, K, t, Epi::F32);
+    tile_override(t, w4);
     if (waves) *waves = w4 ? 4 : 8;
     return t;
 }
 
-template <bool S4>
 hipError_t gemm_bf16_tile(const GemmProblem& p, Epi epi, hipStream_t s, GemmTile t, bool w4)
 {
     if (t.bm == 256 && t.bn == 256)
-        return w4 ? launch_bf16<256, 256, 2, 2, S4>(p, epi, s) : launch_bf16<256, 256, 2, 4, S4>(p, epi, s);
+        return w4 ? launch_bf16<256, 256, 2, 2>(p, epi, s) : launch_bf16<256, 256, 2, 4>(p, epi, s);
     if (t.bm == 256 && t.bn == 192)
-        return w4 ? launch_bf16<256, 192, 2, 2, S4>(p, epi, s) : launch_bf16<256, 192, 4, 2, S4>(p, epi, s);
+        return w4 ? launch_bf16<256, 192, 2, 2>(p, epi, s) : launch_bf16<256, 192, 4, 2>(p, epi, s);
     if (t.bm == 256 && t.bn == 128)
-        return w4 ? launch_bf16<256, 128, 2, 2, S4>(p, epi, s) : launch_bf16<256, 128, 4, 2, S4>(p, epi, s);
-    return w4 ? launch_bf16<128, 128, 2, 2, S4>(p, epi, s) : launch_bf16<128, 128, 2, 4, S4>(p, epi, s);
+        return w4 ? launch_bf16<256, 128, 2, 2>(p, epi, s) : launch_bf16<256, 128, 4, 2>(p, epi, s);
+    return w4 ? launch_bf16<128, 128, 2, 2>(p, epi, s) : launch_bf16<128, 128, 2, 4>(p, epi, s);
 }
 
 // Eight waves (two per SIMD) per workgroup by default: while one wave of a SIMD waits on
@@ -1151,42 +943,37 @@ static GemmTile glu_pick_tile(int M, int N, int K, bool* w4)
 
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
-    bool w4 = false, s4 = false;
+    bool w4 = false;
     GemmTile t;
     if (epi == Epi::SwiGlu) {
         t = glu_pick_tile(p.M, p.N, p.K, &w4);
         GemmTile o = t;
-        bool ow4 = false, os4 = false;
-        if (tile_override(o, ow4, os4) && glu_ok(o, ow4)) { t = o; w4 = ow4; s4 = os4; }
+        bool ow4 = false;
+        if (tile_override(o, ow4) && glu_ok(o, ow4)) { t = o; w4 = ow4; }
     } else if (epi == Epi::F32 && p.k_splits > 1) {
-        // a K-split launch exists to fill the compute units with the largest tile; the
-        // 4-stage pipeline does not implement the split
+        // a K-split launch exists to fill the compute units with the largest tile
         t = GemmTile{256, 256};
-        tile_override(t, w4, s4);
-        s4 = false;
+        tile_override(t, w4);
     } else {
         t = gemm_bf16_pick_tile(p.M, p.N, p.K);
         w4 = prefer_four_waves(p.M, p.N, p.K, t, epi);
-        tile_override(t, w4, s4);
+        tile_override(t, w4);
     }
-    return s4 ? gemm_bf16_tile<true>(p, epi, s, t, w4) : gemm_bf16_tile<false>(p, epi, s, t, w4);
+    return gemm_bf16_tile(p, epi, s, t, w4);
 }
 
 // A Q/K/V projection with few output columns (grouped-query attention: 4096 x 1280 x 8192
 // on a rank with 8 query and one key/value head) gives 80 tiles of 256 x 256 for 256 CUs,
 // and smaller tiles run at a much lower rate. Cutting K into S parts gives S times the
 // blocks; the parts' fp32 sums go through qkv_reduce_scatter. S = min(4, 256 / tiles) when
-// the tiles fill at most half of the CUs and K is at least 4096. TPSHARD_QKV_SPLIT (1 to 8)
-// overrides the count: a test knob (the workspace size follows it).
+// the tiles fill at most half of the CUs and K is at least 4096. The test override
+// "qkv_split=<1..8>" replaces the count (the workspace size follows it).
 int qkv_k_splits(int M, int N, int K)
 {
     const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
     int s = 1;
     if (2 * tiles <= 256 && K >= 4096) s = (int)std::min<long>(4, 256 / std::max<long>(tiles, 1));
-    if (const char* e = std::getenv("TPSHARD_QKV_SPLIT")) {
-        const int v = std::atoi(e);
-        if (v >= 1 && v <= 8) s = v;
-    }
+    if (const int v = tuning().qkv_split) s = v;
     return s;
 }
 

@@ -7,6 +7,19 @@
 
 namespace tps {
 
+// Launch choices a test may force (tp_set_test_overrides); zero everywhere means "the
+// library's own choice". The library reads no environment variable.
+struct Tuning {
+    int gemm_bm, gemm_bn, gemm_w4;   // GEMM tile (0: chosen per shape) and 4-wave layout
+    int qkv_split;                   // K-split count of the Q/K/V projection (0: chosen)
+    int attn_sets;                   // attention waves sets per workgroup, 1 or 2 (0: chosen)
+    int attn_split;                  // key-range split: 1 off, 2 forced (0: chosen)
+    int sum_grid;                    // partial-sum workgroups (0: one lane per vector)
+    int sum_unroll;                  // partial-sum vectors per lane, 1, 2 or 4 (0: 4)
+};
+// A copy of the current overrides (defined with the C ABI).
+Tuning tuning();
+
 // Output stage of the tensor-core GEMM C[m, n] = sum_k A[m, k] * B[n, k].
 enum class Epi : int {
     BiasGelu = 0,   // C = GeLU(acc + bias[n])  stored in the GEMM's element type (Y_i)

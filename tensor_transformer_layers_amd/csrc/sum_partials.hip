@@ -8,8 +8,6 @@
 // requests per lane are in flight. The adds run in the fixed order 0, 1, ..., N-1, so the
 // result is bitwise reproducible. Reads and writes are non-temporal: every byte is touched
 // exactly once.
-#include <cstdlib>
-
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -96,13 +94,8 @@ __global__ void sum_tail_kernel(Parts parts, int n, int64_t start, int64_t numel
 // loop runs once) with the U = 4 instantiation, whose register footprint keeps two waves per
 // SIMD resident; measured on the 8 x 32 Mi-element sum this streams at about 6.4 TB/s, above a
 // plain copy kernel, while more resident waves (U = 1) or a capped grid reach 5.2 to 5.8 TB/s.
-// TPSHARD_SUM_GRID (workgroups, 0 = one lane per vector) and TPSHARD_SUM_UNROLL (1, 2 or 4)
-// override the defaults -- tuning knobs for sweeping the launch shape.
-static int env_int(const char* name, int dflt)
-{
-    const char* e = std::getenv(name);
-    return e ? std::atoi(e) : dflt;
-}
+// The test overrides "sum_grid=<workgroups>" and "sum_unroll=1|2|4" replace the defaults, so
+// that the tests run every launch shape.
 
 template <int U, bool BF16>
 void launch_u(const Parts& parts, int n, int64_t n4, void* out, unsigned grid, hipStream_t s)
@@ -127,9 +120,10 @@ hipError_t launch(const Parts& parts, int n, int64_t numel, void* out, hipStream
 {
     const int64_t n4 = numel / 4;
     if (n4 > 0) {
-        const int unroll = env_int("TPSHARD_SUM_UNROLL", 4);
+        const Tuning tu = tuning();
+        const int unroll = tu.sum_unroll ? tu.sum_unroll : 4;
         int64_t grid64 = (n4 + kThreads - 1) / kThreads;
-        const int64_t cap = env_int("TPSHARD_SUM_GRID", 0);
+        const int64_t cap = tu.sum_grid;
         if (cap > 0 && grid64 > cap) grid64 = cap;
         if (grid64 > 0x7fffffff) grid64 = 0x7fffffff;   // the loop is grid-stride
         const unsigned grid = (unsigned)grid64;

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -36,8 +37,66 @@ tp_status ok()
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // A GEMM tile addresses its 256 operand rows through one buffer descriptor (32-bit byte
-// offsets, range below 2 GiB), so a reduced (K) dimension is limited to 2^22 elements.
-constexpr int64_t kMaxReduced = int64_t(1) << 22;
+// offsets, range below 2 GiB): 256 bf16 rows of K elements span 2^31 bytes at K = 2^22, so a
+// reduced (K) dimension must stay below 2^22 (it is a multiple of 8: at most 2^22 - 8).
+constexpr int64_t kMaxReduced = (int64_t(1) << 22) - 8;
+// A head's keys and values are addressed the same way with 256-byte rows (d = 128).
+constexpr int64_t kMaxSeq = int64_t(1) << 22;
+
+// Whether two byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// ---- test overrides -------------------------------------------------------------------------
+std::mutex g_tuning_mu;
+tps::Tuning g_tuning{};
+
+// Parse "key=value[,key=value...]" into t; false on an unknown key or a bad value.
+bool parse_tuning(const char* spec, tps::Tuning& t)
+{
+    t = tps::Tuning{};
+    const char* c = spec;
+    while (*c) {
+        const char* end = std::strchr(c, ',');
+        const size_t len = end ? (size_t)(end - c) : std::strlen(c);
+        char item[64];
+        if (len == 0 || len >= sizeof(item)) return false;
+        std::memcpy(item, c, len);
+        item[len] = '\0';
+        char* eq = std::strchr(item, '=');
+        if (!eq) return false;
+        *eq = '\0';
+        const char* key = item;
+        const char* val = eq + 1;
+        char* stop = nullptr;
+        if (std::strcmp(key, "gemm_tile") == 0) {
+            int bm = 0, bn = 0, n = 0;
+            if (std::sscanf(val, "%dx%d%n", &bm, &bn, &n) != 2) return false;
+            const bool known = (bm == 256 && (bn == 256 || bn == 192 || bn == 128)) ||
+                               (bm == 128 && bn == 128);
+            const char* rest = val + n;
+            if (!known || (*rest && std::strcmp(rest, "w4") != 0)) return false;
+            t.gemm_bm = bm;
+            t.gemm_bn = bn;
+            t.gemm_w4 = *rest ? 1 : 0;
+        } else {
+            const long v = std::strtol(val, &stop, 10);
+            if (stop == val || *stop) return false;
+            if (std::strcmp(key, "qkv_split") == 0 && v >= 1 && v <= 8) t.qkv_split = (int)v;
+            else if (std::strcmp(key, "attn_sets") == 0 && (v == 1 || v == 2)) t.attn_sets = (int)v;
+            else if (std::strcmp(key, "attn_split") == 0 && (v == 1 || v == 2)) t.attn_split = (int)v;
+            else if (std::strcmp(key, "sum_grid") == 0 && v >= 0 && v <= INT32_MAX) t.sum_grid = (int)v;
+            else if (std::strcmp(key, "sum_unroll") == 0 && (v == 1 || v == 2 || v == 4)) t.sum_unroll = (int)v;
+            else return false;
+        }
+        if (end && !end[1]) return false;   // a trailing comma
+        c = end ? end + 1 : c + len;
+    }
+    return true;
+}
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -89,7 +148,7 @@ tp_status validate_mlp_sizes(int64_t tokens, int64_t hidden, int64_t ffn, int n,
         return fail(TP_ERR_ALIGN, "hidden=%lld and ffn/N=%lld must be multiples of 8",
                     (long long)hidden, (long long)(ffn / n));
     if (hidden > kMaxReduced || ffn / n > kMaxReduced)
-        return fail(TP_ERR_SHAPE, "hidden=%lld and ffn/N=%lld must not exceed 2^22", (long long)hidden,
+        return fail(TP_ERR_SHAPE, "hidden=%lld and ffn/N=%lld must be below 2^22", (long long)hidden,
                     (long long)(ffn / n));
     return TP_OK;
 }
@@ -142,7 +201,7 @@ tp_status validate_linear(int64_t rows, int64_t in_f, int64_t out_f, int n, int 
         return fail(TP_ERR_ALIGN, "reduced dimension %lld and output width %lld must be multiples of 8",
                     (long long)k, (long long)w);
     if (k > kMaxReduced)
-        return fail(TP_ERR_SHAPE, "reduced dimension %lld must not exceed 2^22", (long long)k);
+        return fail(TP_ERR_SHAPE, "reduced dimension %lld must be below 2^22", (long long)k);
     return TP_OK;
 }
 
@@ -194,9 +253,9 @@ tp_status validate_attn_sizes(int64_t batch, int64_t seq, int64_t hidden, int n_
         return fail(TP_ERR_SHAPE, "batch, seq, hidden and n_heads must be >= 1");
     if (batch * seq > INT32_MAX || hidden > INT32_MAX)
         return fail(TP_ERR_SHAPE, "sizes above 2^31-1 are not supported");
-    if (hidden > kMaxReduced || seq > kMaxReduced)   // (each head's K and V^T: one descriptor too)
-        return fail(TP_ERR_SHAPE, "hidden=%lld and seq=%lld must not exceed 2^22", (long long)hidden,
-                    (long long)seq);
+    if (hidden > kMaxReduced || seq > kMaxSeq)
+        return fail(TP_ERR_SHAPE, "hidden=%lld must be below 2^22 and seq=%lld at most 2^22",
+                    (long long)hidden, (long long)seq);
     if (hidden % n_heads != 0)
         return fail(TP_ERR_NOT_DIVISIBLE, "hidden=%lld not divisible by n_heads=%d", (long long)hidden,
                     n_heads);
@@ -265,11 +324,38 @@ tp_status check_parts(const void* const* parts, int n_parts, const char* what)
     return TP_OK;
 }
 
+// The exchange kernels read every input range while other lanes write the output: an output
+// that shares a byte with an input is rejected.
+tp_status check_no_overlap(const void* const* parts, int n_parts, size_t part_bytes, const void* out,
+                           size_t out_bytes, const char* what)
+{
+    for (int q = 0; q < n_parts; ++q)
+        if (overlap(out, out_bytes, parts[q], part_bytes))
+            return fail(TP_ERR_ALIAS, "%s overlaps input %d", what, q);
+    return TP_OK;
+}
+
 }  // namespace
+
+tps::Tuning tps::tuning()
+{
+    std::lock_guard<std::mutex> lock(g_tuning_mu);
+    return g_tuning;
+}
 
 extern "C" {
 
 int tp_abi_version(void) { return TP_SHARD_ABI_VERSION; }
+
+tp_status tp_set_test_overrides(const char* spec)
+{
+    tps::Tuning t{};
+    if (spec && !parse_tuning(spec, t))
+        return fail(TP_ERR_SHAPE, "unknown override or bad value in \"%s\"", spec);
+    std::lock_guard<std::mutex> lock(g_tuning_mu);
+    g_tuning = t;
+    return ok();
+}
 
 const char* tp_last_error(void) { return g_err; }
 
@@ -327,7 +413,7 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
     tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
     if (st != TP_OK) return st;
     if (tokens > kMaxReduced)   // dA and dB reduce over the tokens
-        return fail(TP_ERR_SHAPE, "tokens=%lld must not exceed 2^22 in the backward", (long long)tokens);
+        return fail(TP_ERR_SHAPE, "tokens=%lld must be below 2^22 in the backward", (long long)tokens);
     if (rank < 0 || rank >= n_shards)
         return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
     if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(dZ) ||
@@ -595,6 +681,10 @@ tp_status tp_reduce_scatter_partials(const float* const* Z_parts, int n_parts, i
     if (st != TP_OK) return st;
     if (!H_r) return fail(TP_ERR_NULL, "H_r must be non-NULL");
     if (!aligned16(H_r)) return fail(TP_ERR_ALIGN, "H_r is not 16-byte aligned");
+    st = check_no_overlap(reinterpret_cast<const void* const*>(Z_parts), n_parts,
+                          (size_t)(batch * seq * hidden) * 4, H_r,
+                          (size_t)(batch * (seq / n_parts) * hidden) * dt_size(out_dt), "H_r");
+    if (st != TP_OK) return st;
     st = check_device();
     if (st != TP_OK) return st;
     tps::SpProblem p{};
@@ -622,6 +712,21 @@ tp_status tp_sp_residual_layernorm_fwd(const float* const* Z_parts, int n_parts,
         (residual_r && !aligned16(residual_r)))
         return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
     if (!(eps >= 0.0f) || eps > 1e30f) return fail(TP_ERR_SHAPE, "eps must be finite and >= 0");
+    {
+        const size_t pb = (size_t)(batch * seq * hidden) * 4;
+        const size_t ob = (size_t)(batch * (seq / n_parts) * hidden) * dt_size(dt);
+        st = check_no_overlap(reinterpret_cast<const void* const*>(Z_parts), n_parts, pb, H_r, ob, "H_r");
+        if (st == TP_OK)
+            st = check_no_overlap(reinterpret_cast<const void* const*>(Z_parts), n_parts, pb, Y_r, ob, "Y_r");
+        if (st == TP_OK && overlap(H_r, ob, Y_r, ob))
+            st = fail(TP_ERR_ALIAS, "H_r and Y_r overlap");
+        if (st == TP_OK && residual_r && overlap(residual_r, ob, Y_r, ob))
+            st = fail(TP_ERR_ALIAS, "residual_r and Y_r overlap");
+        // each lane reads its residual vector before writing the same vector of H_r
+        if (st == TP_OK && residual_r && residual_r != H_r && overlap(residual_r, ob, H_r, ob))
+            st = fail(TP_ERR_ALIAS, "residual_r overlaps H_r without being H_r");
+        if (st != TP_OK) return st;
+    }
     st = check_device();
     if (st != TP_OK) return st;
     tps::SpProblem p{};
@@ -643,6 +748,9 @@ tp_status tp_all_gather_rows(const void* const* slices, int n_parts, int64_t bat
     if (st != TP_OK) return st;
     if (!X) return fail(TP_ERR_NULL, "X must be non-NULL");
     if (!aligned16(X)) return fail(TP_ERR_ALIGN, "X is not 16-byte aligned");
+    st = check_no_overlap(slices, n_parts, (size_t)(batch * (seq / n_parts) * hidden) * dt_size(dt),
+                          X, (size_t)(batch * seq * hidden) * dt_size(dt), "X");
+    if (st != TP_OK) return st;
     st = check_device();
     if (st != TP_OK) return st;
     return hip_status(tps::all_gather_rows(slices, n_parts, (int)batch, (int)seq,
@@ -676,6 +784,15 @@ tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t nume
         if (!aligned16(Z_parts[r])) return fail(TP_ERR_ALIGN, "partial %d is not 16-byte aligned", r);
     }
     if (!aligned16(Z)) return fail(TP_ERR_ALIGN, "Z is not 16-byte aligned");
+    // Each lane reads element vector i of every partial and then writes vector i of Z, so an
+    // fp32 Z may be exactly one of the partials; a bf16 Z (half the row pitch) or any other
+    // overlap would let one lane overwrite inputs another lane has not read yet.
+    const size_t pbytes = (size_t)numel * 4, zbytes = (size_t)numel * dt_size(out_dt);
+    for (int r = 0; r < n_parts; ++r) {
+        const bool same = out_dt == TP_F32 && static_cast<const void*>(Z_parts[r]) == Z;
+        if (!same && overlap(Z, zbytes, Z_parts[r], pbytes))
+            return fail(TP_ERR_ALIAS, "Z overlaps partial %d (only an fp32 Z may be a partial itself)", r);
+    }
     tp_status st = check_device();
     if (st != TP_OK) return st;
     hipError_t e = tps::sum_partials(Z_parts, n_parts, numel, Z, out_dt == TP_BF16,

@@ -10,6 +10,8 @@
 // Both are HBM streaming kernels. The transpose moves 64 x 64 tiles through LDS: 16-byte
 // row-contiguous loads, a padded LDS tile (row pitch 66 elements, so the column reads of
 // the store phase fall on distinct banks), 16-byte row-contiguous stores.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -27,45 +29,52 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const bf16* __restr
                                                              int64_t ld_out)
 {
     __shared__ bf16 tile[kTile][kPitch];
-    const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+    const int c0 = blockIdx.x * kTile;
     const int tid = threadIdx.x;
-    // load: 64 rows x 8 chunks of 8 elements; thread -> (row, chunk), 2 passes
+    // row tiles (of ld_out, padding included) strided over the grid's y extent, which is
+    // capped at 65535
+    const int64_t n_rt = (ld_out + kTile - 1) / kTile;
+    for (int64_t rt = blockIdx.y; rt < n_rt; rt += gridDim.y) {
+        const int r0 = (int)(rt * kTile);
+        if (rt != blockIdx.y) __syncthreads();   // the previous tile's LDS reads are done
+        // load: 64 rows x 8 chunks of 8 elements; thread -> (row, chunk), 2 passes
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int idx = tid + pass * kThreads;
-        const int rr = idx >> 3, ch = idx & 7;
-        const int r = r0 + rr, c = c0 + ch * 8;
-        bf16x8 v;
-        if (r < rows && c < cols) {   // cols is a multiple of 8: a chunk is all in or all out
-            v = *reinterpret_cast<const bf16x8*>(in + (int64_t)r * ld_in + c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = bf16(0.f);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (GELU) {
-                tile[rr][ch * 8 + e] = to_bf16(gelu_erf(static_cast<float>(v[e])));
+        for (int pass = 0; pass < 2; ++pass) {
+            const int idx = tid + pass * kThreads;
+            const int rr = idx >> 3, ch = idx & 7;
+            const int r = r0 + rr, c = c0 + ch * 8;
+            bf16x8 v;
+            if (r < rows && c < cols) {   // cols is a multiple of 8: a chunk is all in or all out
+                v = *reinterpret_cast<const bf16x8*>(in + (int64_t)r * ld_in + c);
             } else {
-                tile[rr][ch * 8 + e] = v[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = bf16(0.f);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (GELU) {
+                    tile[rr][ch * 8 + e] = to_bf16(gelu_erf(static_cast<float>(v[e])));
+                } else {
+                    tile[rr][ch * 8 + e] = v[e];
+                }
             }
         }
-    }
-    __syncthreads();
-    // store: out row c (64 of them) x 8 chunks of 8 input rows each
+        __syncthreads();
+        // store: out row c (64 of them) x 8 chunks of 8 input rows each
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int idx = tid + pass * kThreads;
-        const int cc = idx >> 3, ch = idx & 7;
-        const int c = c0 + cc, r = r0 + ch * 8;
-        if (c >= cols || r >= ld_out) continue;
-        bf16x8 v;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int idx = tid + pass * kThreads;
+            const int cc = idx >> 3, ch = idx & 7;
+            const int c = c0 + cc, r = r0 + ch * 8;
+            if (c >= cols || r >= ld_out) continue;
+            bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = tile[ch * 8 + e][cc];   // rows >= rows were zeroed
-        if (r + 8 <= ld_out) {
-            *reinterpret_cast<bf16x8*>(out + (int64_t)c * ld_out + r) = v;
-        } else {
-            for (int e = 0; e < 8 && r + e < ld_out; ++e) out[(int64_t)c * ld_out + r + e] = v[e];
+            for (int e = 0; e < 8; ++e) v[e] = tile[ch * 8 + e][cc];   // rows >= rows were zeroed
+            if (r + 8 <= ld_out) {
+                *reinterpret_cast<bf16x8*>(out + (int64_t)c * ld_out + r) = v;
+            } else {
+                for (int e = 0; e < 8 && r + e < ld_out; ++e) out[(int64_t)c * ld_out + r + e] = v[e];
+            }
         }
     }
 }
@@ -106,7 +115,8 @@ hipError_t transpose_bf16(const void* in, int rows, int cols, int64_t ld_in, voi
     if (rows < 1 || cols < 1 || cols % 8 != 0 || ld_out < rows || ld_out % 8 != 0)
         return hipErrorInvalidValue;
     const int64_t tr = (ld_out + kTile - 1) / kTile;   // cover the zero padding too
-    dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)tr), block(kThreads);
+    dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)std::min<int64_t>(tr, 65535)),
+        block(kThreads);
     const bf16* i = reinterpret_cast<const bf16*>(in);
     bf16* o = reinterpret_cast<bf16*>(out);
     if (gelu)

@@ -30,9 +30,50 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _require_cuda(*ts):
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices (%s and %s)" % (dev, t.device))
+
+
+def _need(name: str, t: Optional[torch.Tensor], shape, dtype, optional: bool = False) -> None:
+    """Exact shape and dtype of one argument (checked before any ABI call: a mismatched
+    tensor would otherwise become an out-of-bounds access in a kernel)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a tensor" % name)
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _need_2d(name: str, t: torch.Tensor, dtype=None):
+    """A 2-D tensor (of ``dtype`` if given); returns its shape."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError("%s must be a 2-D tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return tuple(t.shape)
+
+
+def _need_workspace(ws: torch.Tensor, nbytes: int) -> int:
+    """A workspace of at least ``nbytes``; returns its size in bytes."""
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError("workspace must be a tensor")
+    have = ws.numel() * ws.element_size()
+    if have < nbytes:
+        raise ValueError("workspace holds %d bytes, %d needed" % (have, nbytes))
+    return have
 
 
 def _stream(stream):
@@ -44,11 +85,17 @@ def column_parallel(X: torch.Tensor, W_i: torch.Tensor, b_i: Optional[torch.Tens
                     n_shards: int, rank: int, gelu: bool = False, Y: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """Y_i = act(X W_i + b_i), W_i [out/N, in] (tp_column_parallel_fwd)."""
-    _require_cuda(X, W_i, b_i)
+    _need_2d("X", X)
     rows, k = X.shape
-    width = W_i.shape[0]
+    dt = X.dtype
+    _dt(X)
+    width = _need_2d("W_i", W_i)[0]
+    _need("W_i", W_i, (width, k), dt)
+    _need("b_i", b_i, (width,), dt, optional=True)
     if Y is None:
         Y = torch.empty(rows, width, dtype=X.dtype, device=X.device)
+    _need("Y", Y, (rows, width), dt)
+    _require_cuda(X, W_i, b_i, Y)
     st = B.tp_column_parallel_fwd(X, W_i, b_i, Y, rows, k, width * n_shards, n_shards, rank,
                                   B.TP_ACT_GELU if gelu else B.TP_ACT_NONE, _dt(X),
                                   _stream(stream))
@@ -59,11 +106,15 @@ def column_parallel(X: torch.Tensor, W_i: torch.Tensor, b_i: Optional[torch.Tens
 def row_parallel(X_i: torch.Tensor, W_i: torch.Tensor, n_shards: int, rank: int,
                  Z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Z_i = X_i W_i (fp32 partial), W_i [out, in/N] (tp_row_parallel_fwd)."""
-    _require_cuda(X_i, W_i)
+    _need_2d("X_i", X_i)
     rows, k = X_i.shape
-    width = W_i.shape[0]
+    _dt(X_i)
+    width = _need_2d("W_i", W_i)[0]
+    _need("W_i", W_i, (width, k), X_i.dtype)
     if Z is None:
         Z = torch.empty(rows, width, dtype=torch.float32, device=X_i.device)
+    _need("Z", Z, (rows, width), torch.float32)
+    _require_cuda(X_i, W_i, Z)
     st = B.tp_row_parallel_fwd(X_i, W_i, Z, rows, k * n_shards, width, n_shards, rank, _dt(X_i),
                                _stream(stream))
     B.check(st)
@@ -91,17 +142,23 @@ def mlp_shard(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor], B
 
     Returns (Z_i fp32 [tokens, hidden], workspace).
     """
-    _require_cuda(X, A_i, a_i, B_i)
+    _need_2d("X", X)
     tokens, hidden = X.shape
-    fl = A_i.shape[0]
-    ffn = fl * n_shards
     dt = _dt(X)
+    fl = _need_2d("A_i", A_i)[0]
+    ffn = fl * n_shards
+    _need("A_i", A_i, (fl, hidden), X.dtype)
+    _need("a_i", a_i, (fl,), X.dtype, optional=True)
+    _need("B_i", B_i, (hidden, fl), X.dtype)
     if Z is None:
         Z = torch.empty(tokens, hidden, dtype=torch.float32, device=X.device)
+    _need("Z", Z, (tokens, hidden), torch.float32)
     if workspace is None:
         workspace = mlp_workspace(tokens, hidden, ffn, n_shards, X.dtype, X.device)
+    wsb = _need_workspace(workspace, B.tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt))
+    _require_cuda(X, A_i, a_i, B_i, Z, workspace)
     st = B.tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z, tokens, hidden, ffn, n_shards, rank, dt,
-                            workspace, workspace.numel(), _stream(stream))
+                            workspace, wsb, _stream(stream))
     B.check(st)
     return Z, workspace
 
@@ -121,20 +178,32 @@ def mlp_shard_backward(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.T
 
     Returns ({"dX": [T, h], "dA": [F/N, h], "da": [F/N], "dB": [h, F/N]} fp32, in the stored
     layouts of X, A_i, a_i, B_i; workspace). dX is the rank's input-gradient partial."""
-    _require_cuda(X, A_i, a_i, B_i, dZ)
+    _need_2d("X", X, torch.bfloat16)
     tokens, hidden = X.shape
-    fl = A_i.shape[0]
+    fl = _need_2d("A_i", A_i)[0]
     ffn = fl * n_shards
+    bf = torch.bfloat16
+    _need("A_i", A_i, (fl, hidden), bf)
+    _need("a_i", a_i, (fl,), bf, optional=True)
+    _need("B_i", B_i, (hidden, fl), bf)
+    _need("dZ", dZ, (tokens, hidden), bf)
     f32 = dict(dtype=torch.float32, device=X.device)
     if out is None:
         out = {"dX": torch.empty(tokens, hidden, **f32), "dA": torch.empty(fl, hidden, **f32),
                "da": torch.empty(fl, **f32) if a_i is not None else None,
                "dB": torch.empty(hidden, fl, **f32)}
+    _need("dX", out.get("dX"), (tokens, hidden), torch.float32)
+    _need("dA", out.get("dA"), (fl, hidden), torch.float32)
+    _need("da", out.get("da"), (fl,), torch.float32, optional=True)
+    _need("dB", out.get("dB"), (hidden, fl), torch.float32)
     if workspace is None:
         workspace = mlp_bwd_workspace(tokens, hidden, ffn, n_shards, X.device)
+    wsb = _need_workspace(workspace, B.tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards,
+                                                                  B.TP_BF16))
+    _require_cuda(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"), out["dB"], workspace)
     st = B.tp_mlp_shard_bwd(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"), out["dB"],
                             tokens, hidden, ffn, n_shards, rank, _dt(X), workspace,
-                            workspace.numel(), _stream(stream))
+                            wsb, _stream(stream))
     B.check(st)
     return out, workspace
 
@@ -156,16 +225,23 @@ def swiglu_shard(X: torch.Tensor, Wg_i: torch.Tensor, Wu_i: torch.Tensor, Wd_i: 
     [tokens, hidden], workspace); the gated activation A_i [tokens, F/N] bf16 sits at offset
     0 of the workspace (``mlp_hidden_view``).
     """
-    _require_cuda(X, Wg_i, Wu_i, Wd_i)
+    _need_2d("X", X, torch.bfloat16)
     tokens, hidden = X.shape
-    fl = Wg_i.shape[0]
+    fl = _need_2d("Wg_i", Wg_i)[0]
     ffn = fl * n_shards
+    _need("Wg_i", Wg_i, (fl, hidden), torch.bfloat16)
+    _need("Wu_i", Wu_i, (fl, hidden), torch.bfloat16)
+    _need("Wd_i", Wd_i, (hidden, fl), torch.bfloat16)
     if Z is None:
         Z = torch.empty(tokens, hidden, dtype=torch.float32, device=X.device)
+    _need("Z", Z, (tokens, hidden), torch.float32)
     if workspace is None:
         workspace = swiglu_workspace(tokens, hidden, ffn, n_shards, X.device)
+    wsb = _need_workspace(workspace, B.tp_swiglu_workspace_bytes(tokens, hidden, ffn, n_shards,
+                                                                 B.TP_BF16))
+    _require_cuda(X, Wg_i, Wu_i, Wd_i, Z, workspace)
     st = B.tp_swiglu_shard_fwd(X, Wg_i, Wu_i, Wd_i, Z, tokens, hidden, ffn, n_shards, rank,
-                               _dt(X), workspace, workspace.numel(), _stream(stream))
+                               _dt(X), workspace, wsb, _stream(stream))
     B.check(st)
     return Z, workspace
 
@@ -204,15 +280,8 @@ def attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch.Ten
                causal: bool = True, Z: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None, stream=None):
     """Rank ``rank``'s attention partial. Returns (Z_i fp32 [batch*seq, hidden], workspace)."""
-    _require_cuda(X, Wqkv_i, bqkv_i, Wo_i)
-    hidden = X.shape[1]
-    if Z is None:
-        Z = torch.empty(batch * seq, hidden, dtype=torch.float32, device=X.device)
-    if workspace is None:
-        workspace = attn_workspace(batch, seq, hidden, n_heads, n_shards, X.device)
-    st = B.tp_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z, batch, seq, hidden, n_heads, causal,
-                             n_shards, rank, _dt(X), workspace, workspace.numel(),
-                             _stream(stream))
+    return gqa_attn_shard(X, Wqkv_i, bqkv_i, Wo_i, batch, seq, n_heads, n_heads, n_shards, rank,
+                          causal, Z=Z, workspace=workspace, stream=stream)
     B.check(st)
     return Z, workspace
 
@@ -235,26 +304,53 @@ def gqa_attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch
     """Rank ``rank``'s grouped-query attention partial (see include/tp_shard.h).
 
     Returns (Z_i fp32 [batch*seq, hidden], workspace)."""
-    _require_cuda(X, Wqkv_i, bqkv_i, Wo_i)
-    hidden = X.shape[1]
+    hidden = _need_2d("X", X, torch.bfloat16)[1]
+    _need("X", X, (batch * seq, hidden), torch.bfloat16)
+    if n_heads < 1 or n_shards < 1 or n_kv_heads < 1 or hidden % n_heads or n_heads % n_shards:
+        raise ValueError("hidden %d, %d heads, %d key/value heads and %d shards do not split "
+                         "evenly" % (hidden, n_heads, n_kv_heads, n_shards))
+    d = hidden // n_heads
+    hl = n_heads // n_shards
+    kvl = n_kv_heads // n_shards if n_kv_heads % n_shards == 0 else 1
+    width = (hl + 2 * kvl) * d
+    _need("Wqkv_i", Wqkv_i, (width, hidden), torch.bfloat16)
+    _need("bqkv_i", bqkv_i, (width,), torch.bfloat16, optional=True)
+    _need("Wo_i", Wo_i, (hidden, hl * d), torch.bfloat16)
     if Z is None:
         Z = torch.empty(batch * seq, hidden, dtype=torch.float32, device=X.device)
+    _need("Z", Z, (batch * seq, hidden), torch.float32)
     if workspace is None:
         workspace = gqa_attn_workspace(batch, seq, hidden, n_heads, n_kv_heads, n_shards, X.device)
+    wsb = _need_workspace(workspace, B.tp_gqa_attn_workspace_bytes(
+        batch, seq, hidden, n_heads, n_kv_heads, n_shards, B.TP_BF16))
+    _require_cuda(X, Wqkv_i, bqkv_i, Wo_i, Z, workspace)
     st = B.tp_gqa_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z, batch, seq, hidden, n_heads,
                                  n_kv_heads, causal, n_shards, rank, _dt(X), workspace,
-                                 workspace.numel(), _stream(stream))
+                                 wsb, _stream(stream))
     B.check(st)
     return Z, workspace
 
 
 # ---- partial sum ------------------------------------------------------------------------------
+def _need_parts(parts: Sequence[torch.Tensor]):
+    if len(parts) < 1:
+        raise ValueError("at least one partial is needed")
+    shape = tuple(parts[0].shape)
+    for q, t in enumerate(parts):
+        _need("partial %d" % q, t, shape, torch.float32)
+    return shape
+
+
 def sum_partials(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    _require_cuda(*parts)
+    shape = _need_parts(parts)
     numel = parts[0].numel()
     if out is None:
-        out = torch.empty(parts[0].shape, dtype=out_dtype, device=parts[0].device)
+        out = torch.empty(shape, dtype=out_dtype, device=parts[0].device)
+    if out.dtype not in _DT:
+        raise ValueError("out has dtype %s, expected float32 or bfloat16" % out.dtype)
+    _need("out", out, shape, out.dtype)
+    _require_cuda(*parts, out)
     st = B.tp_sum_partials(list(parts), len(parts), numel, out, _DT[out.dtype], _stream(stream))
     B.check(st)
     return out
@@ -265,11 +361,16 @@ def reduce_scatter(parts: Sequence[torch.Tensor], batch: int, seq: int, rank: in
                    out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:
     """Rank ``rank``'s slice [batch*seq/N, hidden] of sum(parts) (N = len(parts))."""
-    _require_cuda(*parts)
     N = len(parts)
+    _need_parts(parts)
     hidden = parts[0].shape[-1]
+    _need("partial 0", parts[0], (batch * seq, hidden), torch.float32)
     if out is None:
         out = torch.empty(batch * (seq // N), hidden, dtype=out_dtype, device=parts[0].device)
+    if out.dtype not in _DT:
+        raise ValueError("out has dtype %s, expected float32 or bfloat16" % out.dtype)
+    _need("out", out, (batch * (seq // N), hidden), out.dtype)
+    _require_cuda(*parts, out)
     st = B.tp_reduce_scatter_partials(list(parts), N, batch, seq, hidden, rank, out,
                                       _DT[out.dtype], _stream(stream))
     B.check(st)
@@ -283,14 +384,23 @@ def sp_residual_layernorm(parts: Sequence[torch.Tensor], residual: Optional[torc
                           stream=None):
     """(H_r, Y_r): the rank's slice of sum(parts) + residual, and its LayerNorm (fp32 gamma,
     beta), both [batch*seq/N, hidden] of ``dtype``."""
-    _require_cuda(*parts, residual, gamma, beta)
     N = len(parts)
+    _need_parts(parts)
     hidden = parts[0].shape[-1]
+    _need("partial 0", parts[0], (batch * seq, hidden), torch.float32)
     rows = batch * (seq // N)
+    if dtype not in _DT:
+        raise ValueError("dtype %s is not float32 or bfloat16" % dtype)
+    _need("residual", residual, (rows, hidden), dtype, optional=True)
+    _need("gamma", gamma, (hidden,), torch.float32)
+    _need("beta", beta, (hidden,), torch.float32)
     if H is None:
         H = torch.empty(rows, hidden, dtype=dtype, device=parts[0].device)
     if Y is None:
         Y = torch.empty(rows, hidden, dtype=dtype, device=parts[0].device)
+    _need("H", H, (rows, hidden), dtype)
+    _need("Y", Y, (rows, hidden), dtype)
+    _require_cuda(*parts, residual, gamma, beta, H, Y)
     st = B.tp_sp_residual_layernorm_fwd(list(parts), N, residual, gamma, beta, float(eps), H, Y,
                                         batch, seq, hidden, rank, _DT[dtype], _stream(stream))
     B.check(st)
@@ -300,11 +410,19 @@ def sp_residual_layernorm(parts: Sequence[torch.Tensor], residual: Optional[torc
 def all_gather_rows(slices: Sequence[torch.Tensor], batch: int, seq: int,
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """The full [batch*seq, hidden] tensor from the N ranks' sequence slices."""
-    _require_cuda(*slices)
     N = len(slices)
+    if N < 1:
+        raise ValueError("at least one slice is needed")
     hidden = slices[0].shape[-1]
+    dt = slices[0].dtype
+    if dt not in _DT:
+        raise ValueError("slices have dtype %s, expected float32 or bfloat16" % dt)
+    for q, t in enumerate(slices):
+        _need("slice %d" % q, t, (batch * (seq // N), hidden), dt)
     if out is None:
-        out = torch.empty(batch * seq, hidden, dtype=slices[0].dtype, device=slices[0].device)
+        out = torch.empty(batch * seq, hidden, dtype=dt, device=slices[0].device)
+    _need("out", out, (batch * seq, hidden), dt)
+    _require_cuda(*slices, out)
     st = B.tp_all_gather_rows(list(slices), N, batch, seq, hidden, out, _DT[out.dtype],
                               _stream(stream))
     B.check(st)

@@ -18,3 +18,15 @@ def oracle_lib():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture
+def overrides():
+    """Force launch choices for one test (tp_set_test_overrides); restored afterwards."""
+    from tensor_transformer_layers_amd import binding as B
+
+    def set_(spec):
+        B.check(B.tp_set_test_overrides(spec))
+
+    yield set_
+    B.tp_set_test_overrides(None)

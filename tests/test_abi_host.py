@@ -190,7 +190,7 @@ def test_gqa_validation_and_layout():
             == B.tp_attn_workspace_bytes(4, 2048, 4096, 32, 8, BF16))
 
 
-def test_gqa_workspace_holds_the_split_projection(monkeypatch):
+def test_gqa_workspace_holds_the_split_projection(overrides):
     """4096 x 1280 x 8192 (8 query heads and one key/value head per rank) gives 80 tiles of
     256 x 256: the projection is split three ways along K, and its fp32 partials
     [3][4096][1280] take the space from O on (past the attention's own partials)."""
@@ -198,11 +198,11 @@ def test_gqa_workspace_holds_the_split_projection(monkeypatch):
     o = q + 2 * kv
     assert B.tp_gqa_attn_workspace_bytes(1, 4096, 8192, 64, 8, 8, BF16) == o + 3 * 4096 * 1280 * 4
     # without the split: O, then the key-range halves' outputs and (max, denominator)
-    monkeypatch.setenv("TPSHARD_QKV_SPLIT", "1")
+    overrides("qkv_split=1")
     unsplit = o + 4096 * 1024 * 2 + 256 * 2 * 128 * 128 * 4 + 256 * 2 * 128 * 2 * 4
     assert B.tp_gqa_attn_workspace_bytes(1, 4096, 8192, 64, 8, 8, BF16) == unsplit
     # the multi-head layer shape (4096 x 3072 x 8192: 192 tiles) is not split
-    monkeypatch.delenv("TPSHARD_QKV_SPLIT")
+    overrides(None)
     st, off = B.tp_attn_workspace_layout(1, 4096, 8192, 64, 8, BF16)
     assert st == 0
     assert B.tp_attn_workspace_bytes(1, 4096, 8192, 64, 8, BF16) == (
@@ -218,6 +218,64 @@ def test_sum_validation():
     assert B.tp_sum_partials([P, P + 4], 2, 10, P, F32) == 6
     assert B.tp_sum_partials([P, P], 2, 10, P, 3) == 5
     assert B.tp_sum_partials([P, P], 2, 10, None, F32) == 1
+
+
+def test_sum_and_exchange_aliasing():
+    """An fp32 sum may be written over one of its partials (same pointer); a bf16 output
+    over a partial, or any partial overlap, is TP_ERR_ALIAS. (Calls that pass validation
+    stop at the device check on a host without a GPU: status 8, never 10.)"""
+    Q = P + (1 << 20)
+    assert B.tp_sum_partials([P, Q], 2, 1000, Q, F32) != 10
+    assert B.tp_sum_partials([P, Q], 2, 1000, P, BF16) == 10
+    assert "partial 0" in B.tp_last_error()
+    assert B.tp_sum_partials([P, Q], 2, 1000, Q + 16, F32) == 10
+    assert B.tp_sum_partials([P, Q], 2, 1000, P - 16, F32) == 10
+    assert B.tp_sum_partials([P, Q], 2, 1000, P + 4000, F32) != 10     # just past partial 0
+    # reduce-scatter / boundary / all-gather outputs must not touch an input
+    parts = [P + i * (1 << 26) for i in range(8)]
+    far = P + (1 << 30)
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4096, 8192, 0, parts[3], BF16) == 10
+    assert B.tp_reduce_scatter_partials(parts, 8, 1, 4096, 8192, 0, far, BF16) != 10
+    ln = dict(Z_parts=parts, n_parts=8, residual_r=None, gamma=P, beta=P, eps=1e-5, H_r=far,
+              Y_r=far + (1 << 24), batch=1, seq=4096, hidden=8192, rank=0, dt=BF16)
+    assert B.tp_sp_residual_layernorm_fwd(**ln) != 10
+    assert B.tp_sp_residual_layernorm_fwd(**dict(ln, Y_r=far)) == 10            # Y over H
+    assert B.tp_sp_residual_layernorm_fwd(**dict(ln, H_r=parts[7] + 256)) == 10
+    assert B.tp_sp_residual_layernorm_fwd(**dict(ln, residual_r=far)) != 10     # H is the residual
+    assert B.tp_sp_residual_layernorm_fwd(**dict(ln, residual_r=far + 16)) == 10
+    assert B.tp_all_gather_rows(parts, 8, 1, 4096, 8192, parts[0] + 1024, BF16) == 10
+
+
+def test_reduced_dimension_limit_is_below_2_22():
+    """256 bf16 rows of K = 2^22 elements span 2^31 bytes, past a buffer descriptor's range:
+    K = 2^22 is rejected, K = 2^22 - 8 passes validation."""
+    big, ok = 1 << 22, (1 << 22) - 8
+    assert B.tp_column_parallel_fwd(P, P, None, P, 8, big, 8, 1, 0, 0, BF16) == 2
+    assert B.tp_column_parallel_fwd(P, P, None, P, 8, ok, 8, 1, 0, 0, BF16) != 2
+    assert B.tp_row_parallel_fwd(P, P, P, 8, big, 8, 1, 0, BF16) == 2
+    assert B.tp_mlp_workspace_bytes(8, big, 8, 1, BF16) == 0
+    assert B.tp_mlp_workspace_bytes(8, 8, big, 1, BF16) == 0
+    assert B.tp_mlp_workspace_bytes(8, ok, ok, 1, BF16) > 0
+    assert B.tp_mlp_bwd_workspace_bytes(big, 8, 8, 1, BF16) == 0
+    assert B.tp_mlp_bwd_workspace_bytes(ok, 8, 8, 1, BF16) > 0
+
+
+def test_test_overrides_parsing():
+    assert B.tp_set_test_overrides(None) == 0
+    assert B.tp_set_test_overrides("") == 0
+    for good in ("gemm_tile=256x192", "gemm_tile=128x128w4,qkv_split=3", "attn_sets=1",
+                 "attn_split=2,sum_grid=7,sum_unroll=2"):
+        assert B.tp_set_test_overrides(good) == 0, good
+    for bad in ("gemm_tile=100x100", "gemm_tile=256x256w8", "qkv_split=9", "attn_sets=3",
+                "sum_unroll=3", "nope=1", "qkv_split", "qkv_split=2,", "sum_grid=-1"):
+        assert B.tp_set_test_overrides(bad) == 2, bad
+    B.tp_set_test_overrides(None)
+    # a rejected spec leaves the previous setting in place
+    assert B.tp_set_test_overrides("gemm_tile=128x128") == 0
+    assert B.tp_set_test_overrides("gemm_tile=1x1") == 2
+    assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (128, 128, 8)
+    B.tp_set_test_overrides(None)
+    assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 4)
 
 
 def test_workspace_sizes():
@@ -247,8 +305,8 @@ def test_workspace_sizes():
     assert B.tp_attn_workspace_bytes(1, 5, 256, 2, 1, F32) == 0
 
 
-def test_gemm_tile_info(monkeypatch):
-    monkeypatch.delenv("TPSHARD_GEMM_TILE", raising=False)
+def test_gemm_tile_info(overrides):
+    overrides(None)
     st, bm, bn, w = B.tp_gemm_tile_info(4096, 4096, 8192)
     assert st == 0 and (bm, bn, w) == (256, 256, 8)      # one tile per CU: eight waves
     st, bm, bn, w = B.tp_gemm_tile_info(4096, 3072, 8192)
@@ -262,8 +320,8 @@ def test_gemm_tile_info(monkeypatch):
     assert B.tp_gemm_tile_info(2048, 12288, 24576)[1:] == (256, 192, 4)
     assert B.tp_gemm_tile_info(4096, 3072, 8192)[1:] == (256, 192, 8)    # 256 tiles
     # the override names the layout
-    monkeypatch.setenv("TPSHARD_GEMM_TILE", "256x256")
+    overrides("gemm_tile=256x256")
     assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (256, 256, 8)
-    monkeypatch.setenv("TPSHARD_GEMM_TILE", "128x128w4")
+    overrides("gemm_tile=128x128w4")
     assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (128, 128, 4)
     assert B.tp_gemm_tile_info(0, 1, 1)[0] == 2

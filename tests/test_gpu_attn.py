@@ -79,43 +79,42 @@ def test_attn_small_every_step(case):
 
 
 @pytest.mark.parametrize("case", SMALL)
-def test_attn_forced_key_range_split(case, monkeypatch):
+def test_attn_forced_key_range_split(case, overrides):
     """The same shards with each query tile's keys halved between two workgroups and the
     halves merged by a second kernel (the path long causal sequences take by default; the
     knob forces it on these small grids): ragged tails, single-tile sequences, halves that
     hold no visible key for some queries, d = 64, and the unmasked case."""
-    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "2")
+    overrides("attn_split=2")
     test_attn_small_every_step(case)
 
 
 @pytest.mark.parametrize("case", SMALL)
-def test_attn_qkv_k_split(case, monkeypatch):
+def test_attn_qkv_k_split(case, overrides):
     """The multi-head shards with the Q/K/V projection forced through the K-split path."""
-    monkeypatch.setenv("TPSHARD_QKV_SPLIT", "3")
+    overrides("qkv_split=3")
     test_attn_small_every_step(case)
 
 
-@pytest.mark.parametrize("split,sets", [("2", "2"), ("0", "1")])
+@pytest.mark.parametrize("split,sets", [("2", "2"), ("1", "1")])
 @pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[3], SMALL[5]])
-def test_attn_other_set_counts(case, split, sets, monkeypatch):
+def test_attn_other_set_counts(case, split, sets, overrides):
     """The combinations the default does not take: the key-range split with two sets of
     waves per workgroup (merged through LDS, then across the halves), and one set without
     the split (no merge at all)."""
-    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", split)
-    monkeypatch.setenv("TPSHARD_ATTN_SETS", sets)
+    overrides("attn_split=%s,attn_sets=%s" % (split, sets))
     test_attn_small_every_step(case)
 
 
 @pytest.mark.parametrize("causal", [True, False])
-def test_attn_split_and_unsplit_agree(causal, monkeypatch):
+def test_attn_split_and_unsplit_agree(causal, overrides):
     """Both paths compute the same softmax: agreement to bf16 rounding of O."""
     batch, seq, h, H, N = 2, 300, 512, 4, 2
     w = Workload(name="a", kind="attn", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
                  hidden=h, heads=H, n_shards=N)
     d = attn_inputs(w, seed=17)
-    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "2")
+    overrides("attn_split=2")
     _, O_split, *_ = run_attn(d, batch, seq, H, N, 1, causal)
-    monkeypatch.setenv("TPSHARD_ATTN_SPLIT", "0")
+    overrides("attn_split=1")
     _, O_one, *_ = run_attn(d, batch, seq, H, N, 1, causal)
     e = oracle.rel_frobenius(O_split, O_one)
     print("split vs unsplit O: %.2e" % e)
@@ -133,13 +132,13 @@ def test_attn_causal_first_row_is_projected_value():
         np.testing.assert_allclose(O[b * seq], v[b * seq], rtol=1e-2, atol=1e-2)
 
 
-@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "0")])
-def test_attn_full_size_shard_sampled_rows(rank, split, monkeypatch):
+@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "1")])
+def test_attn_full_size_shard_sampled_rows(rank, split, overrides):
     """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows: the
     default takes the key-range split (256 query tiles of 16 per sequence); also with the
     split turned off (one two-set workgroup per query tile)."""
     if split:
-        monkeypatch.setenv("TPSHARD_ATTN_SPLIT", split)
+        overrides("attn_split=" + split)
     w = WORKLOADS["attn_shard_bf16_b4_s2048_h4096_H32_n8"]
     d = attn_inputs(w)
     Z, O, *_ = run_attn(d, w.batch, w.seq, w.heads, w.n_shards, rank, True)
@@ -159,3 +158,39 @@ def test_attn_full_size_shard_sampled_rows(rank, split, monkeypatch):
     if rank == 0:
         Z2, *_ = run_attn(d, w.batch, w.seq, w.heads, w.n_shards, rank, True)
         assert np.array_equal(Z, Z2), "results must be bitwise repeatable"
+
+
+def test_attn_head_locality_on_gpu():
+    """Each rank evaluates attention for its own heads with no cross-head exchange (llms.blog,
+    "Partitioning Multi-Head and Grouped-Query Attention", step 2), checked on the GPU:
+      * perturbing the W_Q, W_K, W_V columns and W_O rows of every head outside rank r leaves
+        the GPU's Z_r bitwise unchanged;
+      * inside the rank, perturbing local head j's query, key or value columns changes head
+        j's output columns of O_r and leaves the other local head's bits unchanged;
+      * perturbing W_O rows changes Z_r but not O_r."""
+    batch, seq, h, H, N, r = 2, 200, 512, 4, 2, 1      # d = 128, local heads 2 and 3
+    w = Workload(name="a", kind="attn", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, n_shards=N)
+    d = attn_inputs(w, seed=31)
+    dd, hl = h // H, H // N
+    Z0, O0, *_ = run_attn(d, batch, seq, H, N, r, True)
+    # other ranks' heads: columns [0, r h/N) of W_Q/W_K/W_V and the same rows of W_O
+    e = {k: v.copy() for k, v in d.items()}
+    other = slice(0, r * h // N)
+    for k in ("Wq", "Wk", "Wv"):
+        e[k][:, other] += 0.5
+    e["Wo"][other, :] -= 0.5
+    Z1, O1, *_ = run_attn(e, batch, seq, H, N, r, True)
+    assert np.array_equal(Z1, Z0) and np.array_equal(O1, O0)
+    # local head 0 of the rank (global head r * hl): its columns only
+    g0 = slice((r * hl) * dd, (r * hl + 1) * dd)
+    for k in ("Wq", "Wk", "Wv"):
+        e = {kk: v.copy() for kk, v in d.items()}
+        e[k][:, g0] = np.flip(e[k][:, g0], axis=0).copy()
+        _, O2, *_ = run_attn(e, batch, seq, H, N, r, True)
+        assert np.array_equal(O2[:, dd:], O0[:, dd:]), k       # local head 1 untouched
+        assert not np.array_equal(O2[:, :dd], O0[:, :dd]), k   # local head 0 changed
+    e = {kk: v.copy() for kk, v in d.items()}
+    e["Wo"][g0, :] *= -1.0
+    Z3, O3, *_ = run_attn(e, batch, seq, H, N, r, True)
+    assert np.array_equal(O3, O0) and not np.array_equal(Z3, Z0)

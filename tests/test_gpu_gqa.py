@@ -72,11 +72,11 @@ def test_gqa_small_against_oracle(case):
 
 @pytest.mark.parametrize("splits", ["2", "3"])
 @pytest.mark.parametrize("case", SMALL)
-def test_gqa_small_qkv_k_split(case, splits, monkeypatch):
+def test_gqa_small_qkv_k_split(case, splits, overrides):
     """The same shards with the Q/K/V projection forced through the K-split path (fp32
     partials, then the summing scatter): ragged sequences (value columns token by token),
     d = 64, and parts that lie past the end of K (zeros)."""
-    monkeypatch.setenv("TPSHARD_QKV_SPLIT", splits)
+    overrides("qkv_split=" + splits)
     test_gqa_small_against_oracle(case)
 
 

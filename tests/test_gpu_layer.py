@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from gpu_util import dev, host, torch_cuda
-from synth import WORKLOADS, Workload, attn_inputs, bf16_round, normal_matrix, sample_rows
+from synth import WORKLOADS, Workload, attn_inputs, sample_rows
 from tensor_transformer_layers_amd import layout
 
 pytestmark = pytest.mark.gpu
@@ -53,28 +53,65 @@ def test_layer_all_ranks_end_to_end_small():
     assert eh < TOL and ez < TOL
 
 
-def test_layer_full_size_rank0_blocks_sampled():
-    """One rank of the layer at b 1, s 4096, h 8192, 64 heads, F 32768, N 8: the attention
-    shard on sampled rows, and the MLP shard on a seeded stand-in for the attention output."""
+def test_layer_full_size_composed_step():
+    """The layer at b 1, s 4096, h 8192, 64 heads, F 32768, N 8, composed as the benchmark
+    composes it: the 8 attention partials, tp_sum_partials into a bf16 H, the 8 MLP partials
+    on that H, tp_sum_partials into Z (one sum per block: ai360xpert.com "How It Works";
+    llms.blog "Communication Budget and Scaling Limits"). On 40 sampled rows (query-tile and
+    sequence edges included) it checks:
+      * H against the oracle's unsharded attention block;
+      * every rank's MLP partial, and Z, against the oracle fed the GPU's own bf16 H (the
+        "same bf16-rounded inputs" rule);
+      * Z end to end against the oracle's layer (fp64 throughout).
+    Rank 0's LayerShard driver, fed the peers' partials, reproduces Z bitwise."""
     torch = torch_cuda()
     from tensor_transformer_layers_amd import shard
     w = WORKLOADS["layer_shard_bf16_b1_s4096_h8192_H64_f32768_n8"]
     d = attn_inputs(w)
-    N, r, T = w.n_shards, 0, w.tokens
-    W = _rank_weights(d, N, r)
+    N, T = w.n_shards, w.tokens
     X = dev(d["X"], "bf16")
-    Za, _ = shard.attn_shard(X, W["Wqkv"], W["bqkv"], W["Wo"], w.batch, w.seq, w.heads, N, r)
-    rows = sample_rows(T, 16, seed=3, must=[127, 128, 2047])
-    Zo = oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"],
-                           d["Wo"], w.batch, w.seq, w.heads, N, r, True, rows=rows)
-    ea = oracle.rel_frobenius(host(Za)[rows], Zo)
-    # MLP input: a seeded bf16 matrix of the attention output's shape and scale
-    Hin = bf16_round(normal_matrix(np.random.default_rng(99), (T, w.hidden), 1.0))
-    Zm, _ = shard.mlp_shard(dev(Hin, "bf16"), W["A"], W["a"], W["B"], N, r)
-    Zmo = oracle.mlp_shard(Hin[rows], d["A"], d["a"], d["B"], N, r)
-    em = oracle.rel_frobenius(host(Zm)[rows], Zmo)
-    print("layer shard full size: attention err %.2e, MLP err %.2e" % (ea, em))
-    assert ea < TOL and em < TOL
+    za, zm, W0 = [], [], None
+    for r in range(N):
+        W = _rank_weights(d, N, r)
+        za.append(shard.attn_shard(X, W["Wqkv"], W["bqkv"], W["Wo"], w.batch, w.seq, w.heads,
+                                   N, r)[0])
+        if r == 0:
+            W0 = W
+        del W
+    Hs = shard.sum_partials(za, out_dtype=torch.bfloat16)
+    mlp_w = []
+    for r in range(N):
+        A = dev(layout.column_shard(d["A"], N, r), "bf16")
+        a = dev(layout.bias_shard(d["a"], N, r), "bf16")
+        Bm = dev(layout.row_shard(d["B"], N, r), "bf16")
+        zm.append(shard.mlp_shard(Hs, A, a, Bm, N, r)[0])
+        if r == 0:
+            mlp_w = (A, a, Bm)
+        del A, a, Bm
+    Z = shard.sum_partials(zm)
+    drv = shard.LayerShard(w.batch, w.seq, w.hidden, w.heads, w.ffn, N, 0)
+    Zd = drv.forward(X, W0["Wqkv"], W0["bqkv"], W0["Wo"], mlp_w[0], mlp_w[1], mlp_w[2],
+                     za[1:], zm[1:])
+    torch.cuda.synchronize()
+    assert torch.equal(Zd, Z), "the rank-0 driver must reproduce the composed step bitwise"
+    assert torch.equal(drv.H, Hs)
+
+    rows = sample_rows(T, 40, seed=4, must=[0, 1, 127, 128, 255, 2047, 2048, 4095])
+    Hg = host(Hs)[rows]
+    Zg = host(Z)[rows]
+    assert np.isfinite(Zg).all()
+    # attention block: the sum of the 8 rank partials is the unsharded block (N = 1)
+    Ho = oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"],
+                           d["Wo"], w.batch, w.seq, w.heads, 1, 0, True, rows=rows)
+    eh = oracle.rel_frobenius(Hg, Ho)
+    # MLP block on the GPU's own H: each rank's partial, then the sum
+    ems = [oracle.rel_frobenius(host(zm[r])[rows], oracle.mlp_shard(Hg, d["A"], d["a"], d["B"], N, r))
+           for r in range(N)]
+    ez = oracle.rel_frobenius(Zg, oracle.mlp_shard(Hg, d["A"], d["a"], d["B"], 1, 0))
+    e2e = oracle.rel_frobenius(Zg, oracle.mlp_shard(Ho, d["A"], d["a"], d["B"], 1, 0))
+    print("composed layer step: H err %.2e; MLP partial errs %s; Z err %.2e; end-to-end %.2e"
+          % (eh, " ".join("%.2e" % e for e in ems), ez, e2e))
+    assert eh < TOL and max(ems) < TOL and ez < TOL and e2e < TOL
 
 
 def test_mlp_block_all_shards_sweep_n():

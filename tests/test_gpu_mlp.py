@@ -64,12 +64,11 @@ RAGGED = [(1, 64, 64, 1), (37, 200, 240, 2), (300, 264, 1040, 2), (513, 520, 206
 
 
 @pytest.mark.parametrize("tile", [None, "256x256", "256x192", "256x128", "128x128",
-                                  "256x256w4", "256x192w4", "256x128w4", "128x128w4",
-                                  "256x256s4", "256x192s4", "256x128w4s4", "128x128s4"])
+                                  "256x256w4", "256x192w4", "256x128w4", "128x128w4"])
 @pytest.mark.parametrize("shape", RAGGED)
-def test_mlp_bf16_ragged_tiles(shape, tile, monkeypatch):
+def test_mlp_bf16_ragged_tiles(shape, tile, overrides):
     if tile:
-        monkeypatch.setenv("TPSHARD_GEMM_TILE", tile)
+        overrides("gemm_tile=" + tile)
     T, h, F, N = shape
     w = Workload(name="ragged", kind="mlp", dtype="bf16", tokens=T, hidden=h, ffn=F, n_shards=N)
     d = mlp_inputs(w, seed=T + h)
@@ -120,6 +119,12 @@ def test_gelu_erf_sweep_fp32():
     Y, _ = run_shard(d, 1, 0, "f32")
     ref = oracle.gelu(xs.astype(np.float64))
     err = np.abs(Y[:, 0] - ref)
+    # |x| <= 1: absolute error at most 2e-7 (GeLU(x) = x (1 + erf(x / sqrt 2)) / 2, so an erf
+    # within 2e-7 moves GeLU by at most 1e-7 there, plus the final fp32 rounding); beyond,
+    # where GeLU(x) approaches x and its fp32 ulp grows with |x|, 4e-7 |x|.
+    core = np.abs(xs) <= 1.0
+    print("max |GeLU err| on |x| <= 1: %.3e" % err[core].max())
+    assert err[core].max() <= 2e-7
     bound = 4e-7 * np.maximum(1.0, np.abs(xs))
     print("max |GeLU err| %.3e (max err/bound %.3f)" % (err.max(), (err / bound).max()))
     assert (err <= bound).all()

@@ -66,10 +66,10 @@ def test_mlp_backward_small(T, h, F, N):
 
 @pytest.mark.parametrize("tile", ["256x256w4", "128x128w4", "256x192", "256x192w4"])
 @pytest.mark.parametrize("T,h,F,N", [(37, 200, 480, 2), (300, 264, 1040, 2)])
-def test_mlp_backward_small_forced_tiles(T, h, F, N, tile, monkeypatch):
+def test_mlp_backward_small_forced_tiles(T, h, F, N, tile, overrides):
     """The same gradients with every GEMM of the call forced onto one tile layout (the
     GeLU' epilogue and the fp32 products in the 4-wave layouts, on ragged shapes)."""
-    monkeypatch.setenv("TPSHARD_GEMM_TILE", tile)
+    overrides("gemm_tile=" + tile)
     test_mlp_backward_small(T, h, F, N)
 
 

@@ -72,10 +72,9 @@ def test_sum_in_place_on_first_partial():
 
 @pytest.mark.parametrize("unroll", ["1", "2", "4"])
 @pytest.mark.parametrize("grid", ["0", "1", "7", "2048"])
-def test_sum_launch_shapes_exact(unroll, grid, monkeypatch):
+def test_sum_launch_shapes_exact(unroll, grid, overrides):
     """Every launch shape (grid-stride loop, vectors per lane) gives the exact integer sum."""
-    monkeypatch.setenv("TPSHARD_SUM_UNROLL", unroll)
-    monkeypatch.setenv("TPSHARD_SUM_GRID", grid)
+    overrides("sum_unroll=%s,sum_grid=%s" % (unroll, grid))
     for n, numel in ((8, 100003), (3, 4 * 1031 + 2), (13, 777)):
         P = partials_inputs(n, numel, seed=numel + n, integer=True)
         got, c = _run(P)
