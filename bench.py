@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of one tensor-parallel rank's Transformer-layer shard on one MI355X.
 
-Workload (default): one rank (rank 0 of N = 8) of a bf16 layer with hidden 8192, 64 heads of
+Headline workload: one rank (rank 0 of N = 8) of a bf16 layer with hidden 8192, 64 heads of
 d = 128, ffn 32768, batch 1 x seq 4096, causal. One step is the rank's whole forward path:
 
     attention shard  (QKV column-parallel GEMM, causal attention, W_O row-parallel GEMM)
@@ -18,17 +18,25 @@ value = algorithmic FLOPs of the rank's shard (859.0 GFLOP, causal attention cou
 s(s+1)/2 triangle) / wall time per step, in TFLOP/s. Per-stage times come from HIP events
 recorded on the launch stream after each stage in as many instrumented steps before the timed
 ones. The timed steps carry only the two events around the dominant kernel (the slower MLP
-GEMM), whose rate is reported against the bf16 MFMA peak. The fp64 CPU oracle is timed on a bounded sample of the same
-workload on the host cores (rank 0, N = 1 only).
+GEMM), whose rate is reported against the bf16 MFMA peak.
+
+``configs`` times every measured workload on its own unit (an fp32 MLP block of two shards
+and their sum, a bf16 MLP shard, a bf16 attention shard with each of its three steps, the
+layer step above, and all N shards of a large MLP block for N = 1, 2, 4, 8), each with its
+dominant kernel against its roofline. The fp64 CPU oracle is timed on the host cores on the
+same units (bounded row samples where a unit is large) and its results are compared with the
+GPU's outputs of the timed runs: a relative Frobenius error above the tolerance exits
+non-zero.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import glob
+import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -37,9 +45,15 @@ if ROOT not in sys.path:
 
 METRIC = "per-rank TP shard TFLOP/s (MLP + attention) and % of MI355X bf16 MFMA peak"
 WORKLOAD = "layer_shard_bf16_b1_s4096_h8192_H64_f32768_n8"
+W_MLP_F32 = "mlp_f32_t32_h1024_f4096_n2"
+W_MLP_BF16 = "mlp_shard_bf16_t8192_h3072_f12288_n8"
+W_ATTN = "attn_shard_bf16_b4_s2048_h4096_H32_n8"
+W_BLOCK = "mlp_block_bf16_t2048_h12288_f49152"
 # MI355X bf16 dense MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz (the published 2.5 PFLOP/s).
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3     # fp32 matrix (MFMA) peak
 PEAK_HBM_GBS = 8000.0
+TOL = {"f32": 1e-4, "bf16": 1e-2}
 
 
 def log(msg: str) -> None:
@@ -87,43 +101,79 @@ def traffic_for(kernel: str, stage: str):
     return None
 
 
-def cpu_baseline(w, d, rows_n: int):
-    """Time the fp64 oracle on the last ``rows_n`` token rows of rank 0's layer shard."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the OpenMP count only
-        blas = 1
-    T, h, N, H = w.tokens, w.hidden, w.n_shards, w.heads
-    rows = np.arange(T - rows_n, T, dtype=np.int64)
-    hl, dd = H // N, h // H
-    wl = hl * dd
-    Fl = w.ffn // N
-    # FLOPs the oracle performs for these rows: K and V over every position they see
-    # (causal, one sequence), Q, attention, W_O, and the MLP shard on as many rows.
-    need = int(rows.max() % w.seq) + 1
-    flops = (2 * 2.0 * need * h * wl + 2.0 * rows_n * h * wl
-             + sum(4.0 * dd * (int(t % w.seq) + 1) * hl for t in rows)
-             + 2.0 * rows_n * wl * h + 2 * 2.0 * rows_n * h * Fl)
-    oracle._load()
-    t0 = time.perf_counter()
-    oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"], d["Wo"],
-                      w.batch, w.seq, H, N, 0, w.causal, rows=rows)
-    oracle.mlp_shard(d["X"][rows], d["A"], d["a"], d["B"], N, 0)
-    dt = time.perf_counter() - t0
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": int(max(oracle.threads(), blas)),
-        "kind": "oracle",
-        "sample": ("rank 0 of the same layer shard on the last %d token rows: fp64 attention "
-                   "partial (K/V projected over all %d positions they see) and fp64 MLP partial "
-                   "on those rows; %.1f GFLOP in %.2f s" % (rows_n, need, flops / 1e9, dt)),
-    }
+def gemm_kernel_name(M: int, N: int, K: int, epi: int) -> str:
+    """The bf16 GEMM launched for an M x N x K product, named as the profiler names it:
+    gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>."""
+    from tensor_transformer_layers_amd import binding
+    _, tbm, tbn, nw = binding.tp_gemm_tile_info(M, N, K)
+    wgrid = {(256, 256, 8): (2, 4), (256, 192, 8): (4, 2), (256, 128, 8): (4, 2),
+             (128, 128, 8): (2, 4)}.get((tbm, tbn, nw), (2, 2))
+    return "gemm_bf16_kernel<%d, %d, %d, %d, (tps::Epi)%d>" % (tbm, tbn, wgrid[0], wgrid[1], epi)
 
 
+# ---- shader clock during the timed steps ----------------------------------------------------
+class ClockSampler:
+    """Samples the GPU's shader clock from sysfs every ~10 ms in a background thread: the
+    hwmon ``freq1_input`` (current sclk, Hz) where the driver provides it, else the active
+    level of ``pp_dpm_sclk``. Reports what it could read, or why it could not."""
+
+    def __init__(self, period_s: float = 0.01):
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        cands = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
+        if cands:
+            self.source = ("hwmon", cands[0])
+        else:
+            cands = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+            if cands:
+                self.source = ("dpm", cands[0])
+
+    def _read(self):
+        kind, path = self.source
+        with open(path) as f:
+            text = f.read()
+        if kind == "hwmon":
+            return int(text.strip()) / 1e6
+        for line in text.splitlines():
+            if line.strip().endswith("*"):
+                return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except (OSError, ValueError, IndexError):
+                pass
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.source:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        if not self.source:
+            return {"mhz_mean": None, "note": "no sclk file under /sys/class/drm on this host"}
+        s = self.samples
+        if not s:
+            return {"mhz_mean": None, "source": self.source[1], "note": "no readable sample"}
+        return {"mhz_mean": sum(s) / len(s), "mhz_min": min(s), "mhz_max": max(s),
+                "samples": len(s), "source": self.source[1]}
+
+
+# ---- timing helpers -------------------------------------------------------------------------
 def _time_events(fn, reps: int, warmup: int, stream) -> float:
     """Average microseconds per call of fn(), HIP events on ``stream`` around ``reps`` calls."""
     import torch
@@ -139,6 +189,235 @@ def _time_events(fn, reps: int, warmup: int, stream) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def _roof_mfma(name: str, flops: float, us: float, peak: float) -> dict:
+    a = flops / us / 1e6
+    return {"bound": "mfma", "kernel": name, "us": us, "achieved": a, "peak": peak,
+            "unit": "TFLOP/s", "frac": a / peak}
+
+
+def _roof_hbm(name: str, nbytes: float, us: float) -> dict:
+    a = nbytes / us / 1e3
+    return {"bound": "hbm", "kernel": name, "us": us, "achieved": a, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": a / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
+
+
+def _up(x, dtype):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(dtype).cuda()
+
+
+def _host(t):
+    import numpy as np
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def _host32(t):
+    """fp32 host copy (bf16 values are exact in fp32; half the memory of fp64)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+# ---- the measured workloads other than the layer step -----------------------------------------
+def measure_mlp_f32(reps: int = 200, warmup: int = 20):
+    """fp32 MLP block GeLU(XA + a)B: both shards of N = 2 and their on-device sum."""
+    import torch
+    from synth import WORKLOADS, mlp_inputs
+    from tensor_transformer_layers_amd import layout, shard
+    w = WORKLOADS[W_MLP_F32]
+    T, h, F, N = w.tokens, w.hidden, w.ffn, w.n_shards
+    d = mlp_inputs(w, seed=0)
+    X = _up(d["X"], torch.float32)
+    W = [dict(A=_up(layout.column_shard(d["A"], N, r), torch.float32),
+              a=_up(layout.bias_shard(d["a"], N, r), torch.float32),
+              B=_up(layout.row_shard(d["B"], N, r), torch.float32)) for r in range(N)]
+    Zs = [torch.empty(T, h, device="cuda") for _ in range(N)]
+    ws = [shard.mlp_workspace(T, h, F, N, torch.float32) for _ in range(N)]
+    Z = torch.empty(T, h, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def block():
+        for r in range(N):
+            shard.mlp_shard(X, W[r]["A"], W[r]["a"], W[r]["B"], N, r, Z=Zs[r], workspace=ws[r])
+        shard.sum_partials(Zs, out=Z)
+
+    us = _time_events(block, reps, warmup, stream)
+    fl = F // N
+    Y = shard.mlp_hidden_view(ws[0], T, fl, torch.float32)
+    col_us = _time_events(lambda: shard.column_parallel(X, W[0]["A"], W[0]["a"], N, 0, gelu=True,
+                                                        Y=Y), reps, warmup, stream)
+    row_us = _time_events(lambda: shard.row_parallel(Y, W[0]["B"], N, 0, Z=Zs[0]), reps, warmup,
+                          stream)
+    block()
+    torch.cuda.synchronize()
+    flops = 2 * 2.0 * T * h * F
+    # both GEMMs of a shard stream their fp32 weight shard (1024 x 2048 x 4 bytes = 8.4 MB)
+    # plus a 32-row activation: bound by memory and latency, not by the matrix cores
+    col_bytes = 4.0 * (T * h + fl * h + fl + T * fl)
+    row_bytes = 4.0 * (T * fl + h * fl + T * h)
+    dom, dom_us, dom_b = ("column", col_us, col_bytes) if col_us >= row_us else ("row", row_us, row_bytes)
+    kname = "gemm_f32_kernel<32, 64, (tps::Epi)%d>" % (0 if dom == "column" else 1)
+    out = {"workload": w.name, "unit": "block: %d shards + on-device sum" % N, "dtype": "f32",
+           "us": us, "tflops": flops / us / 1e6, "peak": PEAK_FP32_TFLOPS,
+           "frac_peak": flops / us / 1e6 / PEAK_FP32_TFLOPS,
+           "per_shard_kernels_us": {"column": col_us, "row": row_us},
+           "roofline": dict(_roof_hbm(kname, dom_b, dom_us),
+                            mfma_frac=2.0 * T * h * fl / dom_us / 1e6 / PEAK_FP32_TFLOPS)}
+    return out, {"d": d, "Z": _host(Z)}
+
+
+def measure_mlp_bf16(reps: int = 30, warmup: int = 10):
+    """One rank's bf16 MLP shard (rank 0 of N = 8): column GEMM + GeLU, row GEMM."""
+    import torch
+    from synth import WORKLOADS, mlp_inputs
+    from tensor_transformer_layers_amd import layout, shard
+    w = WORKLOADS[W_MLP_BF16]
+    T, h, F, N = w.tokens, w.hidden, w.ffn, w.n_shards
+    fl = F // N
+    d = mlp_inputs(w, seed=0)
+    X = _up(d["X"], torch.bfloat16)
+    A = _up(layout.column_shard(d["A"], N, 0), torch.bfloat16)
+    a = _up(layout.bias_shard(d["a"], N, 0), torch.bfloat16)
+    Bm = _up(layout.row_shard(d["B"], N, 0), torch.bfloat16)
+    Z = torch.empty(T, h, device="cuda")
+    ws = shard.mlp_workspace(T, h, F, N, torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    us = _time_events(lambda: shard.mlp_shard(X, A, a, Bm, N, 0, Z=Z, workspace=ws), reps, warmup,
+                      stream)
+    Y = shard.mlp_hidden_view(ws, T, fl, torch.bfloat16)
+    col_us = _time_events(lambda: shard.column_parallel(X, A, a, N, 0, gelu=True, Y=Y), reps,
+                          warmup, stream)
+    row_us = _time_events(lambda: shard.row_parallel(Y, Bm, N, 0, Z=Z), reps, warmup, stream)
+    shard.mlp_shard(X, A, a, Bm, N, 0, Z=Z, workspace=ws)
+    torch.cuda.synchronize()
+    flops = 4.0 * T * h * fl
+    if col_us >= row_us:
+        roof = _roof_mfma(gemm_kernel_name(T, fl, h, 0), flops / 2, col_us, PEAK_BF16_TFLOPS)
+    else:
+        roof = _roof_mfma(gemm_kernel_name(T, h, fl, 1), flops / 2, row_us, PEAK_BF16_TFLOPS)
+    out = {"workload": w.name, "unit": "one rank's shard (rank 0 of %d)" % N, "dtype": "bf16",
+           "us": us, "tflops": flops / us / 1e6, "peak": PEAK_BF16_TFLOPS,
+           "frac_peak": flops / us / 1e6 / PEAK_BF16_TFLOPS,
+           "kernels_us": {"column_gemm_gelu": col_us, "row_gemm": row_us}, "roofline": roof}
+    return out, {"d": d, "Z": _host(Z)}
+
+
+def measure_attn(reps: int = 30, warmup: int = 10):
+    """One rank's bf16 causal attention shard (rank 0 of N = 8), the whole call and each of
+    its three steps on their own (the same kernels: tp_qkv_projection_fwd,
+    tp_head_attention_fwd, tp_row_parallel_fwd on the workspace's O)."""
+    import torch
+    from synth import WORKLOADS, attn_inputs
+    from tensor_transformer_layers_amd import layout, shard
+    w = WORKLOADS[W_ATTN]
+    b, s, h, H, N = w.batch, w.seq, w.hidden, w.heads, w.n_shards
+    T, d_h, hl = b * s, h // H, H // N
+    wl = hl * d_h
+    d = attn_inputs(w, seed=0)
+    X = _up(d["X"], torch.bfloat16)
+    Wqkv = _up(layout.qkv_shard(d["Wq"], d["Wk"], d["Wv"], N, 0), torch.bfloat16)
+    bqkv = _up(layout.qkv_bias_shard(d["bq"], d["bk"], d["bv"], N, 0), torch.bfloat16)
+    Wo = _up(layout.row_shard(d["Wo"], N, 0), torch.bfloat16)
+    Z = torch.empty(T, h, device="cuda")
+    ws = shard.attn_workspace(b, s, h, H, N)
+    stream = torch.cuda.current_stream()
+    us = _time_events(lambda: shard.attn_shard(X, Wqkv, bqkv, Wo, b, s, H, N, 0, True, Z=Z,
+                                               workspace=ws), reps, warmup, stream)
+    O = shard.attn_views(ws, b, s, h, H, N)["o"]
+    q_us = _time_events(lambda: shard.qkv_projection(X, Wqkv, bqkv, b, s, H, H, N, 0, ws), reps,
+                        warmup, stream)
+    a_us = _time_events(lambda: shard.head_attention(b, s, h, H, H, N, 0, True, ws), reps,
+                        warmup, stream)
+    o_us = _time_events(lambda: shard.row_parallel(O, Wo, N, 0, Z=Z), reps, warmup, stream)
+    shard.attn_shard(X, Wqkv, bqkv, Wo, b, s, H, N, 0, True, Z=Z, workspace=ws)
+    torch.cuda.synchronize()
+    fq = 2.0 * T * h * 3 * wl
+    fa = 4.0 * d_h * (s * (s + 1) // 2) * hl * b
+    fo = 2.0 * T * wl * h
+    flops = fq + fa + fo
+    # W_O: bf16 O_i [T, Hl d] and W_O,i [h, Hl d] in, fp32 Z_i [T, h] out
+    wo_bytes = 2.0 * T * wl + 2.0 * h * wl + 4.0 * T * h
+    out = {"workload": w.name, "unit": "one rank's shard (rank 0 of %d)" % N, "dtype": "bf16",
+           "us": us, "tflops": flops / us / 1e6, "peak": PEAK_BF16_TFLOPS,
+           "frac_peak": flops / us / 1e6 / PEAK_BF16_TFLOPS,
+           "steps": {
+               "qkv_projection": _roof_mfma(gemm_kernel_name(T, 3 * wl, h, 2), fq, q_us,
+                                            PEAK_BF16_TFLOPS),
+               "attention": _roof_mfma("attn_fwd_kernel (with its key-range merge, if any)",
+                                       fa, a_us, PEAK_BF16_TFLOPS),
+               "out_projection": dict(_roof_hbm(gemm_kernel_name(T, h, wl, 1), wo_bytes, o_us),
+                                      mfma_frac=fo / o_us / 1e6 / PEAK_BF16_TFLOPS),
+           }}
+    dom = max(out["steps"], key=lambda k: out["steps"][k]["us"])
+    out["roofline"] = dict(out["steps"][dom], step=dom)
+    return out, {"d": d, "Z": _host(Z)}
+
+
+def measure_block_sweep(reps: int = 20, warmup: int = 10):
+    """All N shards of one bf16 MLP block (T 2048, h 12288, F 49152) plus the on-device sum,
+    N in {1, 2, 4, 8}: how the shard's GEMM shape moves the MFMA utilisation. One set of full
+    weights (seeded, on the device) is sliced into N shards for every N."""
+    import torch
+    from synth import WORKLOADS
+    from tensor_transformer_layers_amd import binding, shard
+    w = WORKLOADS[W_BLOCK]
+    T, h, F = w.tokens, w.hidden, w.ffn
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device="cuda", generator=g) * std).to(torch.bfloat16)
+
+    X = rnd(T, h)
+    At = rnd(F, h, std=0.02)       # [F, h]: column shards are row blocks
+    a = rnd(F, std=0.02)
+    Bt = rnd(h, F, std=0.02)       # [h, F]: row shards are column blocks
+    sweep, keep = {}, {}
+    for N in (1, 2, 4, 8):
+        fl = F // N
+        A_s = [At[r * fl:(r + 1) * fl] for r in range(N)]
+        a_s = [a[r * fl:(r + 1) * fl] for r in range(N)]
+        B_s = [Bt[:, r * fl:(r + 1) * fl].contiguous() for r in range(N)]
+        Zs = [torch.empty(T, h, device="cuda") for _ in range(N)]
+        Zsum = torch.empty(T, h, device="cuda")
+        ws = shard.mlp_workspace(T, h, F, N, torch.bfloat16)
+        shard_us = _time_events(lambda: shard.mlp_shard(X, A_s[0], a_s[0], B_s[0], N, 0, Z=Zs[0],
+                                                        workspace=ws), reps, warmup, stream)
+
+        def block():
+            for r in range(N):
+                shard.mlp_shard(X, A_s[r], a_s[r], B_s[r], N, r, Z=Zs[r], workspace=ws)
+            shard.sum_partials(Zs, out=Zsum)
+
+        block_us = _time_events(block, max(4, reps // N), 2, stream)
+        sum_us = _time_events(lambda: shard.sum_partials(Zs, out=Zsum), reps, warmup, stream)
+        block()
+        torch.cuda.synchronize()
+        fl_shard = 4.0 * T * h * fl
+        sum_bytes = (N + 1) * T * h * 4
+        _, cbm, cbn, cw = binding.tp_gemm_tile_info(T, fl, h)
+        _, rbm, rbn, rw = binding.tp_gemm_tile_info(T, h, fl)
+        sweep["N=%d" % N] = {
+            "shard_us": shard_us, "shard_tflops": fl_shard / shard_us / 1e6,
+            "shard_frac_bf16_peak": fl_shard / shard_us / 1e6 / PEAK_BF16_TFLOPS,
+            "column_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, fl, h, cbm, cbn, cw),
+            "row_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, h, fl, rbm, rbn, rw),
+            "block_us": block_us, "block_tflops": N * fl_shard / block_us / 1e6,
+            "sum_us": sum_us, "sum_gbs": sum_bytes / sum_us / 1e3}
+        keep[N] = {"shard0": Zs[0], "block": Zsum}
+        del A_s, a_s, B_s, Zs, ws
+    out = {"workload": w.name, "unit": "all N shards + on-device sum (block); rank 0 (shard)",
+           "dtype": "bf16", "per_n": sweep}
+    best = max(sweep, key=lambda k: sweep[k]["block_tflops"])
+    out["tflops"] = sweep[best]["block_tflops"]
+    out["frac_peak"] = out["tflops"] / PEAK_BF16_TFLOPS
+    out["best_n"] = best
+    return out, {"X": X, "At": At, "a": a, "Bt": Bt, "keep": keep}
+
+
 def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
     """Throughput of the paths next to the core shard, each on its named workload.
 
@@ -148,7 +427,7 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
     """
     import torch
     from synth import WORKLOADS
-    from tensor_transformer_layers_amd import binding, shard
+    from tensor_transformer_layers_amd import shard
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
     stream = torch.cuda.current_stream()
@@ -227,47 +506,145 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
                                          "call also recomputes P (one more GEMM) and transposes "
                                          "six operands"}
     del X, A_i, a_i, B_i, dZ, grads, ws
-    # all N shards of one MLP block, N in {1, 2, 4, 8}: how the shard's GEMM shape moves the
-    # MFMA utilisation (column GEMM T x F/N x h, row GEMM T x h x F/N), the whole block (every
-    # shard in turn, then the on-device sum) and the sum alone
-    w = WORKLOADS["mlp_block_bf16_t2048_h12288_f49152"]
-    T, h, F = w.tokens, w.hidden, w.ffn
-    X = rnd(T, h)
-    sweep = {}
-    for N in (1, 2, 4, 8):
-        fl = F // N
-        A_s = [rnd(fl, h, std=0.02) for _ in range(N)]
-        a_s = [rnd(fl, std=0.02) for _ in range(N)]
-        B_s = [rnd(h, fl, std=0.02) for _ in range(N)]
-        Zs = [torch.empty(T, h, device="cuda") for _ in range(N)]
-        Zsum = torch.empty(T, h, device="cuda")
-        ws = shard.mlp_workspace(T, h, F, N, torch.bfloat16)
-        shard_us = _time_events(lambda: shard.mlp_shard(X, A_s[0], a_s[0], B_s[0], N, 0, Z=Zs[0],
-                                                        workspace=ws), reps, warmup, stream)
-
-        def block():
-            for r in range(N):
-                shard.mlp_shard(X, A_s[r], a_s[r], B_s[r], N, r, Z=Zs[r], workspace=ws)
-            shard.sum_partials(Zs, out=Zsum)
-
-        block_us = _time_events(block, max(4, reps // N), 2, stream)
-        sum_us = _time_events(lambda: shard.sum_partials(Zs, out=Zsum), reps, warmup, stream)
-        fl_shard = 4.0 * T * h * fl
-        sum_bytes = (N + 1) * T * h * 4
-        _, cbm, cbn, cw = binding.tp_gemm_tile_info(T, fl, h)
-        _, rbm, rbn, rw = binding.tp_gemm_tile_info(T, h, fl)
-        sweep["N=%d" % N] = {
-            "shard_us": shard_us, "shard_tflops": fl_shard / shard_us / 1e6,
-            "shard_frac_bf16_peak": fl_shard / shard_us / 1e6 / PEAK_BF16_TFLOPS,
-            "column_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, fl, h, cbm, cbn, cw),
-            "row_gemm": "%dx%dx%d, tile %dx%d, %d waves" % (T, h, fl, rbm, rbn, rw),
-            "block_us": block_us, "block_tflops": N * fl_shard / block_us / 1e6,
-            "sum_us": sum_us, "sum_gbs": sum_bytes / sum_us / 1e3}
-        del A_s, a_s, B_s, Zs, Zsum, ws
-    out["mlp_block_sweep"] = {"workload": w.name, "per_n": sweep}
-    del X
     torch.cuda.synchronize()
     return out
+
+
+# ---- the CPU oracle: timings on the same units, and parity of the timed outputs ---------------
+def _threads_used() -> int:
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the OpenMP count only
+        blas = 1
+    return int(max(oracle.threads(), blas))
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def cpu_leg(layer, ctx) -> dict:
+    """Time the fp64 oracle on each workload's unit (or a stated row sample of it) and compare
+    its results with the GPU's outputs of the timed runs. Returns {"layer": cpu_baseline,
+    workload: cpu_baseline, ..., "parity": {...}}."""
+    import numpy as np
+    import oracle
+    from synth import WORKLOADS, sample_rows
+    oracle._load()
+    cores = _threads_used()
+    res, parity = {}, {}
+
+    def base(flops, dt, sample, unit="TFLOP/s", extra=None):
+        b = {"value": flops / dt / 1e12, "unit": unit, "cores": cores, "kind": "oracle",
+             "sample": sample + "; %.2f GFLOP in %.3f s" % (flops / 1e9, dt)}
+        if extra:
+            b.update(extra)
+        return b
+
+    # layer step, rank 0: attention partial on X and MLP partial on the GPU's own H, all rows
+    w, d, g = layer["w"], layer["d"], layer["gpu"]
+    T, h, N, H = w.tokens, w.hidden, w.n_shards, w.heads
+    fl = stage_flops(w)
+    Za, ta = _timed(lambda: oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"],
+                                              d["bv"], d["Wo"], w.batch, w.seq, H, N, 0, w.causal))
+    Zm, tm = _timed(lambda: oracle.mlp_shard(g["H"], d["A"], d["a"], d["B"], N, 0))
+    rows = sample_rows(T, 32, seed=5, must=[0, 127, 128, 4095])
+    Zz = oracle.mlp_shard(g["H"][rows], d["A"], d["a"], d["B"], 1, 0)
+    parity[w.name] = {"attention_partial": oracle.rel_frobenius(g["Z_attn"], Za),
+                      "mlp_partial_on_gpu_H": oracle.rel_frobenius(g["Z_mlp"], Zm),
+                      "layer_output_sampled_rows": oracle.rel_frobenius(g["out"][rows], Zz),
+                      "tol": TOL["bf16"]}
+    res[w.name] = base(sum(fl.values()), ta + tm,
+                       "rank 0 of the layer shard on all %d token rows: fp64 attention partial "
+                       "and fp64 MLP partial (on the GPU's bf16 H)" % T)
+
+    # fp32 MLP block: both shards and the sum, all threads (median of 3) and one thread
+    c = ctx[W_MLP_F32]
+    d1 = c["d"]
+    w1 = WORKLOADS[W_MLP_F32]
+    f1 = 2 * 2.0 * w1.tokens * w1.hidden * w1.ffn
+
+    def blk():
+        return oracle.sum_partials(np.stack([oracle.mlp_shard(d1["X"], d1["A"], d1["a"], d1["B"],
+                                                              w1.n_shards, r).astype(np.float32)
+                                             for r in range(w1.n_shards)]))
+    times = []
+    for _ in range(3):
+        Zb, t = _timed(blk)
+        times.append(t)
+    t_all = sorted(times)[1]
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            _, t1 = _timed(blk)
+        one = {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": t1}
+    except Exception as e:  # threadpoolctl missing or unable to limit the pools
+        one = {"value": None, "note": "single-thread run unavailable: %s" % e}
+    Zu = oracle.mlp_shard(d1["X"], d1["A"], d1["a"], d1["B"], 1, 0)
+    parity[w1.name] = {"block": oracle.rel_frobenius(c["Z"], Zu), "tol": TOL["f32"]}
+    res[w1.name] = base(f1, t_all, "the whole block (%d shards and their sum), median of 3"
+                        % w1.n_shards, extra={"single_thread": one})
+
+    # bf16 MLP shard, rank 0, all rows
+    c = ctx[W_MLP_BF16]
+    w2 = WORKLOADS[W_MLP_BF16]
+    Z2, t2 = _timed(lambda: oracle.mlp_shard(c["d"]["X"], c["d"]["A"], c["d"]["a"], c["d"]["B"],
+                                             w2.n_shards, 0))
+    parity[w2.name] = {"shard": oracle.rel_frobenius(c["Z"], Z2), "tol": TOL["bf16"]}
+    res[w2.name] = base(4.0 * w2.tokens * w2.hidden * (w2.ffn // w2.n_shards), t2,
+                        "rank 0's whole shard (all %d token rows)" % w2.tokens)
+
+    # bf16 attention shard, rank 0, all rows
+    c = ctx[W_ATTN]
+    w3 = WORKLOADS[W_ATTN]
+    d3 = c["d"]
+    Z3, t3 = _timed(lambda: oracle.attn_shard(d3["X"], d3["Wq"], d3["Wk"], d3["Wv"], d3["bq"],
+                                              d3["bk"], d3["bv"], d3["Wo"], w3.batch, w3.seq,
+                                              w3.heads, w3.n_shards, 0, True))
+    parity[w3.name] = {"shard": oracle.rel_frobenius(c["Z"], Z3), "tol": TOL["bf16"]}
+    dh = w3.hidden // w3.heads
+    wl = w3.hidden // w3.n_shards
+    T3 = w3.batch * w3.seq
+    f3 = (2.0 * T3 * w3.hidden * 3 * wl + 4.0 * dh * (w3.seq * (w3.seq + 1) // 2)
+          * (w3.heads // w3.n_shards) * w3.batch + 2.0 * T3 * wl * w3.hidden)
+    res[w3.name] = base(f3, t3, "rank 0's whole shard (all %d token rows)" % T3)
+
+    # large MLP block, N = 1 .. 8: a 64-row sample, the block (= the N = 1 shard) and rank 0's
+    # shard at N = 8; parity of every N's block sum and of the N = 8 shard on those rows
+    c = ctx[W_BLOCK]
+    w5 = WORKLOADS[W_BLOCK]
+    rows5 = sample_rows(w5.tokens, 64, seed=6, must=[0, 255, 256, 2047])
+    X5 = _host(c["X"][rows5])
+    A5, a5, B5 = _host32(c["At"]).T, _host32(c["a"]), _host32(c["Bt"]).T
+    Zb5, tb5 = _timed(lambda: oracle.mlp_shard(X5, A5, a5, B5, 1, 0))
+    Zs5, ts5 = _timed(lambda: oracle.mlp_shard(X5, A5, a5, B5, 8, 0))
+    par5 = {"tol": TOL["bf16"]}
+    for N5, k in c["keep"].items():
+        par5["block_N=%d" % N5] = oracle.rel_frobenius(_host(k["block"])[rows5], Zb5)
+    par5["shard0_N=8"] = oracle.rel_frobenius(_host(c["keep"][8]["shard0"])[rows5], Zs5)
+    parity[w5.name] = par5
+    f5 = 4.0 * len(rows5) * w5.hidden * w5.ffn
+    res[w5.name] = base(f5, tb5, "the block on %d sampled token rows (N = 1: the block is one "
+                        "shard)" % len(rows5),
+                        extra={"per_shard_n8": base(f5 / 8, ts5, "rank 0's shard at N = 8 on "
+                                                    "the same %d rows" % len(rows5))})
+    res["parity"] = parity
+    return res
+
+
+def parity_failures(parity: dict) -> list:
+    bad = []
+    for name, p in parity.items():
+        tol = p["tol"]
+        for k, v in p.items():
+            if k != "tol" and not (v <= tol):
+                bad.append("%s %s: %.3e > %.0e" % (name, k, v, tol))
+    return bad
 
 
 def main() -> int:
@@ -277,12 +654,11 @@ def main() -> int:
     # The shader clock settles over the first tens of milliseconds of sustained MFMA work
     # (the chip is power-limited under these GEMMs), so the default warm-up is long.
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="token rows in the CPU-oracle sample (default: the whole shard)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU-oracle timings and the parity check of the timed outputs")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the timings of the gated MLP, GQA, sequence-parallel and "
-                         "backward paths")
+                    help="skip the other measured workloads and the timings of the gated MLP, "
+                         "GQA, sequence-parallel and backward paths")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (the reference transfer "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -306,7 +682,8 @@ def main() -> int:
     import numpy as np
     import torch
     from synth import WORKLOADS, attn_inputs
-    from tensor_transformer_layers_amd import binding, shard
+    from tensor_transformer_layers_amd import shard
+    from tensor_transformer_layers_amd import binding
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -396,11 +773,12 @@ def main() -> int:
             pair[1].record(stream)
 
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(on_stage=lambda name, pair=dev[i]: mark_dominant(name, pair))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    with ClockSampler() as clock:
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            step(on_stage=lambda name, pair=dev[i]: mark_dominant(name, pair))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
     out = drv.out
     if not bool(torch.isfinite(out).all()):
         log("non-finite output")
@@ -423,18 +801,14 @@ def main() -> int:
                           "gbs": sum_bytes["sum_attention"] / stage_us["sum_attention"] / 1e3},
         "sum_mlp": {"us": stage_us["sum_mlp"], "gbs": sum_bytes["sum_mlp"] / stage_us["sum_mlp"] / 1e3},
     }
-    # The dominant kernel named as the profiler names it:
-    # gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>; its rate from the timed steps.
     M, Nn, K = (T, Fl, h) if dom == "mlp_column" else (T, h, Fl)
-    _, tbm, tbn, nw = binding.tp_gemm_tile_info(M, Nn, K)
-    wgrid = {(256, 256, 8): (2, 4), (256, 192, 8): (4, 2), (256, 128, 8): (4, 2),
-             (128, 128, 8): (2, 4)}.get((tbm, tbn, nw), (2, 2))
-    kname = "gemm_bf16_kernel<%d, %d, %d, %d, (tps::Epi)%d>" % (
-        tbm, tbn, wgrid[0], wgrid[1], 0 if dom == "mlp_column" else 1)
+    kname = gemm_kernel_name(M, Nn, K, 0 if dom == "mlp_column" else 1)
     achieved = fl[dom] / (dom_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_for(kname, dom)}
+    shard_tflops = flop_step / ((stage_us["attention_shard"] + stage_us["mlp_column"]
+                                 + stage_us["mlp_row"]) * 1e-6) / 1e12
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -447,23 +821,72 @@ def main() -> int:
                    "step": "attention shard, sum of %d partials, MLP shard, sum of %d partials"
                            % (N, N)},
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "shard_tflops": (flop_step / ((stage_us["attention_shard"] + stage_us["mlp_column"]
-                                       + stage_us["mlp_row"]) * 1e-6) / 1e12),
+        "shard_tflops": shard_tflops,
         "event_ms_per_step": event_ms,
         "breakdown": breakdown,
         "roofline": roofline,
+        "clock": clock.summary(),
         "cpu_baseline": None,
     }
-    del ranks, za_other, zm_other, drv
+    layer = {"w": w, "d": d, "gpu": {"H": _host(drv.H), "Z_attn": _host(drv.Z_attn),
+                                     "Z_mlp": _host(drv.Z_mlp), "out": _host(drv.out)}}
+    configs = {WORKLOAD: {"workload": WORKLOAD, "unit": "one rank's layer step (rank 0 of %d)" % N,
+                          "dtype": "bf16", "us": ms_per_step * 1e3, "tflops": value,
+                          "peak": PEAK_BF16_TFLOPS, "frac_peak": value / PEAK_BF16_TFLOPS,
+                          "roofline": roofline}}
+    del ranks, za_other, zm_other, drv, X
     torch.cuda.empty_cache()
+    ctx = {}
     if not args.no_next_rows:
+        for name, fn in ((W_MLP_F32, measure_mlp_f32), (W_MLP_BF16, measure_mlp_bf16),
+                         (W_ATTN, measure_attn), (W_BLOCK, measure_block_sweep)):
+            log("timing %s" % name)
+            with ClockSampler() as ck:
+                configs[name], ctx[name] = fn()
+            configs[name]["clock"] = ck.summary()
+            torch.cuda.empty_cache()
         log("timing the paths next to the core shard")
         line["next_rows"] = measure_next_rows()
+    line["configs"] = configs
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a %d-row sample" % args.cpu_rows)
-        line["cpu_baseline"] = cpu_baseline(w, d, args.cpu_rows)
+        log("timing the CPU oracle and checking the timed outputs")
+        cb = cpu_leg(layer, ctx) if ctx else cpu_leg_layer_only(layer)
+        line["cpu_baseline"] = cb.pop(WORKLOAD)
+        line["parity"] = cb.pop("parity")
+        for name, b in cb.items():
+            configs[name]["cpu_baseline"] = b
+        bad = parity_failures(line["parity"])
+        if bad:
+            print(json.dumps(line), flush=True)
+            log("parity failure: " + "; ".join(bad))
+            return 1
     print(json.dumps(line), flush=True)
     return 0
+
+
+def cpu_leg_layer_only(layer) -> dict:
+    """The layer step's oracle timing and parity alone (when the other workloads are skipped)."""
+    import oracle
+    from synth import sample_rows
+    oracle._load()
+    w, d, g = layer["w"], layer["d"], layer["gpu"]
+    fl = stage_flops(w)
+    Za, ta = _timed(lambda: oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"],
+                                              d["bv"], d["Wo"], w.batch, w.seq, w.heads,
+                                              w.n_shards, 0, w.causal))
+    Zm, tm = _timed(lambda: oracle.mlp_shard(g["H"], d["A"], d["a"], d["B"], w.n_shards, 0))
+    rows = sample_rows(w.tokens, 32, seed=5, must=[0, 127, 128, 4095])
+    Zz = oracle.mlp_shard(g["H"][rows], d["A"], d["a"], d["B"], 1, 0)
+    f = sum(fl.values())
+    return {w.name: {"value": f / (ta + tm) / 1e12, "unit": "TFLOP/s", "cores": _threads_used(),
+                     "kind": "oracle",
+                     "sample": "rank 0 of the layer shard on all %d token rows: fp64 attention "
+                               "partial and fp64 MLP partial (on the GPU's bf16 H); %.2f GFLOP "
+                               "in %.3f s" % (w.tokens, f / 1e9, ta + tm)},
+            "parity": {w.name: {"attention_partial": oracle.rel_frobenius(g["Z_attn"], Za),
+                                "mlp_partial_on_gpu_H": oracle.rel_frobenius(g["Z_mlp"], Zm),
+                                "layer_output_sampled_rows": oracle.rel_frobenius(g["out"][rows], Zz),
+                                "tol": TOL["bf16"]}}}
 
 
 if __name__ == "__main__":

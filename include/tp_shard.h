@@ -273,6 +273,30 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * The attention shard's first two steps as separate calls (llms.blog, "Partitioning
+ * Multi-Head and Grouped-Query Attention", steps 1 and 2); the third, Z_i = O_i W_O,i, is
+ * tp_row_parallel_fwd on the workspace's O. tp_gqa_attn_shard_fwd is exactly these three
+ * launches in order, so running them one by one gives its bits (and lets a caller time each).
+ *
+ * tp_qkv_projection_fwd: step 1, the column-parallel Q, K, V projections of the rank's heads
+ *   into the workspace's Q, K and Vt regions (layout and scaling as for tp_gqa_attn_shard_fwd;
+ *   n_kv_heads = n_heads for multi-head attention).
+ * tp_head_attention_fwd: step 2, softmax(Q K^T / sqrt(d) + M) V of every local head from the
+ *   workspace's Q, K and Vt into its O (heads concatenated locally), with no cross-head
+ *   exchange. The workspace must hold step 1's results for the same sizes.
+ * Arguments, workspace size (tp_gqa_attn_workspace_bytes) and errors as for
+ * tp_gqa_attn_shard_fwd.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_qkv_projection_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                                int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                int n_kv_heads, int n_shards, int rank, tp_dtype dt,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+tp_status tp_head_attention_fwd(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                int n_kv_heads, int causal, int n_shards, int rank, tp_dtype dt,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Partial sum, the single-device stand-in for the tensor-parallel all-reduce:
  *   Z = Z_0 + Z_1 + ... + Z_{n_parts-1}       (llms.blog, Row-Parallel Linear Layer: the
  *                                              output and communication bullets)

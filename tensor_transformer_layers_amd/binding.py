@@ -34,7 +34,8 @@ EXPORTED = (
     "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
     "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_gqa_attn_workspace_bytes",
     "tp_gqa_attn_workspace_layout", "tp_gqa_attn_shard_fwd", "tp_attn_workspace_bytes",
-    "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_sum_partials", "tp_gemm_tile_info",
+    "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_qkv_projection_fwd",
+    "tp_head_attention_fwd", "tp_sum_partials", "tp_gemm_tile_info",
     "tp_set_test_overrides", "tp_last_error", "tp_abi_version",
 )
 
@@ -114,6 +115,12 @@ def lib():
     L.tp_attn_shard_fwd.restype = _int
     L.tp_attn_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                     _int, _int, _vp, _sz, _vp]
+    L.tp_qkv_projection_fwd.restype = _int
+    L.tp_qkv_projection_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
+                                        _int, _vp, _sz, _vp]
+    L.tp_head_attention_fwd.restype = _int
+    L.tp_head_attention_fwd.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int, _int, _int,
+                                        _vp, _sz, _vp]
     L.tp_gemm_tile_info.restype = _int
     L.tp_gemm_tile_info.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int),
                                     ctypes.POINTER(_int)]
@@ -261,6 +268,20 @@ def tp_attn_shard_fwd(X, Wqkv_i, bqkv_i, Wo_i, Z_i, batch, seq, hidden, n_heads,
     return lib().tp_attn_shard_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(bqkv_i), _ptr(Wo_i), _ptr(Z_i),
                                    batch, seq, hidden, n_heads, int(causal), n_shards, rank, dt,
                                    _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def tp_qkv_projection_fwd(X, Wqkv_i, bqkv_i, batch, seq, hidden, n_heads, n_kv_heads, n_shards,
+                          rank, dt, workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_qkv_projection_fwd(_ptr(X), _ptr(Wqkv_i), _ptr(bqkv_i), batch, seq, hidden,
+                                       n_heads, n_kv_heads, n_shards, rank, dt, _ptr(workspace),
+                                       workspace_bytes, _stream(stream))
+
+
+def tp_head_attention_fwd(batch, seq, hidden, n_heads, n_kv_heads, causal, n_shards, rank, dt,
+                          workspace, workspace_bytes, stream=None) -> int:
+    return lib().tp_head_attention_fwd(batch, seq, hidden, n_heads, n_kv_heads, int(causal),
+                                       n_shards, rank, dt, _ptr(workspace), workspace_bytes,
+                                       _stream(stream))
 
 
 def tp_sum_partials(Z_parts: Sequence, n_parts, numel, Z, out_dt, stream=None) -> int:

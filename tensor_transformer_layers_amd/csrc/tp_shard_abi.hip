@@ -324,6 +324,76 @@ tp_status check_parts(const void* const* parts, int n_parts, const char* what)
     return TP_OK;
 }
 
+// Shape, rank and workspace checks shared by the attention calls.
+tp_status validate_attn_call(int64_t batch, int64_t seq, int64_t hidden, int n_heads, int n_kv_heads,
+                             int n_shards, int rank, tp_dtype dt, void* workspace,
+                             size_t workspace_bytes, AttnLayout* L)
+{
+    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt, L);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (workspace && !aligned16(workspace))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    if (!workspace || workspace_bytes < L->total)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L->total,
+                    workspace ? workspace_bytes : (size_t)0);
+    return TP_OK;
+}
+
+// Step 1 of the attention block: the column-parallel Q/K/V projection of the local heads into
+// the workspace (Q scaled, per head; V transposed).
+tp_status launch_qkv(const void* X, const void* Wqkv_i, const void* bqkv_i, int64_t batch,
+                     int64_t seq, int64_t hidden, const AttnLayout& L, char* ws, hipStream_t s)
+{
+    const int T = (int)(batch * seq);
+    const int w = L.hl * L.d;       // local query width
+    const int wkv = L.kvl * L.d;    // local key (and value) width
+    tps::GemmProblem g{};
+    g.A = X; g.lda = hidden;
+    g.B = Wqkv_i; g.ldb = hidden;
+    g.bias = bqkv_i;
+    g.M = T; g.N = w + 2 * wkv; g.K = (int)hidden;
+    g.q = ws + L.q; g.k = ws + L.k; g.vt = ws + L.vt;
+    g.seq = (int)seq; g.heads_local = L.hl; g.kv_heads_local = L.kvl; g.head_dim = L.d;
+    g.ld_vt = L.ld_vt;
+    // The softmax's scale 1/sqrt(d), with log2(e) for its base-2 exponentials, is folded into
+    // the stored queries (one rounding of the fp32 result either way).
+    g.q_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    if (L.qkv_splits > 1) {
+        // few output columns: the projection runs as K-split fp32 partials, then one pass
+        // sums them and applies the bias, the scale and the scatter
+        float* parts = reinterpret_cast<float*>(ws + L.qkv_part);
+        g.k_splits = L.qkv_splits;
+        g.split_stride = (int64_t)g.M * g.N;
+        tps::GemmProblem gp = g;
+        gp.bias = nullptr;
+        gp.C = parts; gp.ldc = g.N;
+        hipError_t e = tps::gemm_bf16(gp, tps::Epi::F32, s);
+        if (e != hipSuccess) return hip_status(e, "QKV projection launch");
+        return hip_status(tps::qkv_reduce_scatter(g, parts, s), "QKV scatter launch");
+    }
+    return hip_status(tps::gemm_bf16(g, tps::Epi::Qkv, s), "QKV projection launch");
+}
+
+// Step 2: head-local attention from the workspace's Q, K, V^T into its O (heads concatenated).
+tp_status launch_heads(int64_t batch, int64_t seq, int causal, const AttnLayout& L, char* ws,
+                       hipStream_t s)
+{
+    tps::AttnProblem a{};
+    a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;
+    a.batch = (int)batch; a.heads_local = L.hl; a.kv_heads_local = L.kvl; a.seq = (int)seq;
+    a.head_dim = L.d; a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
+    const size_t part = tps::attention_partial_bytes((int)batch, L.hl, (int)seq, L.d, causal, &a.kv_split);
+    if (part) {
+        a.part_o = reinterpret_cast<float*>(ws + L.part_o);
+        a.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+    } else {
+        a.kv_split = 1;
+    }
+    return hip_status(tps::attention_fwd(a, s), "attention launch");
+}
+
 // The exchange kernels read every input range while other lanes write the output: an output
 // that shares a byte with an input is rejected.
 tp_status check_no_overlap(const void* const* parts, int n_parts, size_t part_bytes, const void* out,
@@ -590,6 +660,38 @@ tp_status tp_gqa_attn_workspace_layout(int64_t batch, int64_t seq, int64_t hidde
     return ok();
 }
 
+tp_status tp_qkv_projection_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
+                                int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                int n_kv_heads, int n_shards, int rank, tp_dtype dt,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!X || !Wqkv_i) return fail(TP_ERR_NULL, "X and Wqkv_i must be non-NULL");
+    AttnLayout L;
+    tp_status st = validate_attn_call(batch, seq, hidden, n_heads, n_kv_heads, n_shards, rank, dt,
+                                      workspace, workspace_bytes, &L);
+    if (st != TP_OK) return st;
+    if (!aligned16(X) || !aligned16(Wqkv_i) || (bqkv_i && !aligned16(bqkv_i)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    st = check_device();
+    if (st != TP_OK) return st;
+    return launch_qkv(X, Wqkv_i, bqkv_i, batch, seq, hidden, L, reinterpret_cast<char*>(workspace),
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+tp_status tp_head_attention_fwd(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
+                                int n_kv_heads, int causal, int n_shards, int rank, tp_dtype dt,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    AttnLayout L;
+    tp_status st = validate_attn_call(batch, seq, hidden, n_heads, n_kv_heads, n_shards, rank, dt,
+                                      workspace, workspace_bytes, &L);
+    if (st != TP_OK) return st;
+    st = check_device();
+    if (st != TP_OK) return st;
+    return launch_heads(batch, seq, causal, L, reinterpret_cast<char*>(workspace),
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
 tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* bqkv_i,
                                 const void* Wo_i, float* Z_i, int64_t batch, int64_t seq,
                                 int64_t hidden, int n_heads, int n_kv_heads, int causal,
@@ -599,76 +701,31 @@ tp_status tp_gqa_attn_shard_fwd(const void* X, const void* Wqkv_i, const void* b
     if (!X || !Wqkv_i || !Wo_i || !Z_i)
         return fail(TP_ERR_NULL, "X, Wqkv_i, Wo_i and Z_i must be non-NULL");
     AttnLayout L;
-    tp_status st = validate_attn_sizes(batch, seq, hidden, n_heads, n_kv_heads, n_shards, dt, &L);
+    tp_status st = validate_attn_call(batch, seq, hidden, n_heads, n_kv_heads, n_shards, rank, dt,
+                                      workspace, workspace_bytes, &L);
     if (st != TP_OK) return st;
-    if (rank < 0 || rank >= n_shards)
-        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
     if (!aligned16(X) || !aligned16(Wqkv_i) || !aligned16(Wo_i) || !aligned16(Z_i) ||
-        (bqkv_i && !aligned16(bqkv_i)) || (workspace && !aligned16(workspace)))
+        (bqkv_i && !aligned16(bqkv_i)))
         return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
-    if (!workspace || workspace_bytes < L.total)
-        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
-                    workspace ? workspace_bytes : (size_t)0);
     st = check_device();
     if (st != TP_OK) return st;
-
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = reinterpret_cast<char*>(workspace);
-    const int T = (int)(batch * seq);
-    const int w = L.hl * L.d;       // local query width
-    const int wkv = L.kvl * L.d;    // local key (and value) width
     // 1. Column-parallel QKV projection of the local heads, scattered per head (V transposed).
-    tps::GemmProblem g{};
-    g.A = X; g.lda = hidden;
-    g.B = Wqkv_i; g.ldb = hidden;
-    g.bias = bqkv_i;
-    g.M = T; g.N = w + 2 * wkv; g.K = (int)hidden;
-    g.q = ws + L.q; g.k = ws + L.k; g.vt = ws + L.vt;
-    g.seq = (int)seq; g.heads_local = L.hl; g.kv_heads_local = L.kvl; g.head_dim = L.d;
-    g.ld_vt = L.ld_vt;
-    // The softmax's scale 1/sqrt(d), with log2(e) for its base-2 exponentials, is folded into
-    // the stored queries (one rounding of the fp32 result either way).
-    g.q_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
-    hipError_t e;
-    if (L.qkv_splits > 1) {
-        // few output columns: the projection runs as K-split fp32 partials, then one pass
-        // sums them and applies the bias, the scale and the scatter
-        float* parts = reinterpret_cast<float*>(ws + L.qkv_part);
-        g.k_splits = L.qkv_splits;
-        g.split_stride = (int64_t)g.M * g.N;
-        tps::GemmProblem gp = g;
-        gp.bias = nullptr;
-        gp.C = parts; gp.ldc = g.N;
-        e = tps::gemm_bf16(gp, tps::Epi::F32, s);
-        if (e != hipSuccess) return hip_status(e, "QKV projection launch");
-        e = tps::qkv_reduce_scatter(g, parts, s);
-        if (e != hipSuccess) return hip_status(e, "QKV scatter launch");
-    } else {
-        e = tps::gemm_bf16(g, tps::Epi::Qkv, s);
-        if (e != hipSuccess) return hip_status(e, "QKV projection launch");
-    }
+    st = launch_qkv(X, Wqkv_i, bqkv_i, batch, seq, hidden, L, ws, s);
+    if (st != TP_OK) return st;
     // 2. Head-local attention; heads concatenated locally into O_i.
-    tps::AttnProblem a{};
-    a.q = ws + L.q; a.k = ws + L.k; a.vt = ws + L.vt; a.o = ws + L.o;
-    a.batch = (int)batch; a.heads_local = L.hl; a.kv_heads_local = L.kvl; a.seq = (int)seq;
-    a.head_dim = L.d; a.ld_vt = L.ld_vt; a.causal = causal ? 1 : 0;
-    const size_t part = tps::attention_partial_bytes((int)batch, L.hl, (int)seq, L.d, causal, &a.kv_split);
-    if (part) {
-        a.part_o = reinterpret_cast<float*>(ws + L.part_o);
-        a.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
-    } else {
-        a.kv_split = 1;
-    }
-    e = tps::attention_fwd(a, s);
-    if (e != hipSuccess) return hip_status(e, "attention launch");
+    st = launch_heads(batch, seq, causal, L, ws, s);
+    if (st != TP_OK) return st;
     // 3. Row-parallel output projection: Z_i = O_i W_O,i (fp32 partial).
+    const int T = (int)(batch * seq);
+    const int w = L.hl * L.d;
     tps::GemmProblem g3{};
     g3.A = ws + L.o; g3.lda = w;
     g3.B = Wo_i; g3.ldb = w;
     g3.C = Z_i; g3.ldc = hidden;
     g3.M = T; g3.N = (int)hidden; g3.K = w;
-    e = tps::gemm_bf16(g3, tps::Epi::F32, s);
-    return hip_status(e, "output projection launch");
+    return hip_status(tps::gemm_bf16(g3, tps::Epi::F32, s), "output projection launch");
 }
 
 tp_status tp_reduce_scatter_partials(const float* const* Z_parts, int n_parts, int64_t batch,

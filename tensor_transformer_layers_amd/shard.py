@@ -331,6 +331,42 @@ def gqa_attn_shard(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch
     return Z, workspace
 
 
+def qkv_projection(X: torch.Tensor, Wqkv_i: torch.Tensor, bqkv_i: Optional[torch.Tensor],
+                   batch: int, seq: int, n_heads: int, n_kv_heads: int, n_shards: int, rank: int,
+                   workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Step 1 of the attention shard alone: Q, K, V^T of the local heads into ``workspace``
+    (tp_qkv_projection_fwd)."""
+    hidden = _need_2d("X", X, torch.bfloat16)[1]
+    _need("X", X, (batch * seq, hidden), torch.bfloat16)
+    if n_heads < 1 or n_shards < 1 or n_kv_heads < 1 or hidden % n_heads or n_heads % n_shards:
+        raise ValueError("hidden %d, %d heads, %d key/value heads and %d shards do not split "
+                         "evenly" % (hidden, n_heads, n_kv_heads, n_shards))
+    d = hidden // n_heads
+    hl = n_heads // n_shards
+    kvl = n_kv_heads // n_shards if n_kv_heads % n_shards == 0 else 1
+    _need("Wqkv_i", Wqkv_i, ((hl + 2 * kvl) * d, hidden), torch.bfloat16)
+    _need("bqkv_i", bqkv_i, ((hl + 2 * kvl) * d,), torch.bfloat16, optional=True)
+    wsb = _need_workspace(workspace, B.tp_gqa_attn_workspace_bytes(
+        batch, seq, hidden, n_heads, n_kv_heads, n_shards, B.TP_BF16))
+    _require_cuda(X, Wqkv_i, bqkv_i, workspace)
+    B.check(B.tp_qkv_projection_fwd(X, Wqkv_i, bqkv_i, batch, seq, hidden, n_heads, n_kv_heads,
+                                    n_shards, rank, B.TP_BF16, workspace, wsb, _stream(stream)))
+    return workspace
+
+
+def head_attention(batch: int, seq: int, hidden: int, n_heads: int, n_kv_heads: int,
+                   n_shards: int, rank: int, causal: bool, workspace: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    """Step 2 of the attention shard alone: every local head's attention from the workspace's
+    Q, K, V^T into its O (tp_head_attention_fwd)."""
+    wsb = _need_workspace(workspace, B.tp_gqa_attn_workspace_bytes(
+        batch, seq, hidden, n_heads, n_kv_heads, n_shards, B.TP_BF16))
+    _require_cuda(workspace)
+    B.check(B.tp_head_attention_fwd(batch, seq, hidden, n_heads, n_kv_heads, causal, n_shards,
+                                    rank, B.TP_BF16, workspace, wsb, _stream(stream)))
+    return workspace
+
+
 # ---- partial sum ------------------------------------------------------------------------------
 def _need_parts(parts: Sequence[torch.Tensor]):
     if len(parts) < 1:

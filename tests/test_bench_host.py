@@ -59,3 +59,28 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "--gpus must be 1" in r.stderr
     assert r.stdout == ""
+
+
+def test_parity_failures_flag_errors_above_tolerance_and_nan():
+    good = {"w": {"a": 1e-3, "b": 9.9e-3, "tol": 1e-2}}
+    assert bench.parity_failures(good) == []
+    bad = {"w": {"a": 1e-3, "b": 2e-2, "tol": 1e-2}, "f32": {"block": float("nan"), "tol": 1e-4}}
+    msgs = bench.parity_failures(bad)
+    assert len(msgs) == 2 and any("w b" in m for m in msgs) and any("f32 block" in m for m in msgs)
+
+
+def test_clock_sampler_reports_what_it_can_read(tmp_path):
+    s = bench.ClockSampler()
+    with s:
+        pass
+    out = s.summary()
+    assert "mhz_mean" in out
+    # a dpm table with the active level starred, as the driver prints it
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1800Mhz *\n2: 2400Mhz\n")
+    s.source = ("dpm", str(f))
+    assert s._read() == 1800.0
+    f2 = tmp_path / "freq1_input"
+    f2.write_text("2100000000\n")
+    s.source = ("hwmon", str(f2))
+    assert s._read() == 2100.0

@@ -194,3 +194,33 @@ def test_attn_head_locality_on_gpu():
     e["Wo"][g0, :] *= -1.0
     Z3, O3, *_ = run_attn(e, batch, seq, H, N, r, True)
     assert np.array_equal(O3, O0) and not np.array_equal(Z3, Z0)
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[3], SMALL[5]])
+def test_attn_steps_one_by_one_equal_the_shard_call(case):
+    """The projection, head-local attention and output projection called one by one give
+    the shard call's bits (Z and every workspace region the steps write)."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import binding as B
+    from tensor_transformer_layers_amd import shard
+    batch, seq, h, H, N, causal, bias = case
+    w = Workload(name="a", kind="attn", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, n_shards=N)
+    d = attn_inputs(w, seed=seq + 3, with_bias=bias)
+    r = N - 1
+    X = dev(d["X"], "bf16")
+    Wqkv = dev(layout.qkv_shard(d["Wq"], d["Wk"], d["Wv"], N, r), "bf16")
+    bqkv = dev(layout.qkv_bias_shard(d["bq"], d["bk"], d["bv"], N, r), "bf16") if bias else None
+    Wo = dev(layout.row_shard(d["Wo"], N, r), "bf16")
+    Z1, ws1 = shard.attn_shard(X, Wqkv, bqkv, Wo, batch, seq, H, N, r, causal)
+    ws2 = torch.zeros_like(ws1)
+    shard.qkv_projection(X, Wqkv, bqkv, batch, seq, H, H, N, r, ws2)
+    shard.head_attention(batch, seq, h, H, H, N, r, causal, ws2)
+    O2 = shard.attn_views(ws2, batch, seq, h, H, N)["o"]
+    Z2 = shard.row_parallel(O2, Wo, N, r)
+    torch.cuda.synchronize()
+    assert torch.equal(Z1, Z2)
+    v1, v2 = shard.attn_views(ws1, batch, seq, h, H, N), shard.attn_views(ws2, batch, seq, h, H, N)
+    for k in ("q", "k", "o"):
+        assert torch.equal(v1[k], v2[k]), k
+    assert torch.equal(v1["vt"][..., :seq], v2["vt"][..., :seq])
