@@ -137,6 +137,24 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Allocation-free MLP shard, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): tp_mlp_shard_fwd with Y_i = GeLU(X A_i + a_i) kept in a device scratch array
+ * of the library instead of a workspace. Same arguments (without the workspace), same two
+ * kernels, same bits, same errors; additionally TP_ERR_WORKSPACE when Y_i
+ * (tokens * ffn/N * element size, rounded up to 256 bytes) exceeds TP_NOALLOC_SCRATCH_BYTES.
+ * The call allocates nothing: the scratch is a static device array, one per device that runs
+ * the library, held until the process ends (its address is looked up once per device).
+ * Every call on a device shares that device's scratch, so calls that may overlap in time on
+ * one device (different streams, different threads) race: serialize them.
+ * ---------------------------------------------------------------------------------------- */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a_i,
+                                   const void* B_i, float* Z_i, int64_t tokens, int64_t hidden,
+                                   int64_t ffn, int n_shards, int rank, tp_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Backward pass of the MLP shard (llms.blog, "Partitioning the MLP Block": one all-reduce in
  * the backward pass, over the input gradients of the column-parallel layer). For the
  * forward Z_i = GeLU(P) B_r, P = X A_r + a_r, and the upstream gradient dZ of the block

@@ -30,6 +30,7 @@ STATUS_NAMES = {
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
     "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
+    "tp_mlp_shard_fwd_noalloc",
     "tp_mlp_bwd_workspace_bytes", "tp_mlp_shard_bwd",
     "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
     "tp_sp_residual_layernorm_fwd", "tp_all_gather_rows", "tp_gqa_attn_workspace_bytes",
@@ -78,6 +79,9 @@ def lib():
     L.tp_mlp_shard_fwd.restype = _int
     L.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                    _vp, _sz, _vp]
+    L.tp_mlp_shard_fwd_noalloc.restype = _int
+    L.tp_mlp_shard_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                           _int, _vp]
     L.tp_mlp_bwd_workspace_bytes.restype = _sz
     L.tp_mlp_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
     L.tp_mlp_shard_bwd.restype = _int
@@ -179,6 +183,13 @@ def tp_mlp_shard_fwd(X, A_i, a_i, B_i, Z_i, tokens, hidden, ffn, n_shards, rank,
     return lib().tp_mlp_shard_fwd(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(Z_i), tokens,
                                   hidden, ffn, n_shards, rank, dt, _ptr(workspace),
                                   workspace_bytes, _stream(stream))
+
+
+def tp_mlp_shard_fwd_noalloc(X, A_i, a_i, B_i, Z_i, tokens, hidden, ffn, n_shards, rank, dt,
+                             stream=None) -> int:
+    return lib().tp_mlp_shard_fwd_noalloc(_ptr(X), _ptr(A_i), _ptr(a_i), _ptr(B_i), _ptr(Z_i),
+                                          tokens, hidden, ffn, n_shards, rank, dt,
+                                          _stream(stream))
 
 
 def tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:

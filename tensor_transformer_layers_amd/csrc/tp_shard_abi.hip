@@ -394,6 +394,36 @@ tp_status launch_heads(int64_t batch, int64_t seq, int causal, const AttnLayout&
     return hip_status(tps::attention_fwd(a, s), "attention launch");
 }
 
+// ---- allocation-free MLP shard -------------------------------------------------------------
+// Scratch of tp_mlp_shard_fwd_noalloc: the hidden activation Y_i [tokens, ffn/N] that
+// tp_mlp_shard_fwd keeps in the caller's workspace. Each device holds its own copy of this
+// array (from the library's load until the process ends). In host code the name is only a
+// stand-in: kernels receive the device address from hipGetSymbolAddress, kept per device.
+constexpr size_t kScratchBytes = TP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// This device's address of the scratch array (looked up once per device, that device current).
+tp_status device_scratch(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(TP_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TP_OK;
+}
+
 // The exchange kernels read every input range while other lanes write the output: an output
 // that shares a byte with an input is rejected.
 tp_status check_no_overlap(const void* const* parts, int n_parts, size_t part_bytes, const void* out,
@@ -461,6 +491,36 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
     if (e != hipSuccess) return hip_status(e, "column-parallel kernel launch");
     // Row-parallel: Z_i = Y_i B_i, [tokens, hidden] fp32 partial.
     e = launch_row(workspace, B_i, Z_i, tokens, ffn / n_shards, hidden, dt, s);
+    return hip_status(e, "row-parallel kernel launch");
+}
+
+tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a_i,
+                                   const void* B_i, float* Z_i, int64_t tokens, int64_t hidden,
+                                   int64_t ffn, int n_shards, int rank, tp_dtype dt, void* stream)
+{
+    if (!X || !A_i || !B_i || !Z_i) return fail(TP_ERR_NULL, "X, A_i, B_i and Z_i must be non-NULL");
+    tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Z_i) ||
+        (a_i && !aligned16(a_i)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t need = tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt);
+    if (need > kScratchBytes)
+        return fail(TP_ERR_WORKSPACE,
+                    "Y_i of %zu bytes exceeds the %zu-byte device scratch of the allocation-free "
+                    "call; use tp_mlp_shard_fwd with a workspace", need, kScratchBytes);
+    st = check_device();
+    if (st != TP_OK) return st;
+    void* ws = nullptr;
+    st = device_scratch(&ws);
+    if (st != TP_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the same two launches as tp_mlp_shard_fwd, with Y_i in the device scratch
+    hipError_t e = launch_column(X, A_i, a_i, ws, tokens, hidden, ffn / n_shards, TP_ACT_GELU, dt, s);
+    if (e != hipSuccess) return hip_status(e, "column-parallel kernel launch");
+    e = launch_row(ws, B_i, Z_i, tokens, ffn / n_shards, hidden, dt, s);
     return hip_status(e, "row-parallel kernel launch");
 }
 

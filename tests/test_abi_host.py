@@ -325,3 +325,20 @@ def test_gemm_tile_info(overrides):
     overrides("gemm_tile=128x128w4")
     assert B.tp_gemm_tile_info(4096, 8192, 4096)[1:] == (128, 128, 4)
     assert B.tp_gemm_tile_info(0, 1, 1)[0] == 2
+
+
+def test_noalloc_mlp_validation():
+    """The allocation-free MLP shard validates like tp_mlp_shard_fwd and refuses a Y_i larger
+    than its 64 MiB device scratch (TP_ERR_WORKSPACE) before touching the device."""
+    a = dict(X=P, A_i=P, a_i=P, B_i=P, Z_i=P, tokens=32, hidden=1024, ffn=4096, n_shards=2,
+             rank=0, dt=F32)
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(a, X=None)) == 1
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(a, n_shards=3)) == 3
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(a, rank=2)) == 4
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(a, dt=7)) == 5
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(a, Z_i=P + 4)) == 6
+    # 8192 x 4096 bf16 = 64 MiB exactly fits; one more token row does not
+    big = dict(a, tokens=8192, hidden=1024, ffn=8192, dt=BF16)
+    assert B.tp_mlp_shard_fwd_noalloc(**big) not in (1, 2, 3, 4, 5, 6, 7)
+    assert B.tp_mlp_shard_fwd_noalloc(**dict(big, tokens=8193)) == 7
+    assert "scratch" in B.tp_last_error()
