@@ -101,11 +101,14 @@ def traffic_for(kernel: str, stage: str):
     return None
 
 
-def gemm_kernel_name(M: int, N: int, K: int, epi: int) -> str:
+def gemm_kernel_name(M: int, N: int, K: int, epi: int, four_waves_ok: bool = True) -> str:
     """The bf16 GEMM launched for an M x N x K product, named as the profiler names it:
-    gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>."""
+    gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>. The Q/K/V scatter (2) and the
+    fused sums (6, 7) always run eight waves (``four_waves_ok`` False for the latter)."""
     from tensor_transformer_layers_amd import binding
     _, tbm, tbn, nw = binding.tp_gemm_tile_info(M, N, K)
+    if epi == 2 or not four_waves_ok:
+        nw = 8
     wgrid = {(256, 256, 8): (2, 4), (256, 192, 8): (4, 2), (256, 128, 8): (4, 2),
              (128, 128, 8): (2, 4)}.get((tbm, tbn, nw), (2, 2))
     return "gemm_bf16_kernel<%d, %d, %d, %d, (tps::Epi)%d>" % (tbm, tbn, wgrid[0], wgrid[1], epi)
@@ -220,9 +223,154 @@ def _host32(t):
     return t.detach().to(torch.float32).cpu().numpy()
 
 
+# ---- the layer step ---------------------------------------------------------------------------
+def layer_stage_cost(w, stage: str):
+    """Algorithmic (FLOPs, HBM bytes) of one stage of rank 0's layer step, or None for a stage
+    of several kernels. Bytes count every operand once and every output once."""
+    T, h, N = w.tokens, w.hidden, w.n_shards
+    d = h // w.heads
+    wl = (w.heads // N) * d
+    Fl = w.ffn // N
+    fl = stage_flops(w)
+    peers = 4.0 * T * h * (N - 1)          # the other ranks' fp32 partials
+    return {
+        "qkv_projection": (fl["qkv_projection"], 2.0 * (T * h + 3 * wl * h + 3 * T * wl)),
+        "out_projection_sum": (fl["out_projection"], 2.0 * (T * wl + h * wl) + peers + 2.0 * T * h),
+        "mlp_column": (fl["mlp_column"], 2.0 * (T * h + Fl * h + Fl + T * Fl)),
+        "mlp_row": (fl["mlp_row"], 2.0 * (T * Fl + h * Fl) + 4.0 * T * h),
+        "mlp_row_sum": (fl["mlp_row"], 2.0 * (T * Fl + h * Fl) + peers + 4.0 * T * h),
+        "sum_attention": (0.0, 4.0 * T * h * N + 2.0 * T * h),
+        "sum_mlp": (0.0, 4.0 * T * h * N + 4.0 * T * h),
+    }.get(stage)
+
+
+def layer_stage_kernel(w, stage: str) -> str:
+    """The kernel of a one-kernel stage, named as the profiler names it."""
+    T, h, N = w.tokens, w.hidden, w.n_shards
+    wl = (w.heads // N) * (h // w.heads)
+    Fl = w.ffn // N
+    return {"qkv_projection": lambda: gemm_kernel_name(T, 3 * wl, h, 2),
+            "out_projection_sum": lambda: gemm_kernel_name(T, h, wl, 7, four_waves_ok=False),
+            "mlp_column": lambda: gemm_kernel_name(T, Fl, h, 0),
+            "mlp_row": lambda: gemm_kernel_name(T, h, Fl, 1),
+            "mlp_row_sum": lambda: gemm_kernel_name(T, h, Fl, 6, four_waves_ok=False),
+            "sum_attention": lambda: "sum_kernel<%d, 4, true>" % N,
+            "sum_mlp": lambda: "sum_kernel<%d, 4, false>" % N}[stage]()
+
+
+def stage_roofline(w, stage: str, us: float, traffic=None) -> dict:
+    """The stage's kernel against the roofline that bounds it: HBM when its algorithmic bytes
+    take longer at 8 TB/s than its FLOPs at the bf16 MFMA peak, else MFMA."""
+    flops, nbytes = layer_stage_cost(w, stage)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    name = layer_stage_kernel(w, stage)
+    if t_hbm > t_mfma:
+        r = _roof_hbm(name, nbytes, us)
+        if flops:
+            r["mfma_frac"] = flops / us / 1e6 / PEAK_BF16_TFLOPS
+    else:
+        r = _roof_mfma(name, flops, us, PEAK_BF16_TFLOPS)
+        r["algorithmic_bytes"] = nbytes
+    r["stage"] = stage
+    r["traffic"] = traffic_for(name, stage) if traffic is None else traffic
+    return r
+
+
+def time_layer_step(drv, step, w, fl, steps: int, warmup: int, stream) -> dict:
+    """Warm-up, then ``steps`` instrumented steps (an event after each stage) for the per-stage
+    medians, then ``steps`` timed steps carrying only the two events around the dominant
+    kernel (the longest one-kernel stage), bracketed by device synchronizations."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stages = drv.STAGES
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        marks = iter(ev[i][1:])
+        step(on_stage=lambda name, m=marks: next(m).record(stream))
+    torch.cuda.synchronize()
+    # the median over the steps of each stage (one host stall between two launches would
+    # otherwise lengthen the stage it falls into, in the mean)
+    stage_us = {s: float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3
+                                    for i in range(steps)]))
+                for j, s in enumerate(stages)}
+    single = [s for s in stages if layer_stage_cost(w, s) is not None]
+    dom = max(single, key=lambda s: stage_us[s])
+    before = stages[stages.index(dom) - 1] if stages.index(dom) > 0 else None
+    dev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+
+    def mark_dominant(name, pair):
+        if name == before:
+            pair[0].record(stream)
+        elif name == dom:
+            pair[1].record(stream)
+
+    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        t_start = time.perf_counter()
+        for i in range(steps):
+            if before is None:
+                dev[i][0].record(stream)
+            step(on_stage=lambda name, pair=dev[i]: mark_dominant(name, pair))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    dom_us = sum(a.elapsed_time(b) for a, b in dev) * 1e3 / steps
+    breakdown = {}
+    for s in stages:
+        c = layer_stage_cost(w, s)
+        e = {"us": stage_us[s]}
+        if s == "attention_shard":
+            f = fl["qkv_projection"] + fl["attention"] + fl["out_projection"]
+            e["tflops"] = f / stage_us[s] / 1e6
+        elif s == "attention":
+            e["tflops"] = fl["attention"] / stage_us[s] / 1e6
+        elif c is not None:
+            if c[0]:
+                e["tflops"] = c[0] / stage_us[s] / 1e6
+            e["gbs"] = c[1] / stage_us[s] / 1e3
+        breakdown[s] = e
+    return {"ms_per_step": elapsed / steps * 1e3, "event_ms": sum(stage_us.values()) / 1e3,
+            "stage_us": stage_us, "breakdown": breakdown,
+            "roofline": stage_roofline(w, dom, dom_us), "clock": clock.summary()}
+
+
 # ---- the measured workloads other than the layer step -----------------------------------------
+def _time_graph(fn, reps: int, warmup: int = 3):
+    """Average microseconds per fn() when ``reps`` calls are captured once in a HIP graph and
+    the graph is replayed (launch-bound work: the host's per-call overhead is left out).
+    Returns (us, graph)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (n * reps), g
+
+
 def measure_mlp_f32(reps: int = 200, warmup: int = 20):
-    """fp32 MLP block GeLU(XA + a)B: both shards of N = 2 and their on-device sum."""
+    """fp32 MLP block GeLU(XA + a)B: both shards of N = 2 and their on-device sum. Each call
+    is a few microseconds of GPU work, less than the host needs to issue it, so the block and
+    its kernels are timed as replays of a captured HIP graph (the eager rate is reported too);
+    every replay's output is checked bitwise against the eager result."""
     import torch
     from synth import WORKLOADS, mlp_inputs
     from tensor_transformer_layers_amd import layout, shard
@@ -243,13 +391,24 @@ def measure_mlp_f32(reps: int = 200, warmup: int = 20):
             shard.mlp_shard(X, W[r]["A"], W[r]["a"], W[r]["B"], N, r, Z=Zs[r], workspace=ws[r])
         shard.sum_partials(Zs, out=Z)
 
-    us = _time_events(block, reps, warmup, stream)
+    eager_us = _time_events(block, reps, warmup, stream)
+    block()
+    torch.cuda.synchronize()
+    Z_eager = Z.clone()
+    us, gblock = _time_graph(block, 20)
+    for _ in range(3):           # every replay reproduces the eager bits
+        Z.zero_()
+        torch.cuda.synchronize()
+        gblock.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(Z, Z_eager):
+            raise RuntimeError("graph replay of the fp32 block differs from the eager result")
     fl = F // N
     Y = shard.mlp_hidden_view(ws[0], T, fl, torch.float32)
-    col_us = _time_events(lambda: shard.column_parallel(X, W[0]["A"], W[0]["a"], N, 0, gelu=True,
-                                                        Y=Y), reps, warmup, stream)
-    row_us = _time_events(lambda: shard.row_parallel(Y, W[0]["B"], N, 0, Z=Zs[0]), reps, warmup,
-                          stream)
+    col_us, _ = _time_graph(lambda: shard.column_parallel(X, W[0]["A"], W[0]["a"], N, 0,
+                                                          gelu=True, Y=Y), 50)
+    row_us, _ = _time_graph(lambda: shard.row_parallel(Y, W[0]["B"], N, 0, Z=Zs[0]), 50)
+    sum_us, _ = _time_graph(lambda: shard.sum_partials(Zs, out=Z), 50)
     block()
     torch.cuda.synchronize()
     flops = 2 * 2.0 * T * h * F
@@ -257,12 +416,14 @@ def measure_mlp_f32(reps: int = 200, warmup: int = 20):
     # plus a 32-row activation: bound by memory and latency, not by the matrix cores
     col_bytes = 4.0 * (T * h + fl * h + fl + T * fl)
     row_bytes = 4.0 * (T * fl + h * fl + T * h)
+    mb = 1 if T <= 16 else (2 if T <= 32 else 4)
     dom, dom_us, dom_b = ("column", col_us, col_bytes) if col_us >= row_us else ("row", row_us, row_bytes)
-    kname = "gemm_f32_kernel<32, 64, (tps::Epi)%d>" % (0 if dom == "column" else 1)
+    kname = "gemm_f32_skinny_kernel<%d, (tps::Epi)%d>" % (mb, 0 if dom == "column" else 1)
     out = {"workload": w.name, "unit": "block: %d shards + on-device sum" % N, "dtype": "f32",
-           "us": us, "tflops": flops / us / 1e6, "peak": PEAK_FP32_TFLOPS,
+           "us": us, "timing": "HIP graph replay of 20 blocks",
+           "eager_us": eager_us, "tflops": flops / us / 1e6, "peak": PEAK_FP32_TFLOPS,
            "frac_peak": flops / us / 1e6 / PEAK_FP32_TFLOPS,
-           "per_shard_kernels_us": {"column": col_us, "row": row_us},
+           "per_shard_kernels_us": {"column": col_us, "row": row_us}, "sum_us": sum_us,
            "roofline": dict(_roof_hbm(kname, dom_b, dom_us),
                             mfma_frac=2.0 * T * h * fl / dom_us / 1e6 / PEAK_FP32_TFLOPS)}
     return out, {"d": d, "Z": _host(Z)}
@@ -729,87 +890,35 @@ def main() -> int:
           for r in range(N)]
     za_other, zm_other = za[1:], zm[1:]
     del za[0], zm[0], Hs
-    drv = shard.LayerShard(w.batch, w.seq, h, H, F, N, rank=0, causal=w.causal)
     R0 = ranks[0]
     stream = torch.cuda.current_stream()
-
-    def step(on_stage=None):
-        return drv.forward(X, R0["Wqkv"], R0["bqkv"], R0["Wo"], R0["A"], R0["a"], R0["B"],
-                           za_other, zm_other, stream=stream, on_stage=on_stage)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log("warmup done (%d steps); timing %d steps" % (args.warmup, args.steps))
-
-    stages = shard.LayerShard.STAGES
-    # Per-stage breakdown from as many instrumented steps, run before the timed ones: an event
-    # after each stage's launches. Each event record leaves the stream idle for a few
-    # microseconds, so the timed steps carry only the two events around the dominant kernel.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        marks = iter(ev[i][1:])
-        step(on_stage=lambda name, m=marks: next(m).record(stream))
-    torch.cuda.synchronize()
-    stage_us = {s: 0.0 for s in stages}
-    for i in range(args.steps):
-        for j, s in enumerate(stages):
-            stage_us[s] += ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 / args.steps
-    event_ms = sum(stage_us.values()) / 1e3
-    # Dominant kernel: the slower of the two MLP GEMMs (each stage is one kernel launch).
-    dom = max(("mlp_column", "mlp_row"), key=lambda s: stage_us[s])
-    before = stages[stages.index(dom) - 1]
-
-    dev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-
-    def mark_dominant(name, pair):
-        if name == before:
-            pair[0].record(stream)
-        elif name == dom:
-            pair[1].record(stream)
-
-    torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t_start = time.perf_counter()
-        for i in range(args.steps):
-            step(on_stage=lambda name, pair=dev[i]: mark_dominant(name, pair))
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t_start
-    out = drv.out
-    if not bool(torch.isfinite(out).all()):
-        log("non-finite output")
-        return 1
-    ms_per_step = elapsed / args.steps * 1e3
-    dom_us = sum(a.elapsed_time(b) for a, b in dev) * 1e3 / args.steps
-
     fl = stage_flops(w)
     flop_step = sum(fl.values())
+    # Two forms of the same step, the same bits of H and of the output: the unfused one writes
+    # the rank's fp32 partials and sums them with tp_sum_partials; the fused one adds the
+    # peers' partials in the row-parallel products' epilogues (tp_row_parallel_sum_fwd).
+    variants = {}
+    for fused in (False, True):
+        name = "fused_sums" if fused else "separate_sums"
+        log("%s: warmup (%d steps), instrumented and timed steps (%d each)"
+            % (name, args.warmup, args.steps))
+        drv = shard.LayerShard(w.batch, w.seq, h, H, F, N, rank=0, causal=w.causal, fused=fused)
+        variants[name] = time_layer_step(drv, lambda drv=drv, on_stage=None: drv.forward(
+            X, R0["Wqkv"], R0["bqkv"], R0["Wo"], R0["A"], R0["a"], R0["B"], za_other, zm_other,
+            stream=stream, on_stage=on_stage), w, fl, args.steps, args.warmup, stream)
+        variants[name]["drv"] = drv
+    a_, b_ = variants["separate_sums"]["drv"], variants["fused_sums"]["drv"]
+    if not (torch.equal(a_.out, b_.out) and torch.equal(a_.H, b_.H)):
+        log("the fused and unfused steps differ")
+        return 1
+    if not bool(torch.isfinite(a_.out).all()):
+        log("non-finite output")
+        return 1
+    best = min(variants, key=lambda k: variants[k]["ms_per_step"])
+    v = variants[best]
+    ms_per_step = v["ms_per_step"]
     value = flop_step / (ms_per_step * 1e-3) / 1e12
-    sum_bytes = {"sum_attention": (N * 4 + 2) * T * h, "sum_mlp": (N * 4 + 4) * T * h}
-    attn_flops = fl["qkv_projection"] + fl["attention"] + fl["out_projection"]
-    breakdown = {
-        "attention_shard": {"us": stage_us["attention_shard"],
-                            "tflops": attn_flops / stage_us["attention_shard"] / 1e6},
-        "mlp_column": {"us": stage_us["mlp_column"],
-                       "tflops": fl["mlp_column"] / stage_us["mlp_column"] / 1e6},
-        "mlp_row": {"us": stage_us["mlp_row"], "tflops": fl["mlp_row"] / stage_us["mlp_row"] / 1e6},
-        "sum_attention": {"us": stage_us["sum_attention"],
-                          "gbs": sum_bytes["sum_attention"] / stage_us["sum_attention"] / 1e3},
-        "sum_mlp": {"us": stage_us["sum_mlp"], "gbs": sum_bytes["sum_mlp"] / stage_us["sum_mlp"] / 1e3},
-    }
-    M, Nn, K = (T, Fl, h) if dom == "mlp_column" else (T, h, Fl)
-    kname = gemm_kernel_name(M, Nn, K, 0 if dom == "mlp_column" else 1)
-    achieved = fl[dom] / (dom_us * 1e-6) / 1e12
-    roofline = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": traffic_for(kname, dom)}
-    shard_tflops = flop_step / ((stage_us["attention_shard"] + stage_us["mlp_column"]
-                                 + stage_us["mlp_row"]) * 1e-6) / 1e12
-
+    unf = variants["separate_sums"]
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -819,22 +928,31 @@ def main() -> int:
                    "heads": H, "head_dim": h // H, "ffn": F, "n_shards": N, "rank": 0,
                    "causal": w.causal, "flop_per_step": flop_step,
                    "step": "attention shard, sum of %d partials, MLP shard, sum of %d partials"
-                           % (N, N)},
+                           % (N, N),
+                   "step_form": best},
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "shard_tflops": shard_tflops,
-        "event_ms_per_step": event_ms,
-        "breakdown": breakdown,
-        "roofline": roofline,
-        "clock": clock.summary(),
+        # the shard kernels alone (the separate-sums form, whose sums are kernels of their own)
+        "shard_tflops": (flop_step / ((unf["stage_us"]["attention_shard"]
+                                       + unf["stage_us"]["mlp_column"]
+                                       + unf["stage_us"]["mlp_row"]) * 1e-6) / 1e12),
+        "event_ms_per_step": v["event_ms"],
+        "breakdown": v["breakdown"],
+        "roofline": v["roofline"],
+        "clock": v["clock"],
+        "step_forms": {k: {"ms_per_step": x["ms_per_step"],
+                           "tflops": flop_step / (x["ms_per_step"] * 1e-3) / 1e12,
+                           "breakdown": x["breakdown"], "roofline": x["roofline"],
+                           "clock": x["clock"]} for k, x in variants.items()},
         "cpu_baseline": None,
     }
-    layer = {"w": w, "d": d, "gpu": {"H": _host(drv.H), "Z_attn": _host(drv.Z_attn),
-                                     "Z_mlp": _host(drv.Z_mlp), "out": _host(drv.out)}}
+    layer = {"w": w, "d": d, "gpu": {"H": _host(a_.H), "Z_attn": _host(a_.Z_attn),
+                                     "Z_mlp": _host(a_.Z_mlp), "out": _host(a_.out)}}
     configs = {WORKLOAD: {"workload": WORKLOAD, "unit": "one rank's layer step (rank 0 of %d)" % N,
                           "dtype": "bf16", "us": ms_per_step * 1e3, "tflops": value,
                           "peak": PEAK_BF16_TFLOPS, "frac_peak": value / PEAK_BF16_TFLOPS,
-                          "roofline": roofline}}
-    del ranks, za_other, zm_other, drv, X
+                          "step_form": best, "roofline": v["roofline"]}}
+    del variants, a_, b_, v
+    del ranks, za_other, zm_other, X
     torch.cuda.empty_cache()
     ctx = {}
     if not args.no_next_rows:

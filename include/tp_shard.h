@@ -112,6 +112,31 @@ tp_status tp_row_parallel_fwd(const void* X_i, const void* W_i, float* Z_i, int6
                               tp_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Row-parallel linear layer with the all-reduce's sum fused into it (same page, 2. Row-
+ * Parallel Linear Layer: the output is the sum of the N partials X_q W_q). Rank r computes
+ * its product X_i W_i and, in the same kernel, adds the other ranks' partials to it:
+ *   Z = Z_0 + Z_1 + ... + Z_{N-1},   Z_r = X_i W_i (this rank's product, never stored)
+ * in fp32, in the fixed order 0, 1, ..., N-1 with Z_r in its place, stored as out_dt: the same
+ * bits as tp_row_parallel_fwd into Z_r followed by tp_sum_partials. The rank's own partial
+ * neither goes to memory nor comes back (on one device the other partials are resident
+ * inputs; across devices they are what the exchange delivers).
+ *
+ *   X_i      [rows, in_features/N]          bf16
+ *   W_i      [out_features, in_features/N]  bf16
+ *   Z_parts  HOST array of n_shards DEVICE pointers, each [rows, out_features] fp32 (16-byte
+ *            aligned); entry rank is not read (may be NULL), a NULL elsewhere is a missing
+ *            rank (TP_ERR_NULL)
+ *   Z        [rows, out_features] out_dt (fp32, or bf16 rounded to nearest even); must not
+ *            overlap any input (TP_ERR_ALIAS)
+ * dt: TP_BF16 only; n_shards at most 8 (TP_ERR_SHAPE). Other rules as for
+ * tp_row_parallel_fwd.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_row_parallel_sum_fwd(const void* X_i, const void* W_i, const float* const* Z_parts,
+                                  void* Z, tp_dtype out_dt, int64_t rows, int64_t in_features,
+                                  int64_t out_features, int n_shards, int rank, tp_dtype dt,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * MLP shard: Z_i = GeLU(X A_i + a_i) B_i          (ai360xpert.com "How It Works", steps 1-2;
  *                                                  llms.blog MLP block, steps 1-3)
  * GeLU is the exact form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).

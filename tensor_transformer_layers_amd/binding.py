@@ -29,7 +29,8 @@ STATUS_NAMES = {
 
 # Every symbol include/tp_shard.h declares.
 EXPORTED = (
-    "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
+    "tp_column_parallel_fwd", "tp_row_parallel_fwd", "tp_row_parallel_sum_fwd",
+    "tp_mlp_workspace_bytes", "tp_mlp_shard_fwd",
     "tp_mlp_shard_fwd_noalloc",
     "tp_mlp_bwd_workspace_bytes", "tp_mlp_shard_bwd",
     "tp_swiglu_workspace_bytes", "tp_swiglu_shard_fwd", "tp_reduce_scatter_partials",
@@ -74,6 +75,9 @@ def lib():
                                          _int, _vp]
     L.tp_row_parallel_fwd.restype = _int
     L.tp_row_parallel_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]
+    L.tp_row_parallel_sum_fwd.restype = _int
+    L.tp_row_parallel_sum_fwd.argtypes = [_vp, _vp, ctypes.POINTER(_vp), _vp, _int, _i64, _i64,
+                                          _i64, _int, _int, _int, _vp]
     L.tp_mlp_workspace_bytes.restype = _sz
     L.tp_mlp_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int]
     L.tp_mlp_shard_fwd.restype = _int
@@ -172,6 +176,13 @@ def tp_row_parallel_fwd(X_i, W_i, Z_i, rows, in_features, out_features, n_shards
                         stream=None) -> int:
     return lib().tp_row_parallel_fwd(_ptr(X_i), _ptr(W_i), _ptr(Z_i), rows, in_features,
                                      out_features, n_shards, rank, dt, _stream(stream))
+
+
+def tp_row_parallel_sum_fwd(X_i, W_i, Z_parts, Z, out_dt, rows, in_features, out_features,
+                            n_shards, rank, dt, stream=None) -> int:
+    return lib().tp_row_parallel_sum_fwd(_ptr(X_i), _ptr(W_i), _ptr_array(Z_parts), _ptr(Z),
+                                         out_dt, rows, in_features, out_features, n_shards, rank,
+                                         dt, _stream(stream))
 
 
 def tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt) -> int:

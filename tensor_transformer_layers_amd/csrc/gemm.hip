@@ -10,6 +10,10 @@
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
 //             per head, V written transposed for the attention kernel's P V product, Q
 //             multiplied by q_scale (the softmax's scale) before it is rounded.
+//   SumF32    Z = sum_q Z_q with Z_rank = X_i W_i       row-parallel layer with the partial sum
+//   SumBf16   (the all-reduce's sum) fused: the other ranks' fp32 partials are read in the
+//             epilogue and added in the fixed order q = 0 .. N-1, the rank's own product in
+//             its place, so the rank's partial is never written; fp32 or bf16 output.
 //   SwiGlu    A_i = SiLU(X W_gate,i) * (X W_up,i)       gated column-parallel MLP layer: the
 //             block's B slab interleaves gate and up rows in 32-row blocks (loaded from the
 //             two weights), so each wave's pairs of 32-column MFMA blocks hold the gate and
@@ -305,6 +309,48 @@ __device__ __forceinline__ void store_tile(const GemmProblem& p, f32x16 (&acc)[W
         __syncthreads();
         if constexpr (EPI == Epi::Qkv) {
             qkv_write<WTN, RR, PITCH>(p, region, r0 + rr * RR, c0, lane);
+        } else if constexpr (EPI == Epi::SumF32 || EPI == Epi::SumBf16) {
+            // SU vectors per pass (four with four waves, two with eight: the same bytes in
+            // flight per compute unit): the other partials' loads of all of them are issued
+            // before any add (streamed once: non-temporal), then each vector is summed in the
+            // order q = 0 .. n_parts-1 with this product at q = part_rank -- the same fp32
+            // adds, in the same order, as the partial-sum kernel.
+            constexpr int SU = NW == 4 ? 4 : 2;
+            static_assert(PER_LANE % SU == 0, "passes");
+#pragma unroll
+            for (int t = 0; t < PER_LANE; t += SU) {
+                f32x4 own[SU], v[SU][kMaxSumParts];
+                int64_t off[SU];
+                bool ok[SU];
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    const int idx = lane + 64 * (t + u);
+                    const int row = idx / V4, v4 = idx - row * V4;
+                    const int m = r0 + rr * RR + row, n = c0 + v4 * 4;
+                    ok[u] = m < p.M && n < p.N;
+                    own[u] = *reinterpret_cast<const f32x4*>(region + row * PITCH + v4 * 16);
+                    off[u] = (int64_t)m * p.ldc + n;
+#pragma unroll
+                    for (int q = 0; q < kMaxSumParts; ++q)
+                        if (ok[u] && q < p.n_parts && q != p.part_rank)
+                            v[u][q] = __builtin_nontemporal_load(
+                                reinterpret_cast<const f32x4*>(p.part[q] + off[u]));
+                }
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    if (!ok[u]) continue;
+                    f32x4 acc = p.part_rank == 0 ? own[u] : v[u][0];
+#pragma unroll
+                    for (int q = 1; q < kMaxSumParts; ++q)
+                        if (q < p.n_parts) acc += q == p.part_rank ? own[u] : v[u][q];
+                    if constexpr (EPI == Epi::SumF32)
+                        __builtin_nontemporal_store(
+                            acc, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + off[u]));
+                    else
+                        __builtin_nontemporal_store(
+                            to_bf16x4(acc), reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.C) + off[u]));
+                }
+            }
         } else {
 #pragma unroll
             for (int t = 0; t < PER_LANE; ++t) {
@@ -801,6 +847,73 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
     }
 }
 
+// ---- fp32 GEMM for few rows (M <= 64) ------------------------------------------------------
+// With a handful of token rows (32 in the fp32 worked example) the product streams its weight
+// once and does little arithmetic per byte; a grid of 32 x 64 tiles leaves most compute units
+// idle and each workgroup walks the whole K range alone. Here a workgroup owns 16 output
+// columns (one MFMA block-column) for all M rows and its sixteen waves split K: each wave loads
+// the 16-byte chunks of its K range straight into MFMA operands (lane l: weight row (l & 15)
+// or activation row (l & 15), the 4 consecutive K values at 4 (l >> 4) of a 16-wide chunk,
+// fed to 4 consecutive MFMAs as in gemm_f32_kernel), the waves' partial accumulators are
+// added through LDS in the fixed order 0 .. 15, and the epilogue runs once per output vector.
+// Sixteen waves put a wave's whole K range (128 values at K = 2048) in flight at once.
+template <int MB, Epi EPI>
+__global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
+{
+    constexpr int NWV = 16;                     // waves
+    constexpr int UNR = MB <= 2 ? 8 : 4;        // 16-wide K chunks in flight per wave
+    __shared__ f32x4 part[NWV][MB][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int fr = lane & 15, fg = lane >> 4;
+    const float* __restrict__ gA = reinterpret_cast<const float*>(p.A);
+    const float* __restrict__ gB = reinterpret_cast<const float*>(p.B);
+    const int nrow = n0 + fr;                   // the weight row (output column) this lane loads
+    const bool nin = nrow < p.N;
+    const int chunks = (p.K + 15) / 16;
+    const int c_lo = wave * chunks / NWV, c_hi = (wave + 1) * chunks / NWV;
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = c_lo; c0 < c_hi; c0 += UNR) {
+        u32x4 rb[UNR], ra[UNR][MB];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int k = (c0 + u) * 16 + 4 * fg;
+            const bool kin = c0 + u < c_hi && k < p.K;   // K % 4 == 0: a chunk is in or out
+            rb[u] = kin && nin ? ld16(gB + (int64_t)nrow * p.ldb + k) : zero16();
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = mb * 16 + fr;
+                ra[u][mb] = kin && m < p.M ? ld16(gA + (int64_t)m * p.lda + k) : zero16();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const f32x4 fb = __builtin_bit_cast(f32x4, rb[u]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = mfma16x16x4f32(fb[t], __builtin_bit_cast(f32x4, ra[u][mb])[t], acc[mb]);
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) part[wave][mb][lane] = acc[mb];
+    __syncthreads();
+    if (wave != 0) return;
+    // lane holds C[m][n0 + 4 fg + i], i = 0..3, m = 16 mb + fr
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        f32x4 v = part[0][mb][lane];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) v += part[w][mb][lane];
+        const int m = mb * 16 + fr, n = n0 + 4 * fg;
+        if (m < p.M && n < p.N) store_out<EPI, float>(p, m, n, v);
+    }
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
@@ -816,6 +929,8 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         case Epi::Qkv: TPS_LAUNCH(Epi::Qkv) break;
         case Epi::Bias: TPS_LAUNCH(Epi::Bias) break;
         case Epi::GeluGrad: TPS_LAUNCH(Epi::GeluGrad) break;
+        case Epi::SumF32: TPS_LAUNCH(Epi::SumF32) break;
+        case Epi::SumBf16: TPS_LAUNCH(Epi::SumBf16) break;
         case Epi::SwiGlu:
             if constexpr ((BN / WN / 32) % 2 == 0) {
                 TPS_LAUNCH(Epi::SwiGlu)
@@ -883,6 +998,10 @@ static bool tile_override(GemmTile& t, bool& w4)
 // 2500 us at 2048 x 12288 x 49152 and 1068 against 1175 us at K = 24576.
 static bool prefer_four_waves(int M, int N, int K, GemmTile t, Epi epi)
 {
+    // The fused partial sum streams N - 1 partials in its epilogue, which one wave per SIMD
+    // leaves latency-bound (4096 x 8192 x 4096 with 8 partials: 606 us against 405 us for the
+    // product and a separate sum): it keeps eight waves.
+    if (epi == Epi::SumF32 || epi == Epi::SumBf16) return false;
     if (t.bm != 256 || (t.bn != 256 && t.bn != 192) || epi == Epi::Qkv || K < 2048) return false;
     const long tiles = (long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     return tiles >= 512;
@@ -1073,8 +1192,34 @@ hipError_t qkv_reduce_scatter(const GemmProblem& p, const float* parts, hipStrea
     return hipGetLastError();
 }
 
+template <int MB>
+hipError_t launch_f32_skinny(const GemmProblem& p, Epi epi, hipStream_t s)
+{
+    dim3 grid((unsigned)((p.N + 15) / 16)), block(1024);
+    switch (epi) {
+        case Epi::BiasGelu:
+            hipLaunchKernelGGL((gemm_f32_skinny_kernel<MB, Epi::BiasGelu>), grid, block, 0, s, p);
+            break;
+        case Epi::F32:
+            hipLaunchKernelGGL((gemm_f32_skinny_kernel<MB, Epi::F32>), grid, block, 0, s, p);
+            break;
+        case Epi::Bias:
+            hipLaunchKernelGGL((gemm_f32_skinny_kernel<MB, Epi::Bias>), grid, block, 0, s, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Up to 64 rows: the skinny kernel (all rows per workgroup, K split over its waves); beyond,
+// 32 x 64 tiles. The fp32 worked example (32 x 1024 x 2048 and 32 x 2048 x 1024): 20 and 34 us
+// per product on the tiles, against the skinny kernel's times in the benchmark's configs.
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)
 {
+    if (p.M <= 16) return launch_f32_skinny<1>(p, epi, s);
+    if (p.M <= 32) return launch_f32_skinny<2>(p, epi, s);
+    if (p.M <= 64) return launch_f32_skinny<4>(p, epi, s);
     constexpr int BM = 32, BN = 64;
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     dim3 grid(tiles), block(kThreads);

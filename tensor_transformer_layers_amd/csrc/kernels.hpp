@@ -28,7 +28,12 @@ enum class Epi : int {
     Bias = 3,       // C = acc + bias[n]         stored in the GEMM's element type
     SwiGlu = 4,     // C = SiLU(X B^T) * (X B2^T), N output features, bf16 (gated MLP)
     GeluGrad = 5,   // C = acc * GeLU'(aux[m, n]), bf16 (backward through the activation)
+    SumF32 = 6,     // C = sum_q P_q, P_rank = acc, P_q = part[q] otherwise: fp32 (the partial sum
+    SumBf16 = 7,    //     of the row-parallel layer fused into its epilogue), or bf16
 };
+
+// Partials a Sum epilogue adds: at most this many shards.
+constexpr int kMaxSumParts = 8;
 
 struct GemmProblem {
     const void* A;        // [M, K] row-major, leading dimension lda (elements)
@@ -55,6 +60,10 @@ struct GemmProblem {
     // C + s * split_stride (elements). Zero or one: no split.
     int k_splits;
     int64_t split_stride;
+    // SumF32 / SumBf16: n_parts partials [M, N] fp32 with leading dimension ldc; part[part_rank]
+    // is this product (never read), the others are added in the fixed order 0 .. n_parts-1.
+    const float* part[kMaxSumParts];
+    int n_parts, part_rank;
 };
 
 // Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).

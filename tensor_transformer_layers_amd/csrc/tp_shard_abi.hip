@@ -673,6 +673,48 @@ tp_status tp_row_parallel_fwd(const void* X_i, const void* W_i, float* Z_i, int6
     return hip_status(e, "row-parallel kernel launch");
 }
 
+tp_status tp_row_parallel_sum_fwd(const void* X_i, const void* W_i, const float* const* Z_parts,
+                                  void* Z, tp_dtype out_dt, int64_t rows, int64_t in_features,
+                                  int64_t out_features, int n_shards, int rank, tp_dtype dt,
+                                  void* stream)
+{
+    if (!X_i || !W_i || !Z || !Z_parts) return fail(TP_ERR_NULL, "X_i, W_i, Z_parts and Z must be non-NULL");
+    if (dt != TP_BF16) return fail(TP_ERR_DTYPE, "the fused row-parallel sum supports TP_BF16 inputs only");
+    if (out_dt != TP_F32 && out_dt != TP_BF16) return fail(TP_ERR_DTYPE, "out_dt %d not supported", (int)out_dt);
+    tp_status st = validate_linear(rows, in_features, out_features, n_shards, rank, dt, false);
+    if (st != TP_OK) return st;
+    if (n_shards > tps::kMaxSumParts)
+        return fail(TP_ERR_SHAPE, "n_shards=%d above %d for the fused sum", n_shards, tps::kMaxSumParts);
+    if (!aligned16(X_i) || !aligned16(W_i) || !aligned16(Z))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t pbytes = (size_t)(rows * out_features) * 4;
+    const size_t zbytes = (size_t)(rows * out_features) * dt_size(out_dt);
+    for (int q = 0; q < n_shards; ++q) {
+        if (q == rank) continue;
+        if (!Z_parts[q]) return fail(TP_ERR_NULL, "partial %d is NULL (missing rank)", q);
+        if (!aligned16(Z_parts[q])) return fail(TP_ERR_ALIGN, "partial %d is not 16-byte aligned", q);
+        if (overlap(Z, zbytes, Z_parts[q], pbytes))
+            return fail(TP_ERR_ALIAS, "Z overlaps partial %d", q);
+    }
+    const int64_t k = in_features / n_shards;
+    if (overlap(Z, zbytes, X_i, (size_t)(rows * k) * 2) ||
+        overlap(Z, zbytes, W_i, (size_t)(out_features * k) * 2))
+        return fail(TP_ERR_ALIAS, "Z overlaps X_i or W_i");
+    st = check_device();
+    if (st != TP_OK) return st;
+    tps::GemmProblem g{};
+    g.A = X_i; g.lda = k;
+    g.B = W_i; g.ldb = k;
+    g.C = Z; g.ldc = out_features;
+    g.M = (int)rows; g.N = (int)out_features; g.K = (int)k;
+    g.n_parts = n_shards;
+    g.part_rank = rank;
+    for (int q = 0; q < n_shards; ++q) g.part[q] = q == rank ? nullptr : Z_parts[q];
+    return hip_status(tps::gemm_bf16(g, out_dt == TP_BF16 ? tps::Epi::SumBf16 : tps::Epi::SumF32,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                      "fused row-parallel sum kernel launch");
+}
+
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int n_heads,
                                int n_shards, tp_dtype dt)
 {

@@ -121,6 +121,35 @@ def row_parallel(X_i: torch.Tensor, W_i: torch.Tensor, n_shards: int, rank: int,
     return Z
 
 
+def row_parallel_sum(X_i: torch.Tensor, W_i: torch.Tensor,
+                     partials: Sequence[Optional[torch.Tensor]], n_shards: int, rank: int,
+                     out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Z = sum over the N ranks of the row-parallel partials, this rank's X_i W_i computed and
+    added in the same kernel (tp_row_parallel_sum_fwd). ``partials`` holds N entries: the
+    other ranks' fp32 partials [rows, out], and None (or anything: it is not read) at
+    ``rank``. The same bits as row_parallel followed by sum_partials."""
+    _need_2d("X_i", X_i, torch.bfloat16)
+    rows, k = X_i.shape
+    width = _need_2d("W_i", W_i)[0]
+    _need("W_i", W_i, (width, k), torch.bfloat16)
+    if len(partials) != n_shards:
+        raise ValueError("%d partials given for %d shards" % (len(partials), n_shards))
+    peers = [None if q == rank else partials[q] for q in range(n_shards)]
+    for q, t in enumerate(peers):
+        _need("partial %d" % q, t, (rows, width), torch.float32, optional=q == rank)
+    if out is None:
+        out = torch.empty(rows, width, dtype=out_dtype, device=X_i.device)
+    if out.dtype not in _DT:
+        raise ValueError("out has dtype %s, expected float32 or bfloat16" % out.dtype)
+    _need("out", out, (rows, width), out.dtype)
+    _require_cuda(X_i, W_i, out, *[t for t in peers if t is not None])
+    st = B.tp_row_parallel_sum_fwd(X_i, W_i, peers, out, _DT[out.dtype], rows, k * n_shards,
+                                   width, n_shards, rank, B.TP_BF16, _stream(stream))
+    B.check(st)
+    return out
+
+
 # ---- MLP ------------------------------------------------------------------------------------
 def mlp_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, dtype, device="cuda"):
     nbytes = B.tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, _DT[dtype])
@@ -472,23 +501,33 @@ class LayerShard:
     The other ranks' partials are supplied by the caller (on one device they are computed
     by running the other shards); each block ends in exactly one partial sum. Buffers are
     allocated once so that repeated calls allocate nothing.
+
+    ``fused=True`` runs each block's row-parallel product with the partial sum in its
+    epilogue (tp_row_parallel_sum_fwd): the rank's own partials are never written, and H and
+    the output are the same bits as the unfused step's.
     """
 
+    STAGES_UNFUSED = ("attention_shard", "sum_attention", "mlp_column", "mlp_row", "sum_mlp")
+    STAGES_FUSED = ("qkv_projection", "attention", "out_projection_sum", "mlp_column",
+                    "mlp_row_sum")
+    STAGES = STAGES_UNFUSED
+
     def __init__(self, batch: int, seq: int, hidden: int, n_heads: int, ffn: int,
-                 n_shards: int, rank: int, causal: bool = True, device="cuda"):
+                 n_shards: int, rank: int, causal: bool = True, device="cuda",
+                 fused: bool = False):
         self.batch, self.seq, self.hidden = batch, seq, hidden
         self.n_heads, self.ffn, self.n_shards, self.rank = n_heads, ffn, n_shards, rank
-        self.causal = causal
+        self.causal, self.fused = causal, fused
+        self.STAGES = self.STAGES_FUSED if fused else self.STAGES_UNFUSED
         T = batch * seq
         self.attn_ws = attn_workspace(batch, seq, hidden, n_heads, n_shards, device)
         self.mlp_ws = mlp_workspace(T, hidden, ffn, n_shards, torch.bfloat16, device)
-        self.Z_attn = torch.empty(T, hidden, dtype=torch.float32, device=device)
+        self.O = attn_views(self.attn_ws, batch, seq, hidden, n_heads, n_shards)["o"]
+        self.Z_attn = None if fused else torch.empty(T, hidden, dtype=torch.float32, device=device)
         self.H = torch.empty(T, hidden, dtype=torch.bfloat16, device=device)
         self.Y = torch.empty(T, ffn // n_shards, dtype=torch.bfloat16, device=device)
-        self.Z_mlp = torch.empty(T, hidden, dtype=torch.float32, device=device)
+        self.Z_mlp = None if fused else torch.empty(T, hidden, dtype=torch.float32, device=device)
         self.out = torch.empty(T, hidden, dtype=torch.float32, device=device)
-
-    STAGES = ("attention_shard", "sum_attention", "mlp_column", "mlp_row", "sum_mlp")
 
     def forward(self, X, Wqkv_i, bqkv_i, Wo_i, A_i, a_i, B_i,
                 attn_partials_other: List[torch.Tensor], mlp_partials_other: List[torch.Tensor],
@@ -496,10 +535,29 @@ class LayerShard:
         """attn partial -> H = bf16(sum of N attention partials) -> MLP partial on H -> sum.
 
         ``on_stage(name)`` (optional) is called after each stage's launches are enqueued,
-        with the names in ``STAGES`` (used to bracket stages with stream events).
+        with the names in ``self.STAGES`` (used to bracket stages with stream events).
         """
         mark = on_stage or (lambda name: None)
         r, N = self.rank, self.n_shards
+        if self.fused:
+            H_ = self.n_heads
+            qkv_projection(X, Wqkv_i, bqkv_i, self.batch, self.seq, H_, H_, N, r, self.attn_ws,
+                           stream=stream)
+            mark("qkv_projection")
+            head_attention(self.batch, self.seq, self.hidden, H_, H_, N, r, self.causal,
+                           self.attn_ws, stream=stream)
+            mark("attention")
+            peers = list(attn_partials_other)
+            peers.insert(r, None)
+            row_parallel_sum(self.O, Wo_i, peers, N, r, out=self.H, stream=stream)
+            mark("out_projection_sum")
+            column_parallel(self.H, A_i, a_i, N, r, gelu=True, Y=self.Y, stream=stream)
+            mark("mlp_column")
+            peers = list(mlp_partials_other)
+            peers.insert(r, None)
+            row_parallel_sum(self.Y, B_i, peers, N, r, out=self.out, stream=stream)
+            mark("mlp_row_sum")
+            return self.out
         attn_shard(X, Wqkv_i, bqkv_i, Wo_i, self.batch, self.seq, self.n_heads, N, r,
                    self.causal, Z=self.Z_attn, workspace=self.attn_ws, stream=stream)
         mark("attention_shard")

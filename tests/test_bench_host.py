@@ -84,3 +84,22 @@ def test_clock_sampler_reports_what_it_can_read(tmp_path):
     f2.write_text("2100000000\n")
     s.source = ("hwmon", str(f2))
     assert s._read() == 2100.0
+
+
+def test_layer_stage_costs_and_bounds():
+    """Algorithmic FLOPs and bytes of the layer step's one-kernel stages, and the roofline each
+    is rated against: the MFMA GEMMs against the bf16 peak, the sums (and the products with
+    the sum fused in, whose 7 x 134 MB of peer partials take longer at 8 TB/s than their
+    FLOPs at 2.5 PFLOP/s) against HBM."""
+    w = WORKLOADS[LAYER]
+    f, b = bench.layer_stage_cost(w, "mlp_column")
+    assert f == 274_877_906_944 and b == 2 * (4096 * 8192 + 4096 * 8192 + 4096 + 4096 * 4096)
+    f, b = bench.layer_stage_cost(w, "mlp_row_sum")
+    assert b == 2 * (4096 * 4096 + 8192 * 4096) + 7 * 4 * 4096 * 8192 + 4 * 4096 * 8192
+    assert bench.layer_stage_cost(w, "attention_shard") is None
+    assert bench.layer_stage_cost(w, "sum_mlp") == (0.0, (8 * 4 + 4) * 4096 * 8192)
+    for s, want in (("mlp_column", "mfma"), ("mlp_row", "mfma"), ("qkv_projection", "mfma"),
+                    ("mlp_row_sum", "hbm"), ("out_projection_sum", "hbm"), ("sum_mlp", "hbm")):
+        f, b = bench.layer_stage_cost(w, s)
+        got = "hbm" if b / (bench.PEAK_HBM_GBS * 1e9) > f / (bench.PEAK_BF16_TFLOPS * 1e12) else "mfma"
+        assert got == want, s

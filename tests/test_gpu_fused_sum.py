@@ -1,0 +1,80 @@
+"""GPU parity of the row-parallel layer with the partial sum fused into its epilogue
+(tp_row_parallel_sum_fwd): Z = sum_q Z_q with Z_rank = X_i W_i computed in the same kernel.
+
+It must give exactly the bits of tp_row_parallel_fwd into Z_rank followed by tp_sum_partials
+(the same fp32 adds in the same order q = 0 .. N-1), for fp32 and bf16 outputs, every tile
+layout, ragged shapes and any rank; and match the fp64 oracle (sum of the partials plus the
+product) within the bf16 tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import canary_tensor, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def _inputs(torch, T, k, width, N, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    X = torch.randn(T, k, device="cuda", generator=g).to(torch.bfloat16)
+    W = (0.05 * torch.randn(width, k, device="cuda", generator=g)).to(torch.bfloat16)
+    parts = [torch.randn(T, width, device="cuda", generator=g) for _ in range(N)]
+    return X, W, parts
+
+
+def _check(T, k, width, N, rank, out_dtype, seed=0):
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    X, W, parts = _inputs(torch, T, k, width, N, seed)
+    own = shard.row_parallel(X, W, N, rank)
+    ref_parts = list(parts)
+    ref_parts[rank] = own
+    Z_ref = shard.sum_partials(ref_parts, out_dtype=out_dtype)
+    peers = list(parts)
+    peers[rank] = None
+    Zc = canary_tensor((T, width), out_dtype)
+    Z = shard.row_parallel_sum(X, W, peers, N, rank, out=Zc.tensor)
+    torch.cuda.synchronize()
+    assert Zc.intact(), "write outside the output"
+    assert torch.equal(Z, Z_ref), "fused sum differs from row GEMM + tp_sum_partials"
+    # fp64: the peers' partials plus the product
+    Pn = np.stack([host(p) for q, p in enumerate(parts) if q != rank] or [np.zeros((T, width))])
+    ref = Pn.sum(axis=0) + oracle.linear(host(X), host(W).T)
+    return oracle.rel_frobenius(host(Z), ref)
+
+
+@pytest.mark.parametrize("case", [
+    # T, k, width, N, rank
+    (200, 520, 264, 2, 0), (200, 520, 264, 2, 1), (77, 64, 8, 3, 2), (513, 1024, 1000, 8, 5),
+    (1, 256, 64, 1, 0), (300, 2048, 512, 8, 7), (256, 4096, 2048, 4, 0),
+])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fused_sum_bitwise_equal_ragged(case, out):
+    torch = torch_cuda()
+    e = _check(*case, torch.float32 if out == "f32" else torch.bfloat16)
+    print("%s %s: err %.2e" % (case, out, e))
+    assert e < TOL
+
+
+@pytest.mark.parametrize("tile", ["256x256", "256x192", "256x128", "128x128", "256x256w4",
+                                  "256x192w4", "256x128w4", "128x128w4"])
+def test_fused_sum_every_tile_layout(tile, overrides):
+    torch = torch_cuda()
+    overrides("gemm_tile=" + tile)
+    for out in (torch.float32, torch.bfloat16):
+        e = _check(333, 2056, 776, 5, 3, out, seed=len(tile))
+        assert e < TOL, (tile, out)
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_fused_sum_layer_shapes(rank):
+    """The layer's two fused sums at full size: the output projection (4096 x 8192 x 1024,
+    bf16 H) and the MLP row GEMM (4096 x 8192 x 4096, fp32 Z), N = 8."""
+    torch = torch_cuda()
+    e1 = _check(4096, 1024, 8192, 8, rank, torch.bfloat16, seed=rank)
+    e2 = _check(4096, 4096, 8192, 8, rank, torch.float32, seed=rank + 1)
+    print("rank %d: W_O + sum err %.2e, MLP row + sum err %.2e" % (rank, e1, e2))
+    assert e1 < TOL and e2 < TOL

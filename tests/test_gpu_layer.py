@@ -43,8 +43,12 @@ def test_layer_all_ranks_end_to_end_small():
     drv = shard.LayerShard(batch, seq, h, H, F, N, 1)
     Zd = drv.forward(X, W[1]["Wqkv"], W[1]["bqkv"], W[1]["Wo"], W[1]["A"], W[1]["a"], W[1]["B"],
                      [za[0]], [zm[0]])
+    fz = shard.LayerShard(batch, seq, h, H, F, N, 1, fused=True)
+    Zf = fz.forward(X, W[1]["Wqkv"], W[1]["bqkv"], W[1]["Wo"], W[1]["A"], W[1]["a"], W[1]["B"],
+                    [za[0]], [zm[0]])
     torch.cuda.synchronize()
     assert torch.equal(Zd, Z)
+    assert torch.equal(Zf, Z) and torch.equal(fz.H, Hs)
     Ho = oracle.attn_shard(d["X"], d["Wq"], d["Wk"], d["Wv"], d["bq"], d["bk"], d["bv"], d["Wo"],
                            batch, seq, H, 1, 0, True)
     Zo = oracle.mlp_shard(Ho, d["A"], d["a"], d["B"], 1, 0)
@@ -95,6 +99,13 @@ def test_layer_full_size_composed_step():
     torch.cuda.synchronize()
     assert torch.equal(Zd, Z), "the rank-0 driver must reproduce the composed step bitwise"
     assert torch.equal(drv.H, Hs)
+    # the fused step (each block's partial sum in its row-parallel product's epilogue)
+    fz = shard.LayerShard(w.batch, w.seq, w.hidden, w.heads, w.ffn, N, 0, fused=True)
+    Zf = fz.forward(X, W0["Wqkv"], W0["bqkv"], W0["Wo"], mlp_w[0], mlp_w[1], mlp_w[2],
+                    za[1:], zm[1:])
+    torch.cuda.synchronize()
+    assert torch.equal(fz.H, Hs) and torch.equal(Zf, Z), "the fused step must give the same bits"
+    del fz, Zf
 
     rows = sample_rows(T, 40, seed=4, must=[0, 1, 127, 128, 255, 2047, 2048, 4095])
     Hg = host(Hs)[rows]

@@ -80,14 +80,42 @@ def test_mlp_bf16_ragged_tiles(shape, tile, overrides):
     assert ey < TOL["bf16"] and ez < TOL["bf16"]
 
 
-def test_mlp_f32_ragged():
-    w = Workload(name="ragged32", kind="mlp", dtype="f32", tokens=77, hidden=136, ffn=400,
+@pytest.mark.parametrize("T", [77, 1, 13, 16, 17, 32, 47, 64, 65])
+def test_mlp_f32_ragged(T):
+    """fp32 shards with ragged K (136, 200) and widths that are not multiples of 16: up to 64
+    token rows take the few-rows kernel (1, 2 or 4 row blocks), beyond it the 32 x 64 tiles."""
+    w = Workload(name="ragged32", kind="mlp", dtype="f32", tokens=T, hidden=136, ffn=400,
                  n_shards=2)
-    d = mlp_inputs(w, seed=11)
+    d = mlp_inputs(w, seed=11 + T)
     for r in range(2):
         Y, Z = run_shard(d, 2, r, "f32")
-        assert oracle.rel_frobenius(Y, oracle.mlp_column(d["X"], d["A"], d["a"], 2, r)) < 1e-5
-        assert oracle.rel_frobenius(Z, oracle.mlp_shard(d["X"], d["A"], d["a"], d["B"], 2, r)) < 1e-5
+        ey = oracle.rel_frobenius(Y, oracle.mlp_column(d["X"], d["A"], d["a"], 2, r))
+        ez = oracle.rel_frobenius(Z, oracle.mlp_shard(d["X"], d["A"], d["a"], d["B"], 2, r))
+        print("fp32 T=%d rank %d: Y err %.2e, Z err %.2e" % (T, r, ey, ez))
+        assert ey < 1e-5 and ez < 1e-5
+
+
+@pytest.mark.parametrize("T", [8, 32, 64])
+def test_f32_linear_primitives_few_rows(T):
+    """The column primitive without activation (bias epilogue) and the row primitive at few
+    rows, against the oracle's linear layer (K = 1032, widths 264 and 1032)."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    w = Workload(name="prim32", kind="mlp", dtype="f32", tokens=T, hidden=1032, ffn=528,
+                 n_shards=2)
+    d = mlp_inputs(w, seed=T)
+    X = dev(d["X"], "f32")
+    A1 = dev(layout.column_shard(d["A"], 2, 1), "f32")
+    a1 = dev(layout.bias_shard(d["a"], 2, 1), "f32")
+    B1 = dev(layout.row_shard(d["B"], 2, 1), "f32")
+    P = shard.column_parallel(X, A1, a1, 2, 1, gelu=False)
+    Z = shard.row_parallel(P, B1, 2, 1)
+    cols = slice(264, 528)
+    Po = oracle.linear(d["X"], d["A"][:, cols], d["a"][cols])
+    Zo = oracle.linear(host(P), d["B"][cols, :])
+    ep, ez = oracle.rel_frobenius(host(P), Po), oracle.rel_frobenius(host(Z), Zo)
+    print("fp32 primitives T=%d: P err %.2e, Z err %.2e" % (T, ep, ez))
+    assert ep < 1e-5 and ez < 1e-5
 
 
 def test_mlp_bf16_shards_sum_to_unsharded_block():
