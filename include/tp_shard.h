@@ -427,6 +427,8 @@ tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* t
  *           attn_split=1|2            key-range split of the attention off (1) or forced (2)
  *           sum_grid=<n>              partial-sum workgroups (0: one lane per vector)
  *           sum_unroll=1|2|4          partial-sum vectors per lane
+ *           sum_defer=0|1             fused partial sum: 0 keeps every tile's sum in its own
+ *                                     epilogue (1, the default, lets the launcher defer it)
  * The setting is process-wide and applies to launches (and workspace sizes) from then on;
  * set it while no other thread is calling the library. TP_ERR_SHAPE (nothing changed) on an
  * unknown key or a bad value. The library reads no environment variable.

@@ -390,21 +390,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     static_assert(!GLU || FN % 2 == 0, "SwiGlu pairs the wave's 32-column blocks");
     const int tiles_m = (p.M + BM - 1) / BM;
     const int tiles_n = ((GLU ? 2 * p.N : p.N) + BN - 1) / BN;
+    // The fused partial sum in deferred form (p.defer): the workgroup takes two tiles, blocks
+    // b and b + gridDim.x. The first tile's own product goes to C as an fp32 partial, and its
+    // sum (the partials of every rank, in the fixed order) is streamed by the waves that load
+    // no slabs while the second tile's K loop runs: the first tile is complete on every rank
+    // by then. The second tile ends in the ordinary fused epilogue. PHASE: 0 the workgroup's
+    // only tile, 1 the first of two, 2 the second of two.
+    constexpr bool DEFER = EPI == Epi::SumF32 && NW == 8;
+    int dm0 = 0, dn0 = 0;        // origin of the tile whose sum is being streamed
+    auto tile = [&](auto phase_c, const int bid) {
+    constexpr int PHASE = decltype(phase_c)::value;
     int tm, tn;
     if (EPI == Epi::F32 && p.k_splits > 1) {
         // group of blocks -> part of K: A, B and C move to the part, K to its length (a part
         // past the end has length <= 0 and writes zeros)
         const int tiles = tiles_m * tiles_n;
-        const int split = (int)blockIdx.x / tiles;
+        const int split = bid / tiles;
         const int kc = ((p.K + p.k_splits - 1) / p.k_splits + BK - 1) / BK * BK;
         const int kb = split * kc;
         p.A = reinterpret_cast<const bf16*>(p.A) + kb;
         p.B = reinterpret_cast<const bf16*>(p.B) + kb;
         p.C = reinterpret_cast<float*>(p.C) + split * p.split_stride;
         p.K = max(min(p.K - kb, kc), 0);
-        tile_coords(tiles_m, tiles_n, tm, tn, (int)blockIdx.x - split * tiles);
+        tile_coords(tiles_m, tiles_n, tm, tn, bid - split * tiles);
     } else {
-        tile_coords(tiles_m, tiles_n, tm, tn);
+        tile_coords(tiles_m, tiles_n, tm, tn, bid);
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const int f0 = GLU ? n0 / 2 : n0;       // first B row (output feature) of the tile
@@ -570,10 +580,55 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rB2 : rB, (lds_ptr)sink, 4, off, 0, 0, 0);
         }
     };
+    // Streaming of the deferred tile's sum by the waves that load no slabs (NW / 2 x 64 lanes):
+    // at slab kt each lane sums the vector whose loads it issued at slab kt - 1 (the partials of
+    // every rank, the own one read back from C, added in the order 0 .. n_parts-1) and stores
+    // it, then issues the loads of vector kt x lanes + its index. A tile of BM x BN / 4 vectors
+    // needs BM x BN / 4 / lanes slabs (the launcher defers only when the K loop is that long,
+    // and when C's byte offsets fit 31 bits). The code is branch-free: every slot is loaded
+    // (slots past n_parts and lanes past the tile re-read C at a valid offset), and a slot
+    // past n_parts is dropped by a select rather than added.
+    constexpr int SLANES = NW / 2 * 64;
+    constexpr int TVEC = BM * BN / 4;
+    f32x4 sv[kMaxSumParts];
+    uint32_t s_off = 0;
+    bool s_ok = false;
+    auto stream_base = [&](int q) {
+        return reinterpret_cast<const char*>(
+            q < p.n_parts && q != p.part_rank ? p.part[q] : reinterpret_cast<const float*>(p.C));
+    };
+    auto stream_finish = [&]() {
+        f32x4 a = sv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxSumParts; ++q) {
+            const f32x4 t = a + sv[q];
+            a = q < p.n_parts ? t : a;
+        }
+        if (s_ok)
+            __builtin_nontemporal_store(
+                a, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(p.C) + s_off));
+    };
+    auto stream_step = [&](int kt) {
+        if (kt > 0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the previous slab's loads
+            stream_finish();
+        }
+        const int v = kt * SLANES + (wave_u - NW / 2) * 64 + lane;
+        const int row = v / (BN / 4), c4 = v - row * (BN / 4);
+        const int m = dm0 + row, n = dn0 + 4 * c4;
+        s_ok = v < TVEC && m < p.M && n < p.N;
+        s_off = s_ok ? (uint32_t)(m * (int)p.ldc + n) * 4u : 0u;
+#pragma unroll
+        for (int q = 0; q < kMaxSumParts; ++q)
+            sv[q] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(stream_base(q) + s_off));
+    };
     auto k_loop = [&](auto loader) {
         constexpr bool LD = !SPLIT_LOADS || decltype(loader)::value;   // this wave loads
         constexpr int NVW = !SPLIT_LOADS ? NV : (decltype(loader)::value ? 2 * NV : 0);
-        constexpr int NPF = LD ? NPFT : 0;
+        // pre-barrier wait: loading waves let their prefetches stay in flight; streaming waves
+        // their streamed loads and store (the barrier only guards the slabs in LDS)
+        constexpr int NPF = LD ? NPFT : (PHASE == 2 ? kMaxSumParts + 1 : 0);
         fetch(0, 0, loader);
 #pragma unroll
         for (int d = 1; d < kPrefetchAhead; ++d)
@@ -587,8 +642,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             if constexpr (LD) prefetch((kt + kPrefetchAhead) * BK);
             read_frags(cur, 1, fa[1], fb[1]);
             mma(fa[0], fb[0]);
-            InterleaveGroups<0, NM, NR, NVW + NPF>::emit();
+            InterleaveGroups<0, NM, NR, NVW + (LD ? NPF : 0)>::emit();
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PHASE == 2 && !LD) {
+                stream_step(kt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             read_frags(cur, 2, fa[0], fb[0]);
             mma(fa[1], fb[1]);
             InterleaveGroups<0, NM, NR, 0>::emit();
@@ -715,22 +774,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if constexpr (NW == 4)
+    if constexpr (NW == 4) {
         k_loop_deep();
-    else if (!SPLIT_LOADS || wave_u < NW / 2)
+    } else if (!SPLIT_LOADS || wave_u < NW / 2) {
         k_loop(std::true_type{});
-    else
+    } else {
         k_loop(std::false_type{});
+        if constexpr (PHASE == 2) {   // the vector loaded at the last slab
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            stream_finish();
+        }
+    }
 
     if constexpr (GLU) {
         f32x16 gacc[FN / 2][FM];
         swiglu_combine<FN, FM>(acc, gacc);
         store_tile<Epi::Bias, WTM, WTN / 2, NW, (int)sizeof(smem)>(
             p, gacc, reinterpret_cast<char*>(smem), m0 + wm * WTM, f0 + wn * (WTN / 2), wave, lane);
+    } else if constexpr (PHASE == 1) {
+        // the own product of the first tile goes to C; its sum is streamed during the next
+        // tile's K loop, once every wave's stores have completed
+        store_tile<Epi::F32, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
+                                                            m0 + wm * WTM, n0 + wn * WTN, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        dm0 = m0;
+        dn0 = n0;
     } else {
         store_tile<EPI, WTM, WTN, NW, (int)sizeof(smem)>(p, acc, reinterpret_cast<char*>(smem),
                                                        m0 + wm * WTM, n0 + wn * WTN, wave, lane);
     }
+    };
+    if constexpr (DEFER) {
+        if (p.defer) {
+            tile(std::integral_constant<int, 1>{}, (int)blockIdx.x);
+            __syncthreads();   // every wave's stores of the first tile have completed
+            tile(std::integral_constant<int, 2>{}, (int)blockIdx.x + (int)gridDim.x);
+            return;
+        }
+    }
+    tile(std::integral_constant<int, 0>{}, (int)blockIdx.x);
 }
 
 // ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
@@ -920,9 +1002,18 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
     const int ncols = epi == Epi::SwiGlu ? 2 * p.N : p.N;   // gate and up columns
     const int tiles = ((p.M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
     const int splits = epi == Epi::F32 && p.k_splits > 1 ? p.k_splits : 1;
-    dim3 grid(tiles * splits), block(64 * WM * WN);
+    // Deferred fused sum: two tiles per workgroup when half the tiles still give every CU a
+    // workgroup and each XCD keeps its own tiles (the grid a multiple of 8), and the second
+    // tile's K loop has a slab per 256-lane pass over the first tile's vectors.
+    GemmProblem q = p;
+    q.defer = 0;
+    if (epi == Epi::SumF32 && WM * WN == 8 && tiles % 16 == 0 && tiles / 2 >= 256 &&
+        (p.K + 63) / 64 >= BM * BN / 4 / 256 && (int64_t)p.M * p.ldc * 4 <= INT32_MAX &&
+        !tuning().sum_nodefer)
+        q.defer = 1;
+    dim3 grid(q.defer ? tiles / 2 : tiles * splits), block(64 * WM * WN);
 #define TPS_LAUNCH(E) \
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, q);
     switch (epi) {
         case Epi::BiasGelu: TPS_LAUNCH(Epi::BiasGelu) break;
         case Epi::F32: TPS_LAUNCH(Epi::F32) break;

@@ -16,6 +16,7 @@ struct Tuning {
     int attn_split;                  // key-range split: 1 off, 2 forced (0: chosen)
     int sum_grid;                    // partial-sum workgroups (0: one lane per vector)
     int sum_unroll;                  // partial-sum vectors per lane, 1, 2 or 4 (0: 4)
+    int sum_nodefer;                 // 1: the fused-sum GEMM never defers a tile's sum
 };
 // A copy of the current overrides (defined with the C ABI).
 Tuning tuning();
@@ -64,6 +65,9 @@ struct GemmProblem {
     // is this product (never read), the others are added in the fixed order 0 .. n_parts-1.
     const float* part[kMaxSumParts];
     int n_parts, part_rank;
+    // SumF32, set by the launcher: each workgroup takes two tiles and streams the first one's
+    // sum during the second one's K loop (C holds the first tile's own partial meanwhile).
+    int defer;
 };
 
 // Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).

@@ -78,3 +78,34 @@ def test_fused_sum_layer_shapes(rank):
     e2 = _check(4096, 4096, 8192, 8, rank, torch.float32, seed=rank + 1)
     print("rank %d: W_O + sum err %.2e, MLP row + sum err %.2e" % (rank, e1, e2))
     assert e1 < TOL and e2 < TOL
+
+
+@pytest.mark.parametrize("case", [
+    # T, k, width, N, rank, tile: shapes whose launch takes two tiles per workgroup and streams
+    # the first tile's sum during the second one's K loop (ragged rows and K included)
+    (4096, 4096, 8192, 8, 0, None), (4096, 4096, 8192, 8, 7, None),
+    (3996, 4160, 8184, 3, 1, None), (4096, 3072, 6144, 2, 1, "256x192"),
+    (4096, 2048, 4096, 8, 4, "256x128"), (2048, 1024, 4096, 5, 0, "128x128"),
+])
+def test_fused_sum_deferred_form_bitwise(case, overrides):
+    """The deferred form gives the bits of the in-epilogue form and of row GEMM + sum."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    T, k, width, N, rank, tile = case
+    if tile:
+        overrides("gemm_tile=" + tile)
+    X, W, parts = _inputs(torch, T, k, width, N, seed=T + N)
+    peers = list(parts)
+    peers[rank] = None
+    Zc = canary_tensor((T, width), torch.float32)
+    Z = shard.row_parallel_sum(X, W, peers, N, rank, out=Zc.tensor)
+    torch.cuda.synchronize()
+    assert Zc.intact(), "write outside the output"
+    overrides(("gemm_tile=%s," % tile if tile else "") + "sum_defer=0")
+    Z0 = shard.row_parallel_sum(X, W, peers, N, rank)
+    ref_parts = list(parts)
+    ref_parts[rank] = shard.row_parallel(X, W, N, rank)
+    Z_ref = shard.sum_partials(ref_parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z0), "deferred form differs from the in-epilogue form"
+    assert torch.equal(Z, Z_ref), "deferred form differs from row GEMM + tp_sum_partials"
