@@ -425,6 +425,9 @@ tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* t
  *           qkv_split=1..8            K-split count of the Q/K/V projection
  *           attn_sets=1|2             attention wave sets per workgroup
  *           attn_split=1|2            key-range split of the attention off (1) or forced (2)
+ *           attn_pair=1|2             paired causal layout (one workgroup per two 64-query
+ *                                     tiles of equal total causal work) off (1) or on (2, the
+ *                                     default wherever the split and one-set are not forced)
  *           sum_grid=<n>              partial-sum workgroups (0: one lane per vector)
  *           sum_unroll=1|2|4          partial-sum vectors per lane
  *           sum_defer=0|1             fused partial sum: 0 keeps every tile's sum in its own

@@ -20,9 +20,12 @@
 //    every SIMD runs two independent waves, and their partial results (running max,
 //    denominator, unnormalised output) are merged through LDS with the same rescaling.
 //  * One set (with the key-range split, below): 64 KB of LDS, two workgroups per compute unit.
-//  * Key-range split (long causal sequences with few query tiles): each query tile's keys are
-//    halved between two workgroups, which write fp32 partials; attn_merge_kernel combines
-//    them.
+//  * Paired causal layout (causal, fewer than 512 query tiles): a workgroup owns the 64-query
+//    tiles i and n64 - 1 - i of one (sequence, head), whose causal key ranges add up to the
+//    same length for every i, so every workgroup has the same work and no partials leave it.
+//  * Key-range split (available for long causal sequences, forced by a test override): each
+//    query tile's keys are halved between two workgroups, which write fp32 partials;
+//    attn_merge_kernel combines them.
 // Per tile, a wave computes
 //   S^T = K Q^T - m  (MFMA "M" = keys, "N" = queries, K = d; the running max m enters as the
 //                     accumulator input, and Q arrives pre-multiplied by log2(e)/sqrt(d))
@@ -59,9 +62,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, in
                                              0x00020000);
 }
 
-template <int D, bool CAUSAL, int NSETS>
+template <int D, bool CAUSAL, int NSETS, bool PAIRED>
 __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kernel(AttnProblem p)
 {
+    static_assert(!PAIRED || (CAUSAL && NSETS == 2), "pairs are causal, two sets");
     constexpr int KS = D / 32;            // MFMA K-steps of the S product
     constexpr int DB = D / 16;            // 16-row blocks of O^T
     constexpr int KROW = D * 2;           // bytes per K-tile row
@@ -118,7 +122,25 @@ __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kern
     const int half = rem_b / n_bh;
     const int bh = rem_b - half * n_bh;
     const int q0 = qt * BQ;
-    const int qw0 = q0 + wave * QPW;      // this wave's first query
+    int qw0 = q0 + wave * QPW;            // this wave's first query
+    // Paired causal layout: block (pair i, sequence-head) owns the 64-query tiles A = i and
+    // B = n64 - 1 - i, whose causal key ranges add up to the same length for every i. Each
+    // 64-query tile is taken by two waves of each set (32 queries each); set 0 puts A on its
+    // waves 0-1 and B on 2-3, set 1 the other way round, so that the two waves sharing a SIMD
+    // (same wave index in both sets) have one A and one B range between them. With an odd
+    // tile count the middle pair has A = B, and the waves meant for B idle.
+    bool idle = false;
+    int pair_kv = 0;                      // key tiles of the pair (B's causal range)
+    if constexpr (PAIRED) {
+        const int n64 = (p.seq + 2 * QPW - 1) / (2 * QPW);
+        const int pi = (int)blockIdx.x / n_bh;
+        const int ta = pi, tb = n64 - 1 - pi;
+        const bool on_a = (wave < 2) != (set == 1);
+        idle = !on_a && tb == ta;
+        qw0 = idle ? p.seq : (on_a ? ta : tb) * (2 * QPW) + (wave & 1) * QPW;
+        pair_kv = min(p.seq, (tb + 1) * 2 * QPW);
+        pair_kv = (pair_kv + BKV - 1) / BKV;
+    }
 
     const int64_t head_rows = (int64_t)bh * p.seq;
     const bf16* __restrict__ gQ = reinterpret_cast<const bf16*>(p.q) + head_rows * D;
@@ -147,7 +169,7 @@ __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kern
     }
 
     const int kv_end = CAUSAL ? min(p.seq, q0 + BQ) : p.seq;
-    const int n_kv = (kv_end + BKV - 1) / BKV;
+    const int n_kv = PAIRED ? pair_kv : (kv_end + BKV - 1) / BKV;
     // this workgroup's key tiles [t_lo, t_hi): all of them, or one half
     const int n_first = (n_kv + halves - 1) / halves;
     const int t_lo = half == 0 ? 0 : n_first;
@@ -309,7 +331,9 @@ __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kern
         }
     };
     // A tile is needed by a wave unless all the wave's queries precede it (causal).
-    auto needed = [&](int t) { return t < t_hi && (!CAUSAL || t * BKV <= qw0 + QPW - 1); };
+    auto needed = [&](int t) {
+        return !idle && t < t_hi && (!CAUSAL || t * BKV <= qw0 + QPW - 1);
+    };
 
     // Set s takes key tiles t0 = t_lo + s, t0 + 2, ... and runs them as a two-stage pipeline:
     // in iteration it it turns the scores of tile t = t0 + 2 it into probabilities and
@@ -358,32 +382,40 @@ __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kern
     };
     // Windows whose next tile (t + 2, for both sets) lies inside the sequence and wholly
     // before the workgroup's first query (causal) need no mask (tile t then does not either);
-    // the rest (the diagonal, a ragged end) do. Tiles must also lie in [t_lo, t_hi).
-    const int full_tiles = min(min(CAUSAL ? q0 / BKV : n_kv, p.seq / BKV), t_hi);
+    // the rest (the diagonal, a ragged end) do. Tiles must also lie in [t_lo, t_hi). In the
+    // paired layout the count is the wave's own (its queries' first), so waves change loops
+    // at different windows; every wave still runs n_it windows, one barrier each.
+    const int full_tiles = min(min(CAUSAL ? (PAIRED ? (idle ? 0 : qw0 + 1) : q0) / BKV : n_kv,
+                                   p.seq / BKV), t_hi);
     const int n_full_it = min(max(full_tiles - t_lo - NSETS, 0) / NSETS, n_it);
     int it = 0;
-    for (; it + 2 <= n_full_it; it += 2) {
-        window(it, std::false_type{}, sA, sB);
-        window(it + 1, std::false_type{}, sB, sA);
-    }
-    if (it < n_full_it) {
-        window(it, std::false_type{}, sA, sB);
+    {
+        for (; it + 2 <= n_full_it; it += 2) {
+            window(it, std::false_type{}, sA, sB);
+            window(it + 1, std::false_type{}, sB, sA);
+        }
+        if (it < n_full_it) {
+            window(it, std::false_type{}, sA, sB);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sA[kb][0] = sB[kb][0], sA[kb][1] = sB[kb][1];
-        ++it;
+            for (int kb = 0; kb < 4; ++kb) sA[kb][0] = sB[kb][0], sA[kb][1] = sB[kb][1];
+            ++it;
+        }
+        for (; it + 2 <= n_it; it += 2) {
+            window(it, std::true_type{}, sA, sB);
+            window(it + 1, std::true_type{}, sB, sA);
+        }
+        if (it < n_it) window(it, std::true_type{}, sA, sB);
     }
-    for (; it + 2 <= n_it; it += 2) {
-        window(it, std::true_type{}, sA, sB);
-        window(it + 1, std::true_type{}, sB, sA);
-    }
-    if (it < n_it) window(it, std::true_type{}, sA, sB);
 
     // ---- merge the two sets' partials: set 1 publishes (output, max, denominator) of each of
-    // its lanes; the set-0 wave with the same queries (same wave index, same lane) combines
-    // them, rescaling each side by exp2(m_side - m) with m the larger maximum.
+    // its lanes; the set-0 wave with the same queries (same lane) combines them, rescaling
+    // each side by exp2(m_side - m) with m the larger maximum.
     constexpr int NF = DB * 2 * 4 + 4;   // floats per lane: output, 2 maxima, 2 denominators
     static_assert(NSETS == 1 || 4 * NF * 64 * 4 <= (int)sizeof(lds), "merge area");
-    float* xch = reinterpret_cast<float*>(lds) + wave * NF * 64 + lane;   // [wave][field][lane]
+    // [slot][field][lane]: set 1's wave w publishes in the slot of the set-0 wave with the same
+    // queries (w itself, or w + 2 mod 4 in the paired layout)
+    const int slot = PAIRED && set == 1 ? (wave + 2) & 3 : wave;
+    float* xch = reinterpret_cast<float*>(lds) + slot * NF * 64 + lane;
     if constexpr (NSETS == 2) __syncthreads();   // every wave is done with the tiles in the LDS
     if (NSETS == 2 && set == 1) {
 #pragma unroll
@@ -515,6 +547,21 @@ __global__ void zero_vt_pad_kernel(bf16* vt, int64_t rows, int seq, int64_t ld_v
     vt[r * ld_vt + c] = bf16(0.f);
 }
 
+// Paired causal layout (a block owns 64-query tiles i and n64 - 1 - i): the default for
+// causal attention with fewer than 512 query tiles of 128 (at most 256 pair workgroups, one
+// round on the chip), in place of the key-range split. Measured (one box): 4 sequences of
+// 2048 with 4 local heads 33.1 against 37-38 us for the split and its merge; 4096 tokens with
+// 8 local heads 57-59 against 58-59 us; with 512 tiles (8 x 2048) the pairs' two rounds lose
+// (55.5 against 45.5 us for one-set workgroups, two per compute unit). The test override
+// "attn_pair=1" turns it off, "attn_pair=2" forces it; forcing one set per workgroup
+// ("attn_sets=1") or the split turns it off too.
+bool use_pairs(bool causal, int kv_split, int64_t n_tiles)
+{
+    const Tuning t = tuning();
+    if (!causal || kv_split != 1 || t.attn_pair == 1 || t.attn_sets == 1) return false;
+    return t.attn_pair == 2 || n_tiles < 2 * 256;
+}
+
 template <int D>
 hipError_t launch(const AttnProblem& p, hipStream_t s)
 {
@@ -537,16 +584,21 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
     // replaces the choice.
     int nsets = grid.x >= 2 * 256 ? 1 : 2;
     if (const int v = tuning().attn_sets) nsets = v;
-    if (nsets == 1) {
+    if (use_pairs(p.causal != 0, p.kv_split, n_tiles)) {
+        // one block per (pair of 64-query tiles, sequence-head): equal causal work per block
+        const int n64 = (p.seq + 2 * QPW - 1) / (2 * QPW);
+        const dim3 pgrid((unsigned)(((n64 + 1) / 2) * p.batch * p.heads_local));
+        hipLaunchKernelGGL((attn_fwd_kernel<D, true, 2, true>), pgrid, dim3(512), 0, s, p);
+    } else if (nsets == 1) {
         if (p.causal)
-            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 1>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 1, false>), grid, dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 1>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 1, false>), grid, dim3(256), 0, s, p);
     } else {
         if (p.causal)
-            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 2>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_kernel<D, true, 2, false>), grid, dim3(512), 0, s, p);
         else
-            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 2>), grid, dim3(512), 0, s, p);
+            hipLaunchKernelGGL((attn_fwd_kernel<D, false, 2, false>), grid, dim3(512), 0, s, p);
     }
     if (p.kv_split == 2)
         hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)(n_tiles * (BQ / kMergeRows))),
@@ -561,10 +613,12 @@ hipError_t launch(const AttnProblem& p, hipStream_t s)
 // alone for a large share of the kernel. Measured at 256 query tiles, attention plus merge:
 // with 32 query tiles per sequence (4096 tokens) 74 us split against 88 us unsplit; with 16
 // (2048 tokens) 42.9 against 44.0 us once split workgroups run two per compute unit. The
-// default is therefore: causal, under 512 query tiles, and at least 16 query tiles per
-// sequence. The partials are reserved whenever there are under 512 query tiles (the workspace
-// size depends on the shapes only, not on the mask). The test override "attn_split=1" turns
-// the split off, "attn_split=2" forces it wherever the partials are reserved.
+// paired layout balances the same shapes without partials and is the default there; the
+// split remains the choice when pairing is turned off (causal, under 512 query tiles, at
+// least 16 query tiles per sequence). The partials are reserved whenever there are under
+// 512 query tiles (the workspace size depends on the shapes only, not on the mask or the
+// overrides). The test override "attn_split=1" turns the split off, "attn_split=2" forces it
+// wherever the partials are reserved.
 size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim, bool causal,
                                int* kv_split)
 {
@@ -577,6 +631,8 @@ size_t attention_partial_bytes(int batch, int heads_local, int seq, int head_dim
             *kv_split = 1;
         else if (force == 2)
             *kv_split = split;
+        else if (use_pairs(causal, 1, n_tiles))
+            *kv_split = 1;   // the pairs balance the causal work without partials
         else
             *kv_split = causal && n_qt >= 16 ? split : 1;
     }

@@ -14,6 +14,7 @@ struct Tuning {
     int qkv_split;                   // K-split count of the Q/K/V projection (0: chosen)
     int attn_sets;                   // attention waves sets per workgroup, 1 or 2 (0: chosen)
     int attn_split;                  // key-range split: 1 off, 2 forced (0: chosen)
+    int attn_pair;                   // paired causal layout: 1 off, 2 on (0: chosen)
     int sum_grid;                    // partial-sum workgroups (0: one lane per vector)
     int sum_unroll;                  // partial-sum vectors per lane, 1, 2 or 4 (0: 4)
     int sum_nodefer;                 // 1: the fused-sum GEMM never defers a tile's sum

@@ -88,6 +88,7 @@ bool parse_tuning(const char* spec, tps::Tuning& t)
             if (std::strcmp(key, "qkv_split") == 0 && v >= 1 && v <= 8) t.qkv_split = (int)v;
             else if (std::strcmp(key, "attn_sets") == 0 && (v == 1 || v == 2)) t.attn_sets = (int)v;
             else if (std::strcmp(key, "attn_split") == 0 && (v == 1 || v == 2)) t.attn_split = (int)v;
+            else if (std::strcmp(key, "attn_pair") == 0 && (v == 1 || v == 2)) t.attn_pair = (int)v;
             else if (std::strcmp(key, "sum_grid") == 0 && v >= 0 && v <= INT32_MAX) t.sum_grid = (int)v;
             else if (std::strcmp(key, "sum_unroll") == 0 && (v == 1 || v == 2 || v == 4)) t.sum_unroll = (int)v;
             else if (std::strcmp(key, "sum_defer") == 0 && (v == 0 || v == 1)) t.sum_nodefer = 1 - (int)v;

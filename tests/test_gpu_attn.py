@@ -95,14 +95,48 @@ def test_attn_qkv_k_split(case, overrides):
     test_attn_small_every_step(case)
 
 
-@pytest.mark.parametrize("split,sets", [("2", "2"), ("1", "1")])
+@pytest.mark.parametrize("spec", ["attn_split=2,attn_sets=2", "attn_split=1,attn_sets=1",
+                                  "attn_pair=1"])
 @pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[3], SMALL[5]])
-def test_attn_other_set_counts(case, split, sets, overrides):
+def test_attn_other_set_counts(case, spec, overrides):
     """The combinations the default does not take: the key-range split with two sets of
-    waves per workgroup (merged through LDS, then across the halves), and one set without
-    the split (no merge at all)."""
-    overrides("attn_split=%s,attn_sets=%s" % (split, sets))
+    waves per workgroup (merged through LDS, then across the halves), one set without the
+    split (no merge at all), and causal query tiles of 128 without the pairing."""
+    overrides(spec)
     test_attn_small_every_step(case)
+
+
+PAIRED = [
+    # batch, seq, hidden, heads, N, causal, bias: causal shapes for the paired layout (a
+    # workgroup owns 64-query tiles i and n64 - 1 - i); odd tile counts leave the middle
+    # tile alone, ragged ends cut the last tile
+    (1, 960, 512, 4, 2, True, True),     # 15 tiles
+    (2, 1088, 512, 4, 2, True, True),    # 17 tiles
+    (1, 1023, 256, 2, 1, True, False),   # 16 tiles, ragged
+    (3, 191, 256, 4, 2, True, True),     # 3 tiles, ragged, d = 64
+]
+
+
+@pytest.mark.parametrize("case", PAIRED)
+def test_attn_paired_layout(case):
+    """The paired causal layout (the default for causal attention) on odd and ragged tile
+    counts, against the oracle."""
+    test_attn_small_every_step(case)
+
+
+@pytest.mark.parametrize("case", PAIRED[:2])
+def test_attn_paired_agrees_with_unpaired(case, overrides):
+    """Paired and unpaired layouts compute the same softmax: agreement to bf16 rounding."""
+    batch, seq, h, H, N, causal, _ = case
+    w = Workload(name="a", kind="attn", dtype="bf16", tokens=batch * seq, batch=batch, seq=seq,
+                 hidden=h, heads=H, n_shards=N)
+    d = attn_inputs(w, seed=5)
+    _, O_pair, *_ = run_attn(d, batch, seq, H, N, N - 1, causal)
+    overrides("attn_pair=1")
+    _, O_one, *_ = run_attn(d, batch, seq, H, N, N - 1, causal)
+    e = oracle.rel_frobenius(O_pair, O_one)
+    print("paired vs unpaired O: %.2e" % e)
+    assert e < 5e-3
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -132,13 +166,15 @@ def test_attn_causal_first_row_is_projected_value():
         np.testing.assert_allclose(O[b * seq], v[b * seq], rtol=1e-2, atol=1e-2)
 
 
-@pytest.mark.parametrize("rank,split", [(0, None), (5, None), (5, "1")])
-def test_attn_full_size_shard_sampled_rows(rank, split, overrides):
+@pytest.mark.parametrize("rank,spec", [(0, None), (5, None), (5, "attn_split=2"),
+                                       (5, "attn_pair=1")])
+def test_attn_full_size_shard_sampled_rows(rank, spec, overrides):
     """One rank's shard at b 4, s 2048, h 4096, 32 heads, N 8 (causal), 48 sampled rows: the
-    default takes the key-range split (256 query tiles of 16 per sequence); also with the
-    split turned off (one two-set workgroup per query tile)."""
-    if split:
-        overrides("attn_split=" + split)
+    default takes the paired layout (256 workgroups, each two 64-query tiles of one head);
+    also with the key-range split forced, and with neither (one two-set workgroup per
+    128-query tile)."""
+    if spec:
+        overrides(spec)
     w = WORKLOADS["attn_shard_bf16_b4_s2048_h4096_H32_n8"]
     d = attn_inputs(w)
     Z, O, *_ = run_attn(d, w.batch, w.seq, w.heads, w.n_shards, rank, True)
