@@ -561,12 +561,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     constexpr int PFA = (EPI == Epi::Qkv || EPI == Epi::BiasGelu) ? (BM + 255) / 256 : 0;
     constexpr int NPFT = PFI + PFA;
     constexpr int kPrefetchAhead = 2;       // slabs
+    // One workgroup per panel touches it: the workgroups of an XCD run its tiles in step, in
+    // bands of 4 tile-rows by (for the usual shapes) 8 tile-columns (tile_coords), so the B
+    // column panel of a band is shared by its 4 rows and the A row panel by 8 columns; the
+    // first row (column) of each touches the panel for all. The others issue the same
+    // instructions with out-of-range offsets (no memory access), which keeps every wave's
+    // count of loads in flight the same. Layer step 1096 -> 1072 us (one box, alternating):
+    // four and eight times fewer prefetch requests to the L2.
+    const bool pf_b = tm % 4 == 0 || (tiles_m * tiles_n) % 8 != 0;
+    const bool pf_a = tn % 8 == 0 || tiles_n % 8 != 0 || (tiles_m * tiles_n) % 8 != 0;
     auto prefetch = [&](int k0) {
         bf16* sink = smem + 2 * (BM + BN) * BK;
 #pragma unroll
         for (int t = 0; t < PFA; ++t) {
             const int r = (t * 4 + (wave_u & 3)) * 64 + lane;   // a row of the A slab
-            const uint32_t off = k0 < p.K && r < BM ? (uint32_t)(r * p.lda + k0) * 2u : kOutOfRange;
+            const uint32_t off =
+                pf_a && k0 < p.K && r < BM ? (uint32_t)(r * p.lda + k0) * 2u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)sink, 4, off, 0, 0, 0);
         }
 #pragma unroll
@@ -576,7 +586,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             // SwiGlu: B rows [0, BN/2) of the gate, then the same features of the up weight
             const bool up = GLU && r0 >= BN / 2;
             const int rr = up ? r - BN / 2 : r;
-            const uint32_t off = k0 < p.K && r < BN ? (uint32_t)(rr * p.ldb + k0) * 2u : kOutOfRange;
+            const uint32_t off =
+                pf_b && k0 < p.K && r < BN ? (uint32_t)(rr * p.ldb + k0) * 2u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rB2 : rB, (lds_ptr)sink, 4, off, 0, 0, 0);
         }
     };
