@@ -432,6 +432,9 @@ tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* t
  *           sum_unroll=1|2|4          partial-sum vectors per lane
  *           sum_defer=0|1             fused partial sum: 0 keeps every tile's sum in its own
  *                                     epilogue (1, the default, lets the launcher defer it)
+ *           sum_ring=1|2              fused partial sum in ring form (128x128 tiles, each
+ *                                     tile's sum streamed during the next tile's K loop) off
+ *                                     (1) or wherever its shape conditions hold (2)
  * The setting is process-wide and applies to launches (and workspace sizes) from then on;
  * set it while no other thread is calling the library. TP_ERR_SHAPE (nothing changed) on an
  * unknown key or a bad value. The library reads no environment variable.

@@ -135,6 +135,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// s_waitcnt immediate for vmcnt(vm) expcnt(7) lgkmcnt(lgkm); vmcnt's two high bits sit at
+// [15:14], so vm may reach 63 (63: no wait on vector memory).
+constexpr int waitcnt_imm(int vm, int lgkm)
+{
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in that order.
+template <int N, typename F>
+__device__ __forceinline__ void unroll_c(F&& f)
+{
+    if constexpr (N > 0) {
+        unroll_c<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
+// Ring form of the fused partial sum: slabs a streamed vector's loads have to land (the K
+// loop of a ring launch spans a multiple of this many slabs).
+constexpr int kRingDepth = 4;
+
 // Scheduling groups of one pipeline phase: after MFMA I come up to three fragment reads
 // (front-loaded, so that the last read of the phase still has most of the phase's MFMAs to
 // land before the next phase waits on it) and NV (I+1)/NM - NV I/NM slab loads (spread evenly
@@ -395,11 +416,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     // sum (the partials of every rank, in the fixed order) is streamed by the waves that load
     // no slabs while the second tile's K loop runs: the first tile is complete on every rank
     // by then. The second tile ends in the ordinary fused epilogue. PHASE: 0 the workgroup's
-    // only tile, 1 the first of two, 2 the second of two.
+    // only tile, 1 the first of two, 2 the second of two, 3 a ring tile before the last (ring
+    // form below), 4 the ring's last tile.
     constexpr bool DEFER = EPI == Epi::SumF32 && NW == 8;
     int dm0 = 0, dn0 = 0;        // origin of the tile whose sum is being streamed
-    auto tile = [&](auto phase_c, const int bid) {
+    // Ring form (p.defer == 2; 128 x 128 tiles, eight waves): the workgroup takes the tiles
+    // b, b + G, ..., b + (T - 1) G (G workgroups, T = p.ring_tiles). After each K loop but the
+    // last, the tile's own product is staged in LDS (own_lds: fp32 rows padded by 16 bytes),
+    // and during the next tile's K loop the waves that load no slabs stream its sum: at every
+    // slab a lane finishes the vector whose loads it issued RD slabs before (the adds in the
+    // fixed order, then one store) and issues the loads of its next vector, whose own part it
+    // takes from LDS at once. A vector in flight carries its own part and its output offset in
+    // registers, so the stream runs on across tile boundaries and own_lds is free again when
+    // a K loop ends. The last tile ends in the ordinary fused epilogue. Each vector thus has RD
+    // slabs to land, with RD x 7 loads of 16 bytes per streaming lane in flight (the peers'
+    // partials; slots past n_parts re-read a peer's vector and their sum drops it, so the code
+    // has no branch per slot). Vectors outside the tile (and the first tile's stream, which
+    // has nothing to add) read offset 0 and store nothing. The K loop is exactly the 16 slabs
+    // over which the 256 streaming lanes take the 4096 vectors of a tile, one per slab.
+    constexpr bool RING = (EPI == Epi::SumF32 || EPI == Epi::SumBf16) && NW == 8 && BM == 128 &&
+                          BN == 128;
+    constexpr int RD = kRingDepth;
+    constexpr int OWN_PITCH = BN + 4;         // floats per staged row
+    __shared__ __attribute__((aligned(16))) float own_lds[RING ? BM * OWN_PITCH : 4];
+    f32x4 rv[RING ? RD : 1][kMaxSumParts - 1];   // peers' partials of the vectors in flight
+    f32x4 ro[RING ? RD : 1];                  // their own parts
+    uint32_t roff[RING ? RD : 1];             // their element offsets in C
+    bool rok[RING ? RD : 1];                  // a vector of the tile (else nothing is stored)
+    int sm0 = p.M, sn0 = 0;                   // origin of the tile in own_lds (none: rows past M)
+    const float* rP[kMaxSumParts - 1];   // slot j: partial j + (j >= part_rank), if any
+    auto tile = [&](auto phase_c, const int bid, auto role_c) {
     constexpr int PHASE = decltype(phase_c)::value;
+    // 0: the wave's role (slab loads or not) is decided here; 1 / 2: the caller runs the
+    // loading (1) or the other (2) waves' code only (the ring form, whose stream state then
+    // stays out of the loading waves' registers)
+    constexpr int ROLE = decltype(role_c)::value;
     int tm, tn;
     if (EPI == Epi::F32 && p.k_splits > 1) {
         // group of blocks -> part of K: A, B and C move to the part, K to its length (a part
@@ -634,19 +685,77 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             sv[q] = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x4*>(stream_base(q) + s_off));
     };
+    // Ring: issue vector kt x lanes + this lane's index of the tile in own_lds into slot U.
+    auto ring_issue = [&](auto u_c, int kt) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
+        const int v = kt * SLANES + (wave_u - NW / 2) * 64 + lane;
+        const int row = v / (BN / 4), c4 = v - row * (BN / 4);
+        const int m = sm0 + row, n = sn0 + 4 * c4;
+        const bool ok = v < TVEC && m < p.M && n < p.N;
+        rok[U] = ok;
+        roff[U] = ok ? (uint32_t)(m * (int)p.ldc + n) : 0u;
+        ro[U] = *reinterpret_cast<const f32x4*>(own_lds + (v < TVEC ? row : 0) * OWN_PITCH + 4 * c4);
+        // global (not flat) loads: a flat load would also count against the LDS counter that
+        // the fragment reads wait on
+#pragma unroll
+        for (int j = 0; j < kMaxSumParts - 1; ++j)
+            rv[U][j] = __builtin_nontemporal_load(
+                (__attribute__((address_space(1))) const f32x4*)(rP[j] + roff[U]));
+    };
+    // Ring: the sum of slot U's vector, q = 0 .. n_parts-1 with the own part at part_rank (the
+    // adds of the in-epilogue form and of the partial-sum kernel), stored non-temporally.
+    auto ring_finish = [&](auto u_c) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
+        // position q holds slot q below the own rank, the own part at it, slot q - 1 above
+        // (selects on uniform conditions: branches here were if-converted into more selects)
+        f32x4 a = p.part_rank == 0 ? ro[U] : rv[U][0];
+#pragma unroll
+        for (int q = 1; q < kMaxSumParts; ++q) {
+            const f32x4 x = q < p.part_rank ? rv[U][q < kMaxSumParts - 1 ? q : 0]
+                                            : (q == p.part_rank ? ro[U] : rv[U][q - 1]);
+            const f32x4 t = a + x;
+            a = q < p.n_parts ? t : a;
+        }
+        if (rok[U]) {
+            if constexpr (EPI == Epi::SumF32)
+                __builtin_nontemporal_store(
+                    a, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + roff[U]));
+            else
+                __builtin_nontemporal_store(
+                    to_bf16x4(a), reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.C) + roff[U]));
+        }
+    };
+    // Ring, at slab kt: slot U's loads (issued RD slabs ago) have landed once at most the
+    // 7 (RD - 1) loads issued since are in flight (vector-memory operations complete in order;
+    // the stores in between only make the wait stricter).
+    auto ring_step = [&](auto u_c, int kt) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((kMaxSumParts - 1) * (RD - 1), 15));
+        ring_finish(u_c);
+        ring_issue(u_c, kt);
+    };
     auto k_loop = [&](auto loader) {
         constexpr bool LD = !SPLIT_LOADS || decltype(loader)::value;   // this wave loads
         constexpr int NVW = !SPLIT_LOADS ? NV : (decltype(loader)::value ? 2 * NV : 0);
+        constexpr bool RS = RING && PHASE >= 3 && !LD;                   // streams the ring
         // pre-barrier wait: loading waves let their prefetches stay in flight; streaming waves
-        // their streamed loads and store (the barrier only guards the slabs in LDS)
+        // their streamed loads and stores (the barrier only guards the slabs in LDS)
         constexpr int NPF = LD ? NPFT : (PHASE == 2 ? kMaxSumParts + 1 : 0);
+        constexpr int BARW = RS ? waitcnt_imm(63, 0) : waitcnt_imm(NPF, 0);
         fetch(0, 0, loader);
 #pragma unroll
         for (int d = 1; d < kPrefetchAhead; ++d)
             if constexpr (LD) prefetch(d * BK);
-        __syncthreads();
+        if constexpr (RING && PHASE >= 3) {
+            // slab 0 (and the LDS writes of own_lds before the loop) complete; the ring's
+            // loads stay in flight
+            __builtin_amdgcn_s_waitcnt(LD ? waitcnt_imm(NPFT * (kPrefetchAhead - 1), 0)
+                                          : waitcnt_imm(63, 0));
+            __builtin_amdgcn_s_barrier();
+        } else {
+            __syncthreads();
+        }
         read_frags(0, 0, fa[0], fb[0]);
-        for (int kt = 0; kt < KT; ++kt) {
+        auto slab = [&](int kt, auto u_c) __attribute__((always_inline)) {
             const int cur = kt & 1;
             __builtin_amdgcn_sched_barrier(0);
             fetch((kt + 1) * BK, cur ^ 1, loader);
@@ -657,6 +766,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (PHASE == 2 && !LD) {
                 stream_step(kt);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (RS) {
+                ring_step(u_c, kt);
                 __builtin_amdgcn_sched_barrier(0);
             }
             read_frags(cur, 2, fa[0], fb[0]);
@@ -669,13 +781,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
             __builtin_amdgcn_sched_barrier(0);
             // this wave's slab loads have landed (only its NPF newer prefetches may still be
             // in flight) and its fragment reads are done; then the workgroup barrier
-            __builtin_amdgcn_s_waitcnt(0x0070 | NPF);   // vmcnt(NPF) expcnt(7) lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(BARW);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             read_frags(cur ^ 1, 0, fa[0], fb[0]);   // after the last slab: reads zeros, unused
             mma(fa[1], fb[1]);
             InterleaveGroups<0, NM, NR, 0>::emit();
             __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (RS) {
+            // the ring's slot is a compile-time index: RD slabs per trip (KT is a multiple of RD)
+            for (int kt = 0; kt < KT; kt += RD)
+                unroll_c<RD>([&](auto u) __attribute__((always_inline)) {
+                    slab(kt + decltype(u)::value, u);
+                });
+        } else {
+            for (int kt = 0; kt < KT; ++kt) slab(kt, std::integral_constant<int, 0>{});
         }
     };
     // Four waves (one per SIMD, each a 128 x 128 block of the tile): a third fewer fragment
@@ -787,13 +908,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
     };
     if constexpr (NW == 4) {
         k_loop_deep();
-    } else if (!SPLIT_LOADS || wave_u < NW / 2) {
-        k_loop(std::true_type{});
+    } else if (ROLE == 1 || (ROLE == 0 && (!SPLIT_LOADS || wave_u < NW / 2))) {
+        if constexpr (ROLE != 2) k_loop(std::true_type{});
     } else {
         k_loop(std::false_type{});
         if constexpr (PHASE == 2) {   // the vector loaded at the last slab
             __builtin_amdgcn_s_waitcnt(0x0F70);
             stream_finish();
+        }
+        if constexpr (RING && PHASE == 4) {   // the ring's last RD vectors, oldest first
+            unroll_c<RD>([&](auto u) __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(
+                    waitcnt_imm((kMaxSumParts - 1) * (RD - 1 - decltype(u)::value), 15));
+                ring_finish(u);
+            });
         }
     }
 
@@ -802,6 +930,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
         swiglu_combine<FN, FM>(acc, gacc);
         store_tile<Epi::Bias, WTM, WTN / 2, NW, (int)sizeof(smem)>(
             p, gacc, reinterpret_cast<char*>(smem), m0 + wm * WTM, f0 + wn * (WTN / 2), wave, lane);
+    } else if constexpr (PHASE == 3) {
+        // Ring: the product goes to own_lds once every wave is done with its LDS reads (the
+        // slabs, and own_lds for the previous tile's stream). The loading waves also wait for
+        // their last (out-of-range) loads, so that no LDS-DMA write is pending past this point.
+        __builtin_amdgcn_s_waitcnt(ROLE == 1 ? waitcnt_imm(0, 0) : waitcnt_imm(63, 0));
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4*>(own_lds + (wm * WTM + j * 32 + fr) * OWN_PITCH +
+                                              wn * WTN + i * 32 + 8 * q + 4 * fg) =
+                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+        sm0 = m0;
+        sn0 = n0;
     } else if constexpr (PHASE == 1) {
         // the own product of the first tile goes to C; its sum is streamed during the next
         // tile's K loop, once every wave's stores have completed
@@ -815,15 +961,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
                                                        m0 + wm * WTM, n0 + wn * WTN, wave, lane);
     }
     };
-    if constexpr (DEFER) {
-        if (p.defer) {
-            tile(std::integral_constant<int, 1>{}, (int)blockIdx.x);
-            __syncthreads();   // every wave's stores of the first tile have completed
-            tile(std::integral_constant<int, 2>{}, (int)blockIdx.x + (int)gridDim.x);
+    if constexpr (RING) {
+        if (p.defer == 2) {
+#pragma unroll
+            for (int u = 0; u < RD; ++u) {
+                ro[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                roff[u] = 0;
+                rok[u] = false;
+#pragma unroll
+                for (int j = 0; j < kMaxSumParts - 1; ++j) rv[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // a slot past the partials re-reads the first peer's vector (its sum drops it)
+#pragma unroll
+            for (int j = 0; j < kMaxSumParts - 1; ++j) {
+                const int q = j + (j >= p.part_rank ? 1 : 0);
+                rP[j] = q < p.n_parts ? p.part[q] : p.part[p.part_rank == 0 ? 1 : 0];
+            }
+            const int G = (int)gridDim.x;
+            auto ring = [&](auto role) __attribute__((always_inline)) {
+                for (int j = 0; j + 1 < p.ring_tiles; ++j)
+                    tile(std::integral_constant<int, 3>{}, (int)blockIdx.x + j * G, role);
+                tile(std::integral_constant<int, 4>{}, (int)blockIdx.x + (p.ring_tiles - 1) * G,
+                     role);
+            };
+            if (__builtin_amdgcn_readfirstlane(wave) < NW / 2)
+                ring(std::integral_constant<int, 1>{});
+            else
+                ring(std::integral_constant<int, 2>{});
             return;
         }
     }
-    tile(std::integral_constant<int, 0>{}, (int)blockIdx.x);
+    if constexpr (DEFER) {
+        if (p.defer == 1) {
+            tile(std::integral_constant<int, 1>{}, (int)blockIdx.x, std::integral_constant<int, 0>{});
+            __syncthreads();   // every wave's stores of the first tile have completed
+            tile(std::integral_constant<int, 2>{}, (int)blockIdx.x + (int)gridDim.x,
+                 std::integral_constant<int, 0>{});
+            return;
+        }
+    }
+    tile(std::integral_constant<int, 0>{}, (int)blockIdx.x, std::integral_constant<int, 0>{});
 }
 
 // ---- fp32 GEMM (true fp32 products, v_mfma_f32_16x16x4_f32) -------------------------------
@@ -1007,6 +1184,25 @@ __global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
     }
 }
 
+// Ring form of the fused partial sum (128 x 128 tiles, eight waves; see the kernel), for a
+// short K loop, where streaming the peers' partials outweighs the product: the tiles divide
+// into rounds of 256 workgroups (each workgroup then takes tiles / 256 of them, all on its
+// XCD), the K loop is the 16 slabs over which the next tile streams the 4096 vectors of one
+// tile (K in (960, 1024]), the partials' byte offsets fit 31 bits, and there are partials to
+// add. The output projection (4096 x 8192 x 1024 with 8 partials, bf16 H): 246 -> 230 us.
+// With a longer K loop the 128 x 128 product costs more than the stream saves (the MLP row
+// GEMM with its sum, K = 4096, keeps 256 x 256 tiles and the two-tile deferred form). The
+// test override "sum_ring=1" turns it off.
+static bool ring_feasible(const GemmProblem& p, Epi epi)
+{
+    if ((epi != Epi::SumF32 && epi != Epi::SumBf16) || tuning().sum_ring == 1) return false;
+    const long tiles = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const int kt = (p.K + 63) / 64;
+    static_assert(16 % kRingDepth == 0, "ring slots per K loop");
+    return p.n_parts >= 2 && tiles % 256 == 0 && tiles / 256 >= 2 && kt == 16 &&
+           (int64_t)p.M * p.ldc * 4 <= INT32_MAX;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
@@ -1018,11 +1214,17 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
     // tile's K loop has a slab per 256-lane pass over the first tile's vectors.
     GemmProblem q = p;
     q.defer = 0;
-    if (epi == Epi::SumF32 && WM * WN == 8 && tiles % 16 == 0 && tiles / 2 >= 256 &&
-        (p.K + 63) / 64 >= BM * BN / 4 / 256 && (int64_t)p.M * p.ldc * 4 <= INT32_MAX &&
-        !tuning().sum_nodefer)
+    q.ring_tiles = 0;
+    if (BM == 128 && BN == 128 && WM * WN == 8 && ring_feasible(p, epi)) {
+        q.defer = 2;
+        q.ring_tiles = tiles / 256;
+    } else if (epi == Epi::SumF32 && WM * WN == 8 && tiles % 16 == 0 && tiles / 2 >= 256 &&
+               (p.K + 63) / 64 >= BM * BN / 4 / 256 && (int64_t)p.M * p.ldc * 4 <= INT32_MAX &&
+               !tuning().sum_nodefer) {
         q.defer = 1;
-    dim3 grid(q.defer ? tiles / 2 : tiles * splits), block(64 * WM * WN);
+    }
+    dim3 grid(q.defer == 2 ? 256 : q.defer == 1 ? tiles / 2 : tiles * splits),
+        block(64 * WM * WN);
 #define TPS_LAUNCH(E) \
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, q);
     switch (epi) {
@@ -1178,6 +1380,10 @@ hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
     } else {
         t = gemm_bf16_pick_tile(p.M, p.N, p.K);
         w4 = prefer_four_waves(p.M, p.N, p.K, t, epi);
+        if (ring_feasible(p, epi)) {
+            t = GemmTile{128, 128};
+            w4 = false;
+        }
         tile_override(t, w4);
     }
     return gemm_bf16_tile(p, epi, s, t, w4);

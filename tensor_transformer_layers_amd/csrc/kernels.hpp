@@ -18,6 +18,7 @@ struct Tuning {
     int sum_grid;                    // partial-sum workgroups (0: one lane per vector)
     int sum_unroll;                  // partial-sum vectors per lane, 1, 2 or 4 (0: 4)
     int sum_nodefer;                 // 1: the fused-sum GEMM never defers a tile's sum
+    int sum_ring;                    // fused-sum GEMM in ring form: 1 off, 2 wherever feasible
 };
 // A copy of the current overrides (defined with the C ABI).
 Tuning tuning();
@@ -66,9 +67,12 @@ struct GemmProblem {
     // is this product (never read), the others are added in the fixed order 0 .. n_parts-1.
     const float* part[kMaxSumParts];
     int n_parts, part_rank;
-    // SumF32, set by the launcher: each workgroup takes two tiles and streams the first one's
-    // sum during the second one's K loop (C holds the first tile's own partial meanwhile).
+    // Set by the launcher. 1 (SumF32): each workgroup takes two tiles and streams the first
+    // one's sum during the second one's K loop (C holds the first tile's own partial
+    // meanwhile). 2 (ring, 128 x 128 tiles): each workgroup takes ring_tiles tiles, keeps
+    // each one's product in LDS and streams its sum during the next tile's K loop.
     int defer;
+    int ring_tiles;
 };
 
 // Tile shape chosen for a problem (exposed for the benchmark's bookkeeping).

@@ -92,6 +92,7 @@ bool parse_tuning(const char* spec, tps::Tuning& t)
             else if (std::strcmp(key, "sum_grid") == 0 && v >= 0 && v <= INT32_MAX) t.sum_grid = (int)v;
             else if (std::strcmp(key, "sum_unroll") == 0 && (v == 1 || v == 2 || v == 4)) t.sum_unroll = (int)v;
             else if (std::strcmp(key, "sum_defer") == 0 && (v == 0 || v == 1)) t.sum_nodefer = 1 - (int)v;
+            else if (std::strcmp(key, "sum_ring") == 0 && (v == 1 || v == 2)) t.sum_ring = (int)v;
             else return false;
         }
         if (end && !end[1]) return false;   // a trailing comma

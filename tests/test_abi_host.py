@@ -265,11 +265,11 @@ def test_test_overrides_parsing():
     assert B.tp_set_test_overrides("") == 0
     for good in ("gemm_tile=256x192", "gemm_tile=128x128w4,qkv_split=3", "attn_sets=1",
                  "attn_split=2,sum_grid=7,sum_unroll=2", "sum_defer=0", "sum_defer=1",
-                 "attn_pair=1", "attn_pair=2"):
+                 "attn_pair=1", "attn_pair=2", "sum_ring=1", "sum_ring=2"):
         assert B.tp_set_test_overrides(good) == 0, good
     for bad in ("gemm_tile=100x100", "gemm_tile=256x256w8", "qkv_split=9", "attn_sets=3",
                 "sum_unroll=3", "nope=1", "qkv_split", "qkv_split=2,", "sum_grid=-1",
-                "sum_defer=2", "attn_pair=0", "attn_pair=3"):
+                "sum_defer=2", "attn_pair=0", "attn_pair=3", "sum_ring=0", "sum_ring=3"):
         assert B.tp_set_test_overrides(bad) == 2, bad
     B.tp_set_test_overrides(None)
     # a rejected spec leaves the previous setting in place

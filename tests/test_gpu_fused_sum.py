@@ -109,3 +109,37 @@ def test_fused_sum_deferred_form_bitwise(case, overrides):
     torch.cuda.synchronize()
     assert torch.equal(Z, Z0), "deferred form differs from the in-epilogue form"
     assert torch.equal(Z, Z_ref), "deferred form differs from row GEMM + tp_sum_partials"
+
+
+@pytest.mark.parametrize("case", [
+    # T, k, width, N, rank, out: shapes that take the ring form (128 x 128 tiles in rounds of
+    # 256 workgroups, a 16-slab K loop): the layer's output projection, ragged rows, columns
+    # and K, two, three and five partials, the last rank
+    (4096, 1024, 8192, 8, 0, "bf16"), (4096, 1024, 8192, 8, 5, "f32"),
+    (4096, 1024, 8192, 8, 7, "bf16"), (4000, 1000, 8184, 3, 1, "bf16"),
+    (4040, 1000, 8184, 3, 2, "f32"), (2048, 1024, 4096, 2, 1, "f32"),
+    (2048, 984, 4096, 5, 4, "bf16"),
+])
+def test_fused_sum_ring_form_bitwise(case, overrides):
+    """The ring form (each tile's own product kept in LDS, its sum streamed during the next
+    tile's K loop) gives the bits of row GEMM + tp_sum_partials and of the other forms."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    T, k, width, N, rank, out = case
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    X, W, parts = _inputs(torch, T, k, width, N, seed=T + k + N)
+    peers = list(parts)
+    peers[rank] = None
+    overrides("sum_ring=2")
+    Zc = canary_tensor((T, width), odt)
+    Z = shard.row_parallel_sum(X, W, peers, N, rank, out=Zc.tensor)
+    torch.cuda.synchronize()
+    assert Zc.intact(), "write outside the output"
+    overrides("sum_ring=1")
+    Z1 = shard.row_parallel_sum(X, W, peers, N, rank, out=torch.empty_like(Z))
+    ref_parts = list(parts)
+    ref_parts[rank] = shard.row_parallel(X, W, N, rank)
+    Z_ref = shard.sum_partials(ref_parts, out_dtype=odt)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z_ref), "ring form differs from row GEMM + tp_sum_partials"
+    assert torch.equal(Z, Z1), "ring form differs from the other fused form"
