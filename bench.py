@@ -101,13 +101,18 @@ def traffic_for(kernel: str, stage: str):
     return None
 
 
-def gemm_kernel_name(M: int, N: int, K: int, epi: int, four_waves_ok: bool = True) -> str:
+def gemm_kernel_name(M: int, N: int, K: int, epi: int, n_parts: int = 0) -> str:
     """The bf16 GEMM launched for an M x N x K product, named as the profiler names it:
-    gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>. The Q/K/V scatter (2) and the
-    fused sums (6, 7) always run eight waves (``four_waves_ok`` False for the latter)."""
+    gemm_bf16_kernel<tile_m, tile_n, waves_m, waves_n, epilogue>. The Q/K/V scatter (2) always
+    runs eight waves; the fused sums (6 fp32, 7 bf16 output, over ``n_parts`` partials) take
+    the launch the library reports for them."""
     from tensor_transformer_layers_amd import binding
-    _, tbm, tbn, nw = binding.tp_gemm_tile_info(M, N, K)
-    if epi == 2 or not four_waves_ok:
+    if epi in (6, 7):
+        _, tbm, tbn, nw, _form = binding.tp_row_parallel_sum_tile_info(
+            M, N, K, n_parts, binding.TP_F32 if epi == 6 else binding.TP_BF16)
+    else:
+        _, tbm, tbn, nw = binding.tp_gemm_tile_info(M, N, K)
+    if epi == 2:
         nw = 8
     wgrid = {(256, 256, 8): (2, 4), (256, 192, 8): (4, 2), (256, 128, 8): (4, 2),
              (128, 128, 8): (2, 4)}.get((tbm, tbn, nw), (2, 2))
@@ -250,10 +255,10 @@ def layer_stage_kernel(w, stage: str) -> str:
     wl = (w.heads // N) * (h // w.heads)
     Fl = w.ffn // N
     return {"qkv_projection": lambda: gemm_kernel_name(T, 3 * wl, h, 2),
-            "out_projection_sum": lambda: gemm_kernel_name(T, h, wl, 7, four_waves_ok=False),
+            "out_projection_sum": lambda: gemm_kernel_name(T, h, wl, 7, n_parts=N),
             "mlp_column": lambda: gemm_kernel_name(T, Fl, h, 0),
             "mlp_row": lambda: gemm_kernel_name(T, h, Fl, 1),
-            "mlp_row_sum": lambda: gemm_kernel_name(T, h, Fl, 6, four_waves_ok=False),
+            "mlp_row_sum": lambda: gemm_kernel_name(T, h, Fl, 6, n_parts=N),
             "sum_attention": lambda: "sum_kernel<%d, 4, true>" % N,
             "sum_mlp": lambda: "sum_kernel<%d, 4, false>" % N}[stage]()
 

@@ -415,6 +415,19 @@ tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* t
                             int* waves);
 
 /* ------------------------------------------------------------------------------------------
+ * Which launch tp_row_parallel_sum_fwd makes for a row-parallel product of rows x k_local by
+ * out_features x k_local summed over n_parts partials into out_dt: block tile, waves per
+ * workgroup, and form, 0 = each tile's sum in its own epilogue, 1 = deferred (two tiles per
+ * workgroup, the first one's sum streamed during the second one's K loop; fp32 output only),
+ * 2 = ring (each workgroup's tiles in turn, every tile's product kept in LDS and its sum
+ * streamed during the next tile's K loop). Honours the test overrides; launches nothing.
+ * Returns TP_ERR_NULL / TP_ERR_SHAPE / TP_ERR_DTYPE on bad arguments.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_row_parallel_sum_tile_info(int64_t rows, int64_t out_features, int64_t k_local,
+                                         int n_parts, tp_dtype out_dt, int* tile_m, int* tile_n,
+                                         int* waves, int* form);
+
+/* ------------------------------------------------------------------------------------------
  * Test and tuning hook, for callers that need every launch variant exercised (the library's
  * tests): forces launch choices that are otherwise made per shape. Not part of any passage of
  * the method; results stay within the documented precision whatever is forced.
@@ -448,7 +461,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 10
+#define TP_SHARD_ABI_VERSION 11
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,7 @@ EXPORTED = (
     "tp_gqa_attn_workspace_layout", "tp_gqa_attn_shard_fwd", "tp_attn_workspace_bytes",
     "tp_attn_workspace_layout", "tp_attn_shard_fwd", "tp_qkv_projection_fwd",
     "tp_head_attention_fwd", "tp_sum_partials", "tp_gemm_tile_info",
+    "tp_row_parallel_sum_tile_info",
     "tp_set_test_overrides", "tp_last_error", "tp_abi_version",
 )
 
@@ -132,6 +133,9 @@ def lib():
     L.tp_gemm_tile_info.restype = _int
     L.tp_gemm_tile_info.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int),
                                     ctypes.POINTER(_int)]
+    L.tp_row_parallel_sum_tile_info.restype = _int
+    L.tp_row_parallel_sum_tile_info.argtypes = [_i64, _i64, _i64, _int, _int] + \
+        [ctypes.POINTER(_int)] * 4
     L.tp_sum_partials.restype = _int
     L.tp_sum_partials.argtypes = [ctypes.POINTER(_vp), _int, _i64, _vp, _int, _vp]
     L.tp_set_test_overrides.restype = _int
@@ -316,6 +320,14 @@ def tp_gemm_tile_info(M, N, K):
     a, b, c = _int(0), _int(0), _int(0)
     st = lib().tp_gemm_tile_info(M, N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
     return st, a.value, b.value, c.value
+
+
+def tp_row_parallel_sum_tile_info(rows, out_features, k_local, n_parts, out_dt):
+    """(status, tile_m, tile_n, waves, form) of tp_row_parallel_sum_fwd's launch."""
+    v = [_int(0) for _ in range(4)]
+    st = lib().tp_row_parallel_sum_tile_info(rows, out_features, k_local, n_parts, out_dt,
+                                             *[ctypes.byref(x) for x in v])
+    return (st,) + tuple(x.value for x in v)
 
 
 def tp_set_test_overrides(spec: Optional[str]) -> int:

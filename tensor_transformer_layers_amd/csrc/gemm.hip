@@ -1203,26 +1203,31 @@ static bool ring_feasible(const GemmProblem& p, Epi epi)
            (int64_t)p.M * p.ldc * 4 <= INT32_MAX;
 }
 
+// Form of a fused-sum launch with this tile: 2 ring, 1 deferred (two tiles per workgroup,
+// when half the tiles still give every CU a workgroup and each XCD keeps its own tiles, the
+// grid a multiple of 8, and the second tile's K loop has a slab per 256-lane pass over the
+// first tile's vectors), 0 the sum in each tile's own epilogue.
+static int fused_form(const GemmProblem& p, Epi epi, int bm, int bn, int nw)
+{
+    if (epi != Epi::SumF32 && epi != Epi::SumBf16) return 0;
+    if (bm == 128 && bn == 128 && nw == 8 && ring_feasible(p, epi)) return 2;
+    const long tiles = (long)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    if (epi == Epi::SumF32 && nw == 8 && tiles % 16 == 0 && tiles / 2 >= 256 &&
+        (p.K + 63) / 64 >= bm * bn / 4 / 256 && (int64_t)p.M * p.ldc * 4 <= INT32_MAX &&
+        !tuning().sum_nodefer)
+        return 1;
+    return 0;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
 {
     const int ncols = epi == Epi::SwiGlu ? 2 * p.N : p.N;   // gate and up columns
     const int tiles = ((p.M + BM - 1) / BM) * ((ncols + BN - 1) / BN);
     const int splits = epi == Epi::F32 && p.k_splits > 1 ? p.k_splits : 1;
-    // Deferred fused sum: two tiles per workgroup when half the tiles still give every CU a
-    // workgroup and each XCD keeps its own tiles (the grid a multiple of 8), and the second
-    // tile's K loop has a slab per 256-lane pass over the first tile's vectors.
     GemmProblem q = p;
-    q.defer = 0;
-    q.ring_tiles = 0;
-    if (BM == 128 && BN == 128 && WM * WN == 8 && ring_feasible(p, epi)) {
-        q.defer = 2;
-        q.ring_tiles = tiles / 256;
-    } else if (epi == Epi::SumF32 && WM * WN == 8 && tiles % 16 == 0 && tiles / 2 >= 256 &&
-               (p.K + 63) / 64 >= BM * BN / 4 / 256 && (int64_t)p.M * p.ldc * 4 <= INT32_MAX &&
-               !tuning().sum_nodefer) {
-        q.defer = 1;
-    }
+    q.defer = fused_form(p, epi, BM, BN, WM * WN);
+    q.ring_tiles = q.defer == 2 ? tiles / 256 : 0;
     dim3 grid(q.defer == 2 ? 256 : q.defer == 1 ? tiles / 2 : tiles * splits),
         block(64 * WM * WN);
 #define TPS_LAUNCH(E) \
@@ -1364,9 +1369,10 @@ static GemmTile glu_pick_tile(int M, int N, int K, bool* w4)
     return best;
 }
 
-hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
+// The tile and layout gemm_bf16 launches for this problem and epilogue.
+static GemmTile choose_tile(const GemmProblem& p, Epi epi, bool& w4)
 {
-    bool w4 = false;
+    w4 = false;
     GemmTile t;
     if (epi == Epi::SwiGlu) {
         t = glu_pick_tile(p.M, p.N, p.K, &w4);
@@ -1386,7 +1392,33 @@ hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
         }
         tile_override(t, w4);
     }
+    return t;
+}
+
+hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
+{
+    bool w4 = false;
+    const GemmTile t = choose_tile(p, epi, w4);
     return gemm_bf16_tile(p, epi, s, t, w4);
+}
+
+GemmTile gemm_bf16_sum_launch_tile(int M, int N, int K, int n_parts, bool bf16_out, int* waves,
+                                   int* form)
+{
+    GemmProblem p{};
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = K;
+    p.ldb = K;
+    p.ldc = N;
+    p.n_parts = n_parts;
+    const Epi epi = bf16_out ? Epi::SumBf16 : Epi::SumF32;
+    bool w4 = false;
+    const GemmTile t = choose_tile(p, epi, w4);
+    *waves = w4 ? 4 : 8;
+    *form = fused_form(p, epi, t.bm, t.bn, *waves);
+    return t;
 }
 
 // A Q/K/V projection with few output columns (grouped-query attention: 4096 x 1280 x 8192

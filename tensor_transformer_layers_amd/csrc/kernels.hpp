@@ -81,6 +81,10 @@ struct GemmTile { int bm, bn; };
 GemmTile gemm_bf16_pick_tile(int M, int N, int K);
 // Tile and wave count gemm_bf16 launches for this shape (after the environment override).
 GemmTile gemm_bf16_launch_tile(int M, int N, int K, int* waves);
+// Tile, waves and form (0 in-epilogue, 1 deferred, 2 ring) of the fused-sum launch for an
+// M x N x K row-parallel product over n_parts partials.
+GemmTile gemm_bf16_sum_launch_tile(int M, int N, int K, int n_parts, bool bf16_out, int* waves,
+                                   int* form);
 hipError_t gemm_bf16(const GemmProblem& p, Epi epi, hipStream_t stream);
 // K-split count for the Q/K/V projection of an M x N x K shape (1: no split): > 1 when 256 x
 // 256 tiles would occupy at most half of the compute units.

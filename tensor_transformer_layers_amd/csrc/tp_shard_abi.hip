@@ -932,6 +932,26 @@ tp_status tp_gemm_tile_info(int64_t M, int64_t N, int64_t K, int* tile_m, int* t
     return ok();
 }
 
+tp_status tp_row_parallel_sum_tile_info(int64_t rows, int64_t out_features, int64_t k_local,
+                                         int n_parts, tp_dtype out_dt, int* tile_m, int* tile_n,
+                                         int* waves, int* form)
+{
+    if (!tile_m || !tile_n || !waves || !form)
+        return fail(TP_ERR_NULL, "output pointers must be non-NULL");
+    if (rows < 1 || out_features < 1 || k_local < 1 || rows > INT32_MAX ||
+        out_features > INT32_MAX || k_local > INT32_MAX)
+        return fail(TP_ERR_SHAPE, "rows, out_features, k_local must be in [1, 2^31-1]");
+    if (n_parts < 1 || n_parts > tps::kMaxSumParts)
+        return fail(TP_ERR_SHAPE, "n_parts=%d outside [1, %d]", n_parts, tps::kMaxSumParts);
+    if (out_dt != TP_F32 && out_dt != TP_BF16)
+        return fail(TP_ERR_DTYPE, "out_dt %d not supported", (int)out_dt);
+    const tps::GemmTile t = tps::gemm_bf16_sum_launch_tile(
+        (int)rows, (int)out_features, (int)k_local, n_parts, out_dt == TP_BF16, waves, form);
+    *tile_m = t.bm;
+    *tile_n = t.bn;
+    return ok();
+}
+
 tp_status tp_sum_partials(const float* const* Z_parts, int n_parts, int64_t numel, void* Z,
                           tp_dtype out_dt, void* stream)
 {

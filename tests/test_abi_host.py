@@ -344,3 +344,32 @@ def test_noalloc_mlp_validation():
     assert B.tp_mlp_shard_fwd_noalloc(**big) not in (1, 2, 3, 4, 5, 6, 7)
     assert B.tp_mlp_shard_fwd_noalloc(**dict(big, tokens=8193)) == 7
     assert "scratch" in B.tp_last_error()
+
+
+def test_row_parallel_sum_tile_info():
+    """The fused-sum launch the library reports: the ring form for the layer's output
+    projection (16-slab K loop, 2048 tiles of 128 x 128), the deferred form for its MLP row
+    GEMM (fp32 output, K = 4096), the in-epilogue form for a bf16 output with a long K loop,
+    and none of the ring where the override turns it off. No kernel runs."""
+    F32, BF16 = B.TP_F32, B.TP_BF16
+    B.tp_set_test_overrides(None)
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 8, BF16) == (0, 128, 128, 8, 2)
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 8, F32) == (0, 128, 128, 8, 2)
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 4096, 8, F32) == (0, 256, 256, 8, 1)
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 4096, 8, BF16) == (0, 256, 256, 8, 0)
+    # ragged rows, columns and K still divide into rounds of 256 workgroups
+    assert B.tp_row_parallel_sum_tile_info(4000, 8184, 1000, 3, BF16)[1:] == (128, 128, 8, 2)
+    # no partials to add, or tiles that do not fill whole rounds: no ring
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 1, BF16)[4] != 2
+    assert B.tp_row_parallel_sum_tile_info(4096, 8000, 1024, 8, BF16)[4] != 2
+    # a K loop other than 16 slabs: no ring
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 2048, 8, BF16)[4] != 2
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 960, 8, BF16)[4] != 2
+    assert B.tp_set_test_overrides("sum_ring=1") == 0
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 8, BF16) == (0, 256, 256, 8, 0)
+    assert B.tp_set_test_overrides("sum_defer=0") == 0
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 4096, 8, F32) == (0, 256, 256, 8, 0)
+    B.tp_set_test_overrides(None)
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 9, BF16)[0] == 2   # TP_ERR_SHAPE
+    assert B.tp_row_parallel_sum_tile_info(0, 8192, 1024, 8, BF16)[0] == 2
+    assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 8, 7)[0] != 0
