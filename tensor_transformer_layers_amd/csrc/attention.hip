@@ -55,6 +55,19 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// max(v, v of lane ^ X) for X = 16 or 32, in the VALU: a permlane swap of v with itself gives
+// each lane the pair (its own v, its partner's v) in some order. Keeps the softmax's row
+// maximum off the LDS crossbar that a shuffle uses, on every key tile's dependency chain.
+template <int X>
+__device__ __forceinline__ float max_xor(float v, std::integral_constant<int, X>)
+{
+    static_assert(X == 16 || X == 32, "partner distance");
+    const unsigned u = __float_as_uint(v);
+    const auto r = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int64_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
@@ -276,8 +289,8 @@ __global__ __launch_bounds__(256 * NSETS, NSETS == 1 ? 2 : 1) void attn_fwd_kern
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, s[kb][qb][i]);
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
+            m = max_xor(m, std::integral_constant<int, 16>{});
+            m = max_xor(m, std::integral_constant<int, 32>{});
             mx[qb] = m;
             grew = grew || (m_run[qb] == -INFINITY ? m != -INFINITY : m > kLazy);
         }
