@@ -438,7 +438,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmProblem p)
                           BN == 128;
     constexpr int RD = kRingDepth;
     constexpr int OWN_PITCH = BN + 4;         // floats per staged row
-    __shared__ __attribute__((aligned(16))) float own_lds[RING ? BM * OWN_PITCH : 4];
+    // dynamic LDS, requested by ring launches only (BM x OWN_PITCH floats), so that the other
+    // launches of this kernel keep two workgroups per compute unit
+    extern __shared__ __attribute__((aligned(16))) float own_lds[];
     f32x4 rv[RING ? RD : 1][kMaxSumParts - 1];   // peers' partials of the vectors in flight
     f32x4 ro[RING ? RD : 1];                  // their own parts
     uint32_t roff[RING ? RD : 1];             // their element offsets in C
@@ -1230,8 +1232,10 @@ hipError_t launch_bf16(const GemmProblem& p, Epi epi, hipStream_t s)
     q.ring_tiles = q.defer == 2 ? tiles / 256 : 0;
     dim3 grid(q.defer == 2 ? 256 : q.defer == 1 ? tiles / 2 : tiles * splits),
         block(64 * WM * WN);
+    // the ring's product buffer (dynamic LDS): BM rows of BN + 4 floats
+    const size_t dyn = q.defer == 2 ? (size_t)BM * (BN + 4) * 4 : 0;
 #define TPS_LAUNCH(E) \
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, 0, s, q);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, E>), grid, block, dyn, s, q);
     switch (epi) {
         case Epi::BiasGelu: TPS_LAUNCH(Epi::BiasGelu) break;
         case Epi::F32: TPS_LAUNCH(Epi::F32) break;
