@@ -671,7 +671,24 @@ def measure_next_rows(reps: int = 20, warmup: int = 10) -> dict:
                                  "note": "algorithmic FLOPs of the four gradient products; the "
                                          "call also recomputes P (one more GEMM) and transposes "
                                          "six operands"}
-    del X, A_i, a_i, B_i, dZ, grads, ws
+    # the same backward on the P kept by the forward (tp_mlp_shard_fwd_save, outside the
+    # timed region): the four gradient products and the transposes, no recomputation
+    _, P, fws = shard.mlp_shard_save(X, A_i, a_i, B_i, N, 0)
+    us_s = _time_events(lambda: shard.mlp_shard_backward(X, A_i, a_i, B_i, dZ, N, 0, out=grads,
+                                                         workspace=ws, P=P), reps, warmup, stream)
+    out["mlp_shard_backward_saved_p"] = {
+        "workload": w.name, "us": us_s, "tflops": fl_ / us_s / 1e6,
+        "frac_bf16_peak": fl_ / us_s / 1e6 / PEAK_BF16_TFLOPS,
+        "note": "tp_mlp_shard_bwd_saved on the forward's P (same bits as the recomputing call)"}
+    fz = torch.empty(T, h, device="cuda")
+    us_f = _time_events(lambda: shard.mlp_shard(X, A_i, a_i, B_i, N, 0, Z=fz, workspace=fws),
+                        reps, warmup, stream)
+    us_fs = _time_events(lambda: shard.mlp_shard_save(X, A_i, a_i, B_i, N, 0, Z=fz, P=P,
+                                                      workspace=fws), reps, warmup, stream)
+    out["mlp_shard_forward_keeping_p"] = {
+        "workload": w.name, "us_plain": us_f, "us_keeping_p": us_fs,
+        "note": "tp_mlp_shard_fwd against tp_mlp_shard_fwd_save, which also stores P (bf16)"}
+    del X, A_i, a_i, B_i, dZ, grads, ws, P, fws, fz
     torch.cuda.synchronize()
     return out
 

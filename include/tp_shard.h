@@ -180,6 +180,24 @@ tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a
                                    int64_t ffn, int n_shards, int rank, tp_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * MLP shard forward that also keeps the pre-activation for the backward pass:
+ *   P_i = X A_r + a_r,   Z_i = GeLU(P_i) B_r     (llms.blog, "Partitioning the MLP Block",
+ *                                                 steps 2-3, as tp_mlp_shard_fwd)
+ * The same two launches and the same bits of Z_i as tp_mlp_shard_fwd; the column GEMM's
+ * epilogue stores P_i (rounded once to bf16, before the GeLU) beside Y_i. P_i is what
+ * tp_mlp_shard_bwd would otherwise recompute: tp_mlp_shard_bwd_saved takes it instead.
+ *
+ *   X, A_i, a_i, B_i, Z_i, workspace   as for tp_mlp_shard_fwd
+ *   P_i     [tokens, ffn/N]   bf16  output, the caller's buffer; must not overlap the
+ *                                   workspace or Z_i (TP_ERR_ALIAS)
+ * dt: TP_BF16 only (TP_ERR_DTYPE otherwise). Errors as tp_mlp_shard_fwd.
+ * ---------------------------------------------------------------------------------------- */
+tp_status tp_mlp_shard_fwd_save(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                                float* Z_i, void* P_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                                int n_shards, int rank, tp_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Backward pass of the MLP shard (llms.blog, "Partitioning the MLP Block": one all-reduce in
  * the backward pass, over the input gradients of the column-parallel layer). For the
  * forward Z_i = GeLU(P) B_r, P = X A_r + a_r, and the upstream gradient dZ of the block
@@ -187,7 +205,7 @@ tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a
  *   dY = dZ B_r^T,   dP = dY * GeLU'(P),   GeLU'(x) = Phi(x) + x phi(x)
  *   dA_r = X^T dP,   da_r = sum over tokens of dP,   dB_r = GeLU(P)^T dZ
  *   dX_i = dP A_r^T  (rank i's input-gradient partial; the all-reduce sums them)
- * P is recomputed from X, A_i, a_i (nothing is kept from the forward call).
+ * P is recomputed from X, A_i, a_i (tp_mlp_shard_bwd_saved takes the forward's P instead).
  *
  *   X, A_i, a_i, B_i   as for tp_mlp_shard_fwd (bf16; a_i may be NULL)
  *   dZ     [tokens, hidden]   bf16  upstream gradient
@@ -207,6 +225,18 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
                            const void* dZ, float* dX_i, float* dA_i, float* da_i, float* dB_i,
                            int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, int rank,
                            tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same backward with P_i = X A_r + a_r taken from the forward (tp_mlp_shard_fwd_save)
+ * instead of recomputed: one GEMM fewer. Outputs, workspace (tp_mlp_bwd_workspace_bytes) and
+ * errors as tp_mlp_shard_bwd; with the P_i that tp_mlp_shard_fwd_save wrote for the same X,
+ * A_i, a_i, the same bits as tp_mlp_shard_bwd. The bias a_i is not needed (P_i includes it).
+ *   P_i     [tokens, ffn/N]   bf16  input; must not overlap the workspace (TP_ERR_ALIAS)
+ */
+tp_status tp_mlp_shard_bwd_saved(const void* X, const void* A_i, const void* B_i, const void* P_i,
+                                 const void* dZ, float* dX_i, float* dA_i, float* da_i,
+                                 float* dB_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                                 int n_shards, int rank, tp_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Gated (SwiGLU) MLP shard:
@@ -461,7 +491,7 @@ const char* tp_last_error(void);
 /* ABI version of this header (incremented on any signature or layout change). */
 int tp_abi_version(void);
 
-#define TP_SHARD_ABI_VERSION 11
+#define TP_SHARD_ABI_VERSION 12
 
 #ifdef __cplusplus
 }

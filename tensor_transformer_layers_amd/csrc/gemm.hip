@@ -4,7 +4,8 @@
 //
 // Both operands are K-contiguous, which is the layout an MFMA lane consumes: one 16-byte
 // chunk of 8 bf16 (or 4 fp32) consecutive K values per lane. The output stage is fused:
-//   BiasGelu  Y_i = GeLU(X A_i + a_i)                   column-parallel MLP layer
+//   BiasGelu  Y_i = GeLU(X A_i + a_i)                   column-parallel MLP layer (optionally
+//             also P = X A_i + a_i, rounded once, for the backward)
 //   F32       Z_i = Y_i B_i  (fp32 partial)             row-parallel layers (MLP, W_O)
 //   Bias      Y = X W_i + b_i                           column-parallel, no activation
 //   Qkv       [Q | K | V] = X W_qkv,i + b, scattered    column-parallel QKV projection
@@ -89,6 +90,11 @@ __device__ __forceinline__ void store_out(const GemmProblem& p, int m, int n, f3
             bf16* c = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc + n;
             *reinterpret_cast<bf16x4*>(c) = to_bf16x4(v);
         } else if constexpr (EPI == Epi::BiasGelu || EPI == Epi::Bias) {
+            if constexpr (EPI == Epi::BiasGelu && sizeof(T) == 2) {
+                if (p.pre)
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(p.pre) +
+                                               (int64_t)m * p.ldc + n) = to_bf16x4(v);
+            }
             if constexpr (EPI == Epi::BiasGelu) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);

@@ -46,6 +46,9 @@ struct GemmProblem {
     const void* aux;      // GeluGrad: the pre-activation P [M, N] bf16, leading dim ldaux
     int64_t ldaux;
     void* C;              // [M, N] row-major, ldc (BiasGelu / F32)
+    void* pre;            // BiasGelu, bf16 only, optional: the pre-activation acc + bias[n] is
+                          // also stored here, bf16 [M, N] with leading dimension ldc (the
+                          // MLP backward's P, kept from the forward)
     int64_t lda, ldb, ldc;
     int M, N, K;
     // Qkv scatter, row m = b * seq + s: columns [0, Hl d) are the local query heads, then

@@ -209,14 +209,17 @@ tp_status validate_linear(int64_t rows, int64_t in_f, int64_t out_f, int n, int 
 }
 
 // Y[rows, width] = act(X[rows, k] W[width, k]^T + b)
+// With pre (bf16 GeLU only), the pre-activation X W^T + b is stored there as well.
 hipError_t launch_column(const void* X, const void* W, const void* b, void* Y, int64_t rows,
-                         int64_t k, int64_t width, tp_activation act, tp_dtype dt, hipStream_t s)
+                         int64_t k, int64_t width, tp_activation act, tp_dtype dt, hipStream_t s,
+                         void* pre = nullptr)
 {
     tps::GemmProblem g{};
     g.A = X; g.lda = k;
     g.B = W; g.ldb = k;
     g.bias = b;
     g.C = Y; g.ldc = width;
+    g.pre = pre;
     g.M = (int)rows; g.N = (int)width; g.K = (int)k;
     const tps::Epi epi = act == TP_ACT_GELU ? tps::Epi::BiasGelu : tps::Epi::Bias;
     return dt == TP_BF16 ? tps::gemm_bf16(g, epi, s) : tps::gemm_f32(g, epi, s);
@@ -497,6 +500,42 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* A_i, const void* a_i, cons
     return hip_status(e, "row-parallel kernel launch");
 }
 
+tp_status tp_mlp_shard_fwd_save(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                                float* Z_i, void* P_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                                int n_shards, int rank, tp_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    if (!X || !A_i || !B_i || !Z_i || !P_i)
+        return fail(TP_ERR_NULL, "X, A_i, B_i, Z_i and P_i must be non-NULL");
+    if (dt != TP_BF16)
+        return fail(TP_ERR_DTYPE, "the forward that keeps P supports TP_BF16 only (got %d)", (int)dt);
+    tp_status st = validate_mlp_sizes(tokens, hidden, ffn, n_shards, dt);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= n_shards)
+        return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Z_i) ||
+        !aligned16(P_i) || (a_i && !aligned16(a_i)) || (workspace && !aligned16(workspace)))
+        return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t need = tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards, dt);
+    if (!workspace || workspace_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    // P_i is written by the same kernel as Y_i (the workspace) and must outlive the call
+    const size_t pbytes = (size_t)tokens * (size_t)(ffn / n_shards) * 2;
+    if (overlap(P_i, pbytes, workspace, need) ||
+        overlap(P_i, pbytes, Z_i, (size_t)tokens * (size_t)hidden * 4))
+        return fail(TP_ERR_ALIAS, "P_i overlaps the workspace or Z_i");
+    st = check_device();
+    if (st != TP_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the launches of tp_mlp_shard_fwd; the column GEMM's epilogue also stores P
+    hipError_t e = launch_column(X, A_i, a_i, workspace, tokens, hidden, ffn / n_shards,
+                                 TP_ACT_GELU, dt, s, P_i);
+    if (e != hipSuccess) return hip_status(e, "column-parallel kernel launch");
+    e = launch_row(workspace, B_i, Z_i, tokens, ffn / n_shards, hidden, dt, s);
+    return hip_status(e, "row-parallel kernel launch");
+}
+
 tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a_i,
                                    const void* B_i, float* Z_i, int64_t tokens, int64_t hidden,
                                    int64_t ffn, int n_shards, int rank, tp_dtype dt, void* stream)
@@ -535,10 +574,15 @@ size_t tp_mlp_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, i
     return bwd_layout(tokens, hidden, ffn / n_shards).total;
 }
 
-tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
-                           const void* dZ, float* dX_i, float* dA_i, float* da_i, float* dB_i,
-                           int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, int rank,
-                           tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+namespace {
+
+// The MLP shard's backward. P_saved: the forward's pre-activation P [T, F/N] bf16
+// (tp_mlp_shard_fwd_save), or nullptr to recompute it into the workspace from X, A_i, a_i.
+tp_status mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                        const void* P_saved, const void* dZ, float* dX_i, float* dA_i,
+                        float* da_i, float* dB_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                        int n_shards, int rank, tp_dtype dt, void* workspace,
+                        size_t workspace_bytes, void* stream)
 {
     if (!X || !A_i || !B_i || !dZ || !dX_i || !dA_i || !dB_i)
         return fail(TP_ERR_NULL, "X, A_i, B_i, dZ, dX_i, dA_i and dB_i must be non-NULL");
@@ -551,13 +595,17 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
         return fail(TP_ERR_RANK, "rank %d outside [0, %d)", rank, n_shards);
     if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(dZ) ||
         !aligned16(dX_i) || !aligned16(dA_i) || !aligned16(dB_i) || (a_i && !aligned16(a_i)) ||
-        (da_i && !aligned16(da_i)) || (workspace && !aligned16(workspace)))
+        (da_i && !aligned16(da_i)) || (workspace && !aligned16(workspace)) ||
+        (P_saved && !aligned16(P_saved)))
         return fail(TP_ERR_ALIGN, "every pointer must be 16-byte aligned");
     const int64_t T = tokens, h = hidden, fl = ffn / n_shards;
     const BwdLayout L = bwd_layout(T, h, fl);
     if (!workspace || workspace_bytes < L.total)
         return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                     workspace ? workspace_bytes : (size_t)0);
+    // the workspace is written while P is read (the GeLU' epilogue, the GeLU(P) transpose)
+    if (P_saved && overlap(P_saved, (size_t)T * (size_t)fl * 2, workspace, L.total))
+        return fail(TP_ERR_ALIAS, "P_i overlaps the workspace");
     st = check_device();
     if (st != TP_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -565,15 +613,17 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
     hipError_t e;
 #define TPS_TRY(call, what) \
     do { e = (call); if (e != hipSuccess) return hip_status(e, what); } while (0)
-    // 1. P = X A_r + a_r, recomputed, [T, F/N] bf16
-    TPS_TRY(launch_column(X, A_i, a_i, ws + L.p, T, h, fl, TP_ACT_NONE, dt, s), "P = X A + a");
+    // 1. P = X A_r + a_r [T, F/N] bf16: the forward's, or recomputed
+    const char* P = P_saved ? reinterpret_cast<const char*>(P_saved) : ws + L.p;
+    if (!P_saved)
+        TPS_TRY(launch_column(X, A_i, a_i, ws + L.p, T, h, fl, TP_ACT_NONE, dt, s), "P = X A + a");
     // 2. dP = (dZ B_r^T) * GeLU'(P): B_r = B_i^T is [F/N, h], contiguous along h
     TPS_TRY(tps::transpose_bf16(B_i, (int)h, (int)fl, fl, ws + L.bt, h, false, s), "B transpose");
     {
         tps::GemmProblem g{};
         g.A = dZ; g.lda = h;
         g.B = ws + L.bt; g.ldb = h;
-        g.aux = ws + L.p; g.ldaux = fl;
+        g.aux = P; g.ldaux = fl;
         g.C = ws + L.dp; g.ldc = fl;
         g.M = (int)T; g.N = (int)fl; g.K = (int)h;
         TPS_TRY(tps::gemm_bf16(g, tps::Epi::GeluGrad, s), "dP = dZ B^T * GeLU'(P)");
@@ -588,12 +638,34 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
     TPS_TRY(tps::transpose_bf16(X, (int)T, (int)h, h, ws + L.xt, L.t8, false, s), "X transpose");
     TPS_TRY(launch_row(ws + L.dpt, ws + L.xt, dA_i, fl, L.t8, h, dt, s), "dA = dP^T X");
     // 5. dB_i = dZ^T GeLU(P), reduced over tokens: GeLU(P)^T [F/N, T8], dZ^T [h, T8]
-    TPS_TRY(tps::transpose_bf16(ws + L.p, (int)T, (int)fl, fl, ws + L.yt, L.t8, true, s),
+    TPS_TRY(tps::transpose_bf16(P, (int)T, (int)fl, fl, ws + L.yt, L.t8, true, s),
             "GeLU(P) transpose");
     TPS_TRY(tps::transpose_bf16(dZ, (int)T, (int)h, h, ws + L.dzt, L.t8, false, s), "dZ transpose");
     TPS_TRY(launch_row(ws + L.dzt, ws + L.yt, dB_i, h, L.t8, fl, dt, s), "dB = dZ^T Y");
 #undef TPS_TRY
     return ok();
+}
+
+}  // namespace
+
+tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                           const void* dZ, float* dX_i, float* dA_i, float* da_i, float* dB_i,
+                           int64_t tokens, int64_t hidden, int64_t ffn, int n_shards, int rank,
+                           tp_dtype dt, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return mlp_shard_bwd(X, A_i, a_i, B_i, nullptr, dZ, dX_i, dA_i, da_i, dB_i, tokens, hidden,
+                         ffn, n_shards, rank, dt, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_mlp_shard_bwd_saved(const void* X, const void* A_i, const void* B_i, const void* P_i,
+                                 const void* dZ, float* dX_i, float* dA_i, float* da_i,
+                                 float* dB_i, int64_t tokens, int64_t hidden, int64_t ffn,
+                                 int n_shards, int rank, tp_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    if (!P_i) return fail(TP_ERR_NULL, "P_i must be non-NULL");
+    return mlp_shard_bwd(X, A_i, nullptr, B_i, P_i, dZ, dX_i, dA_i, da_i, dB_i, tokens, hidden,
+                         ffn, n_shards, rank, dt, workspace, workspace_bytes, stream);
 }
 
 size_t tp_swiglu_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int n_shards,

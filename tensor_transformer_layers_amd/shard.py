@@ -192,6 +192,38 @@ def mlp_shard(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor], B
     return Z, workspace
 
 
+def mlp_shard_save(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor],
+                   B_i: torch.Tensor, n_shards: int, rank: int, Z: Optional[torch.Tensor] = None,
+                   P: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None):
+    """Rank ``rank``'s MLP partial (bf16), keeping the pre-activation P_i = X A_r + a_r for
+    ``mlp_shard_backward(..., P=P_i)``. Returns (Z_i fp32 [tokens, hidden], P_i bf16
+    [tokens, F/N], workspace)."""
+    _need_2d("X", X, torch.bfloat16)
+    tokens, hidden = X.shape
+    fl = _need_2d("A_i", A_i)[0]
+    ffn = fl * n_shards
+    bf = torch.bfloat16
+    _need("A_i", A_i, (fl, hidden), bf)
+    _need("a_i", a_i, (fl,), bf, optional=True)
+    _need("B_i", B_i, (hidden, fl), bf)
+    if Z is None:
+        Z = torch.empty(tokens, hidden, dtype=torch.float32, device=X.device)
+    if P is None:
+        P = torch.empty(tokens, fl, dtype=bf, device=X.device)
+    _need("Z", Z, (tokens, hidden), torch.float32)
+    _need("P", P, (tokens, fl), bf)
+    if workspace is None:
+        workspace = mlp_workspace(tokens, hidden, ffn, n_shards, X.dtype, X.device)
+    wsb = _need_workspace(workspace, B.tp_mlp_workspace_bytes(tokens, hidden, ffn, n_shards,
+                                                              B.TP_BF16))
+    _require_cuda(X, A_i, a_i, B_i, Z, P, workspace)
+    st = B.tp_mlp_shard_fwd_save(X, A_i, a_i, B_i, Z, P, tokens, hidden, ffn, n_shards, rank,
+                                 B.TP_BF16, workspace, wsb, _stream(stream))
+    B.check(st)
+    return Z, P, workspace
+
+
 def mlp_bwd_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, device="cuda"):
     nbytes = B.tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards, B.TP_BF16)
     if nbytes == 0:
@@ -202,11 +234,13 @@ def mlp_bwd_workspace(tokens: int, hidden: int, ffn: int, n_shards: int, device=
 def mlp_shard_backward(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.Tensor],
                        B_i: torch.Tensor, dZ: torch.Tensor, n_shards: int, rank: int,
                        out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None):
+                       stream=None, P: Optional[torch.Tensor] = None):
     """Gradients of rank ``rank``'s MLP partial for the upstream dZ (bf16).
 
     Returns ({"dX": [T, h], "dA": [F/N, h], "da": [F/N], "dB": [h, F/N]} fp32, in the stored
-    layouts of X, A_i, a_i, B_i; workspace). dX is the rank's input-gradient partial."""
+    layouts of X, A_i, a_i, B_i; workspace). dX is the rank's input-gradient partial. With P
+    (the pre-activation ``mlp_shard_save`` kept) the call takes it instead of recomputing it;
+    a_i then only decides whether da is computed."""
     _need_2d("X", X, torch.bfloat16)
     tokens, hidden = X.shape
     fl = _need_2d("A_i", A_i)[0]
@@ -216,6 +250,7 @@ def mlp_shard_backward(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.T
     _need("a_i", a_i, (fl,), bf, optional=True)
     _need("B_i", B_i, (hidden, fl), bf)
     _need("dZ", dZ, (tokens, hidden), bf)
+    _need("P", P, (tokens, fl), bf, optional=True)
     f32 = dict(dtype=torch.float32, device=X.device)
     if out is None:
         out = {"dX": torch.empty(tokens, hidden, **f32), "dA": torch.empty(fl, hidden, **f32),
@@ -229,10 +264,16 @@ def mlp_shard_backward(X: torch.Tensor, A_i: torch.Tensor, a_i: Optional[torch.T
         workspace = mlp_bwd_workspace(tokens, hidden, ffn, n_shards, X.device)
     wsb = _need_workspace(workspace, B.tp_mlp_bwd_workspace_bytes(tokens, hidden, ffn, n_shards,
                                                                   B.TP_BF16))
-    _require_cuda(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"), out["dB"], workspace)
-    st = B.tp_mlp_shard_bwd(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"), out["dB"],
-                            tokens, hidden, ffn, n_shards, rank, _dt(X), workspace,
-                            wsb, _stream(stream))
+    _require_cuda(X, A_i, a_i, B_i, dZ, P, out["dX"], out["dA"], out.get("da"), out["dB"],
+                  workspace)
+    if P is None:
+        st = B.tp_mlp_shard_bwd(X, A_i, a_i, B_i, dZ, out["dX"], out["dA"], out.get("da"),
+                                out["dB"], tokens, hidden, ffn, n_shards, rank, _dt(X), workspace,
+                                wsb, _stream(stream))
+    else:
+        st = B.tp_mlp_shard_bwd_saved(X, A_i, B_i, P, dZ, out["dX"], out["dA"], out.get("da"),
+                                      out["dB"], tokens, hidden, ffn, n_shards, rank, _dt(X),
+                                      workspace, wsb, _stream(stream))
     B.check(st)
     return out, workspace
 

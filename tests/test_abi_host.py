@@ -373,3 +373,39 @@ def test_row_parallel_sum_tile_info():
     assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 9, BF16)[0] == 2   # TP_ERR_SHAPE
     assert B.tp_row_parallel_sum_tile_info(0, 8192, 1024, 8, BF16)[0] == 2
     assert B.tp_row_parallel_sum_tile_info(4096, 8192, 1024, 8, 7)[0] != 0
+
+
+def test_mlp_fwd_save_and_bwd_saved_validation():
+    """The forward that keeps P_i and the backward that takes it validate like
+    tp_mlp_shard_fwd / tp_mlp_shard_bwd, bf16 only, and refuse a P_i that overlaps a buffer
+    written during the call (TP_ERR_ALIAS), all before touching the device."""
+    T, h, ffn, N = 4096, 8192, 32768, 8
+    fl = ffn // N
+    ws = 1 << 32                                   # fake workspace address, far from the rest
+    need = B.tp_mlp_workspace_bytes(T, h, ffn, N, BF16)
+    f = dict(X=P, A_i=P, a_i=None, B_i=P, Z_i=P, P_i=1 << 36, tokens=T, hidden=h, ffn=ffn,
+             n_shards=N, rank=0, dt=BF16, workspace=ws, workspace_bytes=need)
+    g = lambda **kw: B.tp_mlp_shard_fwd_save(**dict(f, **kw))
+    assert g(P_i=None) == 1 and g(Z_i=None) == 1
+    assert g(dt=F32) == 5                          # bf16 only
+    assert g(n_shards=3) == 3 and g(rank=8) == 4
+    assert g(P_i=(1 << 36) + 8) == 6
+    assert g(workspace_bytes=need - 256) == 7
+    assert g(P_i=ws + need - 256) == 10            # P_i runs into Y_i
+    assert g(P_i=ws - T * fl * 2 + 16) == 10       # ... from below
+    assert g(Z_i=(1 << 36) + 4096) == 10           # Z_i inside P_i
+    # adjacent is fine: validation passes and the call reaches the device check (no GPU here)
+    assert g(P_i=ws + need) not in (1, 2, 3, 4, 5, 6, 7, 10)
+    assert "overlap" not in B.tp_last_error()
+    wsb = B.tp_mlp_bwd_workspace_bytes(T, h, ffn, N, BF16)
+    b = dict(X=P, A_i=P, B_i=P, P_i=1 << 36, dZ=P, dX_i=P, dA_i=P, da_i=None, dB_i=P, tokens=T,
+             hidden=h, ffn=ffn, n_shards=N, rank=0, dt=BF16, workspace=ws, workspace_bytes=wsb)
+    k = lambda **kw: B.tp_mlp_shard_bwd_saved(**dict(b, **kw))
+    assert k(P_i=None) == 1 and k(dZ=None) == 1
+    assert k(dt=F32) == 5
+    assert k(n_shards=3) == 3 and k(rank=-1) == 4
+    assert k(P_i=(1 << 36) + 4) == 6
+    assert k(workspace_bytes=wsb - 1) == 7
+    assert k(tokens=(1 << 22) + 1) == 2
+    assert k(P_i=ws + wsb - 16) == 10              # the workspace is written while P_i is read
+    assert k(P_i=ws + wsb) not in (1, 2, 3, 4, 5, 6, 7, 10)

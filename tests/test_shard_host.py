@@ -94,3 +94,18 @@ def test_backward_checks_gradients():
     _raises("dA has shape", shard.mlp_shard_backward, m["X"], m["A_i"], m["a_i"], m["B_i"], dZ, 2, 0,
             out=out)
     _raises("dZ has shape", shard.mlp_shard_backward, m["X"], m["A_i"], m["a_i"], m["B_i"], dZ[:8], 2, 0)
+
+
+def test_forward_keeping_p_and_backward_taking_it_check_p():
+    m = _mlp()
+    dZ = torch.zeros(16, 64, dtype=bf)
+    _raises("P has shape", shard.mlp_shard_save, m["X"], m["A_i"], m["a_i"], m["B_i"], 2, 0,
+            P=torch.zeros(16, 64, dtype=bf))
+    _raises("P has dtype", shard.mlp_shard_save, m["X"], m["A_i"], m["a_i"], m["B_i"], 2, 0,
+            P=torch.zeros(16, 32, dtype=f32))
+    _raises("X has dtype", shard.mlp_shard_save, m["X"].float(), m["A_i"], m["a_i"], m["B_i"], 2, 0)
+    _raises("device tensors", shard.mlp_shard_save, m["X"], m["A_i"], m["a_i"], m["B_i"], 2, 0)
+    _raises("P has shape", shard.mlp_shard_backward, m["X"], m["A_i"], m["a_i"], m["B_i"], dZ, 2, 0,
+            P=torch.zeros(32, 16, dtype=bf))
+    _raises("device tensors", shard.mlp_shard_backward, m["X"], m["A_i"], m["a_i"], m["B_i"], dZ,
+            2, 0, P=torch.zeros(16, 32, dtype=bf))
