@@ -421,8 +421,14 @@ def measure_mlp_f32(reps: int = 200, warmup: int = 20):
     # plus a 32-row activation: bound by memory and latency, not by the matrix cores
     col_bytes = 4.0 * (T * h + fl * h + fl + T * fl)
     row_bytes = 4.0 * (T * fl + h * fl + T * h)
-    mb = 1 if T <= 16 else (2 if T <= 32 else 4)
     dom, dom_us, dom_b = ("column", col_us, col_bytes) if col_us >= row_us else ("row", row_us, row_bytes)
+    # the library's row blocks per workgroup (16-column blocks, rows split while the grid
+    # stays within 256 workgroups), for the kernel's name
+    cols = -(-(fl if dom == "column" else h) // 16)
+    rblocks = -(-T // 16)
+    groups = max(1, min(rblocks, 256 // cols))
+    need = -(-rblocks // groups)
+    mb = 1 if need <= 1 else (2 if need <= 2 else 4)
     kname = "gemm_f32_skinny_kernel<%d, (tps::Epi)%d>" % (mb, 0 if dom == "column" else 1)
     out = {"workload": w.name, "unit": "block: %d shards + on-device sum" % N, "dtype": "f32",
            "us": us, "timing": "HIP graph replay of 20 blocks",

@@ -1134,7 +1134,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmProblem p)
 // or activation row (l & 15), the 4 consecutive K values at 4 (l >> 4) of a 16-wide chunk,
 // fed to 4 consecutive MFMAs as in gemm_f32_kernel), the waves' partial accumulators are
 // added through LDS in the fixed order 0 .. 15, and the epilogue runs once per output vector.
-// Sixteen waves put a wave's whole K range (128 values at K = 2048) in flight at once.
+// Sixteen waves put a wave's whole K range (128 values at K = 2048) in flight at once. When
+// the column blocks alone leave compute units idle, the rows are split too: workgroup
+// (x, y) takes the MB 16-row blocks from y MB on (the same per-element arithmetic).
 template <int MB, Epi EPI>
 __global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
 {
@@ -1144,6 +1146,7 @@ __global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16;
+    const int mrow0 = blockIdx.y * MB * 16;     // first row of this workgroup's blocks
     const int fr = lane & 15, fg = lane >> 4;
     const float* __restrict__ gA = reinterpret_cast<const float*>(p.A);
     const float* __restrict__ gB = reinterpret_cast<const float*>(p.B);
@@ -1163,7 +1166,7 @@ __global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
             rb[u] = kin && nin ? ld16(gB + (int64_t)nrow * p.ldb + k) : zero16();
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const int m = mb * 16 + fr;
+                const int m = mrow0 + mb * 16 + fr;
                 ra[u][mb] = kin && m < p.M ? ld16(gA + (int64_t)m * p.lda + k) : zero16();
             }
         }
@@ -1187,7 +1190,7 @@ __global__ __launch_bounds__(1024) void gemm_f32_skinny_kernel(GemmProblem p)
         f32x4 v = part[0][mb][lane];
 #pragma unroll
         for (int w = 1; w < NWV; ++w) v += part[w][mb][lane];
-        const int m = mb * 16 + fr, n = n0 + 4 * fg;
+        const int m = mrow0 + mb * 16 + fr, n = n0 + 4 * fg;
         if (m < p.M && n < p.N) store_out<EPI, float>(p, m, n, v);
     }
 }
@@ -1545,7 +1548,8 @@ hipError_t qkv_reduce_scatter(const GemmProblem& p, const float* parts, hipStrea
 template <int MB>
 hipError_t launch_f32_skinny(const GemmProblem& p, Epi epi, hipStream_t s)
 {
-    dim3 grid((unsigned)((p.N + 15) / 16)), block(1024);
+    const int row_groups = (p.M + 16 * MB - 1) / (16 * MB);
+    dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)row_groups), block(1024);
     switch (epi) {
         case Epi::BiasGelu:
             hipLaunchKernelGGL((gemm_f32_skinny_kernel<MB, Epi::BiasGelu>), grid, block, 0, s, p);
@@ -1562,14 +1566,22 @@ hipError_t launch_f32_skinny(const GemmProblem& p, Epi epi, hipStream_t s)
     return hipGetLastError();
 }
 
-// Up to 64 rows: the skinny kernel (all rows per workgroup, K split over its waves); beyond,
-// 32 x 64 tiles. The fp32 worked example (32 x 1024 x 2048 and 32 x 2048 x 1024): 20 and 34 us
+// Up to 64 rows: the skinny kernel (16 columns and up to all rows per workgroup, K split over
+// its waves); beyond, 32 x 64 tiles. The fp32 worked example (32 x 1024 x 2048 and 32 x 2048 x 1024): 20 and 34 us
 // per product on the tiles, against the skinny kernel's times in the benchmark's configs.
 hipError_t gemm_f32(const GemmProblem& p, Epi epi, hipStream_t s)
 {
-    if (p.M <= 16) return launch_f32_skinny<1>(p, epi, s);
-    if (p.M <= 32) return launch_f32_skinny<2>(p, epi, s);
-    if (p.M <= 64) return launch_f32_skinny<4>(p, epi, s);
+    if (p.M <= 64) {
+        // 16-row blocks per workgroup: all of them, unless fewer per workgroup let the grid
+        // cover more of the 256 compute units (the 32-token worked example: 128 and 64
+        // column blocks, two row blocks each)
+        const int cols = (p.N + 15) / 16, rblocks = (p.M + 15) / 16;
+        const int groups = std::max(1, std::min(rblocks, 256 / cols));
+        const int mb = (rblocks + groups - 1) / groups;
+        if (mb <= 1) return launch_f32_skinny<1>(p, epi, s);
+        if (mb <= 2) return launch_f32_skinny<2>(p, epi, s);
+        return launch_f32_skinny<4>(p, epi, s);
+    }
     constexpr int BM = 32, BN = 64;
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     dim3 grid(tiles), block(kThreads);
