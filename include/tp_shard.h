@@ -189,7 +189,7 @@ tp_status tp_mlp_shard_fwd_noalloc(const void* X, const void* A_i, const void* a
  *
  *   X, A_i, a_i, B_i, Z_i, workspace   as for tp_mlp_shard_fwd
  *   P_i     [tokens, ffn/N]   bf16  output, the caller's buffer; must not overlap the
- *                                   workspace or Z_i (TP_ERR_ALIAS)
+ *                                   workspace, Z_i or an input (TP_ERR_ALIAS)
  * dt: TP_BF16 only (TP_ERR_DTYPE otherwise). Errors as tp_mlp_shard_fwd.
  * ---------------------------------------------------------------------------------------- */
 tp_status tp_mlp_shard_fwd_save(const void* X, const void* A_i, const void* a_i, const void* B_i,
@@ -230,7 +230,8 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, cons
  * instead of recomputed: one GEMM fewer. Outputs, workspace (tp_mlp_bwd_workspace_bytes) and
  * errors as tp_mlp_shard_bwd; with the P_i that tp_mlp_shard_fwd_save wrote for the same X,
  * A_i, a_i, the same bits as tp_mlp_shard_bwd. The bias a_i is not needed (P_i includes it).
- *   P_i     [tokens, ffn/N]   bf16  input; must not overlap the workspace (TP_ERR_ALIAS)
+ *   P_i     [tokens, ffn/N]   bf16  input; must not overlap the workspace or a gradient
+ *                                   output (TP_ERR_ALIAS)
  */
 tp_status tp_mlp_shard_bwd_saved(const void* X, const void* A_i, const void* B_i, const void* P_i,
                                  const void* dZ, float* dX_i, float* dA_i, float* da_i,

@@ -520,11 +520,14 @@ tp_status tp_mlp_shard_fwd_save(const void* X, const void* A_i, const void* a_i,
     if (!workspace || workspace_bytes < need)
         return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
-    // P_i is written by the same kernel as Y_i (the workspace) and must outlive the call
-    const size_t pbytes = (size_t)tokens * (size_t)(ffn / n_shards) * 2;
+    // P_i is written by the same kernel as Y_i (the workspace), while X, A_i and a_i are read
+    const size_t fl = (size_t)(ffn / n_shards), pbytes = (size_t)tokens * fl * 2;
     if (overlap(P_i, pbytes, workspace, need) ||
-        overlap(P_i, pbytes, Z_i, (size_t)tokens * (size_t)hidden * 4))
-        return fail(TP_ERR_ALIAS, "P_i overlaps the workspace or Z_i");
+        overlap(P_i, pbytes, Z_i, (size_t)tokens * (size_t)hidden * 4) ||
+        overlap(P_i, pbytes, X, (size_t)tokens * (size_t)hidden * 2) ||
+        overlap(P_i, pbytes, A_i, fl * (size_t)hidden * 2) ||
+        overlap(P_i, pbytes, B_i, (size_t)hidden * fl * 2) || (a_i && overlap(P_i, pbytes, a_i, fl * 2)))
+        return fail(TP_ERR_ALIAS, "P_i overlaps the workspace, Z_i or an input");
     st = check_device();
     if (st != TP_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -603,9 +606,17 @@ tp_status mlp_shard_bwd(const void* X, const void* A_i, const void* a_i, const v
     if (!workspace || workspace_bytes < L.total)
         return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                     workspace ? workspace_bytes : (size_t)0);
-    // the workspace is written while P is read (the GeLU' epilogue, the GeLU(P) transpose)
-    if (P_saved && overlap(P_saved, (size_t)T * (size_t)fl * 2, workspace, L.total))
-        return fail(TP_ERR_ALIAS, "P_i overlaps the workspace");
+    // the workspace and the gradients are written while P is still to be read (the GeLU'
+    // epilogue, then the GeLU(P) transpose after dX and dA are written)
+    if (P_saved) {
+        const size_t pb = (size_t)T * (size_t)fl * 2;
+        if (overlap(P_saved, pb, workspace, L.total) ||
+            overlap(P_saved, pb, dX_i, (size_t)T * (size_t)h * 4) ||
+            overlap(P_saved, pb, dA_i, (size_t)fl * (size_t)h * 4) ||
+            overlap(P_saved, pb, dB_i, (size_t)h * (size_t)fl * 4) ||
+            (da_i && overlap(P_saved, pb, da_i, (size_t)fl * 4)))
+            return fail(TP_ERR_ALIAS, "P_i overlaps the workspace or a gradient");
+    }
     st = check_device();
     if (st != TP_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

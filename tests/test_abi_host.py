@@ -394,6 +394,8 @@ def test_mlp_fwd_save_and_bwd_saved_validation():
     assert g(P_i=ws + need - 256) == 10            # P_i runs into Y_i
     assert g(P_i=ws - T * fl * 2 + 16) == 10       # ... from below
     assert g(Z_i=(1 << 36) + 4096) == 10           # Z_i inside P_i
+    assert g(X=(1 << 36) + 4096) == 10             # ... or an input
+    assert g(a_i=(1 << 36) + T * fl * 2 - 16) == 10
     # adjacent is fine: validation passes and the call reaches the device check (no GPU here)
     assert g(P_i=ws + need) not in (1, 2, 3, 4, 5, 6, 7, 10)
     assert "overlap" not in B.tp_last_error()
@@ -408,4 +410,6 @@ def test_mlp_fwd_save_and_bwd_saved_validation():
     assert k(workspace_bytes=wsb - 1) == 7
     assert k(tokens=(1 << 22) + 1) == 2
     assert k(P_i=ws + wsb - 16) == 10              # the workspace is written while P_i is read
+    assert k(dX_i=(1 << 36) + 64) == 10            # ... and so are the gradients
+    assert k(da_i=(1 << 36) + T * fl * 2 - 16) == 10
     assert k(P_i=ws + wsb) not in (1, 2, 3, 4, 5, 6, 7, 10)
