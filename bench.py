@@ -182,19 +182,33 @@ class ClockSampler:
 
 
 # ---- timing helpers -------------------------------------------------------------------------
-def _time_events(fn, reps: int, warmup: int, stream) -> float:
-    """Average microseconds per call of fn(), HIP events on ``stream`` around ``reps`` calls."""
+def _time_events(fn, reps: int, warmup: int, stream, rounds: int = 3,
+                 warm_ms: float = 60.0) -> float:
+    """Microseconds per call of fn(): HIP events on ``stream`` around ``rounds`` rounds of
+    ``reps`` calls each, the median round's average. The warm-up runs at least ``warmup``
+    calls and at least ``warm_ms`` of wall time in batches of calls: the shader clock settles
+    over the first tens of milliseconds of MFMA work, and a workload of a few hundred
+    microseconds per call would otherwise be timed on a clock still rising."""
     import torch
     for _ in range(warmup):
         fn()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return float(sorted(per)[len(per) // 2])
 
 
 def _roof_mfma(name: str, flops: float, us: float, peak: float) -> dict:
@@ -348,9 +362,9 @@ def time_layer_step(drv, step, w, fl, steps: int, warmup: int, stream) -> dict:
 
 # ---- the measured workloads other than the layer step -----------------------------------------
 def _time_graph(fn, reps: int, warmup: int = 3):
-    """Average microseconds per fn() when ``reps`` calls are captured once in a HIP graph and
-    the graph is replayed (launch-bound work: the host's per-call overhead is left out).
-    Returns (us, graph)."""
+    """Microseconds per fn() when ``reps`` calls are captured once in a HIP graph and the graph
+    is replayed (launch-bound work: the host's per-call overhead is left out); the median of
+    three timed rounds after 60 ms of replays. Returns (us, graph)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -361,14 +375,20 @@ def _time_graph(fn, reps: int, warmup: int = 3):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 5
-    e0.record()
-    for _ in range(n):
+    t0 = time.perf_counter()          # replays for 60 ms first, as _time_events warms up
+    while (time.perf_counter() - t0) * 1e3 < 60.0:
         g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (n * reps), g
+        torch.cuda.synchronize()
+    n, per = 5, []
+    for _ in range(3):                # the median of three rounds of n replays
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / (n * reps))
+    return float(sorted(per)[1]), g
 
 
 def measure_mlp_f32(reps: int = 200, warmup: int = 20):
