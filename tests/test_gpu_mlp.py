@@ -118,6 +118,29 @@ def test_f32_linear_primitives_few_rows(T):
     assert ep < 1e-5 and ez < 1e-5
 
 
+@pytest.mark.parametrize("T,width", [(47, 1600), (33, 4096), (64, 520), (17, 2056)])
+def test_f32_few_rows_row_groups(T, width):
+    """The few-rows fp32 GEMM splits its 16-row blocks over workgroups while the grid stays
+    within 256 (47 rows x 100 column blocks: two groups of two blocks, the last one ragged;
+    33 x 256: one group of three; 64 x 33: four groups of one; 17 x 129: one group of two).
+    Against the oracle's linear layer, and the first 16 rows bitwise equal to a 16-row call
+    (one block per workgroup): the split leaves each output's arithmetic unchanged."""
+    torch = torch_cuda()
+    from tensor_transformer_layers_amd import shard
+    rng = np.random.default_rng(T * 7919 + width)
+    K = 1032
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    W = (rng.standard_normal((width, K)) / 32).astype(np.float32)   # [out, in]
+    b = (rng.standard_normal(width) / 32).astype(np.float32)
+    Y = host(shard.column_parallel(dev(X, "f32"), dev(W, "f32"), dev(b, "f32"), 1, 0))
+    e = oracle.rel_frobenius(Y, oracle.linear(X, W.T, b))
+    Y16 = host(shard.column_parallel(dev(X[:16], "f32"), dev(W, "f32"), dev(b, "f32"), 1, 0))
+    print("fp32 few rows T=%d width=%d: err %.2e" % (T, width, e))
+    assert e < 1e-5
+    assert np.array_equal(Y[:16], Y16)
+    torch.cuda.synchronize()
+
+
 def test_mlp_bf16_shards_sum_to_unsharded_block():
     """sum_r GeLU(X A_r + a_r) B_r on the GPU equals the oracle's unsharded GeLU(X A + a) B."""
     torch = torch_cuda()
